@@ -1,0 +1,274 @@
+"""Seeded synthetic inputs for the MiniMax-H3 DiT block forward.
+
+This module only *makes inputs*: the shapes of the packed-sequence workloads,
+one independent random stream per tensor, packing of fp32 draws into bf16 bit
+patterns, and the INT8 group-32 quantizer that turns a bf16 weight draw into
+the (int8 codes, bf16 scales) pair the weight-only path consumes.  No step of
+the block (normalisation, projection, rotation, attention, gating) is computed
+here, so both the CPU oracle and the GPU path can take these arrays as they are.
+
+Sources for the shapes (page titles and sections; no real checkpoint exists
+here, every tensor is a synthetic draw):
+
+* minimax-h3-mlx README, "Architecture": 50 blocks, hidden 5376, 56x128 heads
+  (inner 7168), SwiGLU FFN 14336, 3D MM-RoPE; one packed sequence
+  [text L | keyframe conditions C | target audio A | target video V]; modality
+  enters through a per-row AdaLN tag.
+* minimax-h3-mlx README, "AdaLN precompute": the per-block projection is
+  [96768, 2688] and 96768 = 18 x 5376, i.e. 3 modality groups x 6 modulation
+  vectors of width D per timestep.
+* minimax-h3-mlx README, "Validation": the packed (t, h, w) grid is built in
+  float64; video and audio share one 40-units-per-second rotary clock.
+
+Readings (stated once, used everywhere):
+
+* tags: 0 = text and condition rows, 1 = audio rows, 2 = video rows.
+* positions: a text or audio row at index i is 1-D, i.e. (i, i, i) on the three
+  rotary axes; a video latent (f, y, x) sits at (f * 20/3, y, x) -- one latent
+  frame is 4 video frames at 24 fps, 1/6 s, i.e. 20/3 units of the 40 u/s clock;
+  a condition (reference image) token on a 32-wide grid sits at (0, y, x).  The
+  grid is built in float64 and cast to float32 once.
+* distributions: x ~ N(0, 1) fp32; W ~ N(0, 1/fan_in) rounded to bf16; biases
+  ~ N(0, 1/fan_in) bf16; QK-norm gains ~ 1 + N(0, 0.01) bf16; modulation table
+  ~ N(0, 0.1) (variance 0.1) bf16.
+* INT8 weight-only: symmetric, groups of 32 along K, one bf16 scale per group:
+  s = bf16(max|w_g| / 127) (s = 0 gives q = 0), q = clamp(round-half-even(w/s),
+  -127, 127).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+# tensor ids of the per-tensor streams: SeedSequence([seed, block, tensor_id])
+_TID = {
+    "x": 0, "w_qkv": 1, "b_qkv": 2, "w_out": 3, "b_out": 4, "w_fc1": 5,
+    "b_fc1": 6, "w_fc2": 7, "b_fc2": 8, "q_norm": 9, "k_norm": 10, "table": 11,
+}
+TAG_TEXT, TAG_AUDIO, TAG_VIDEO = 0, 1, 2
+WFMT_BF16, WFMT_INT8_G32 = 0, 1
+
+
+@dataclasses.dataclass(frozen=True)
+class Dims:
+    hidden: int
+    heads: int
+    head_dim: int
+    ffn: int
+    n_tags: int = 3
+    rope_split: Tuple[int, int, int] = (32, 48, 48)
+    rope_theta: float = 10000.0
+    ln_eps: float = 1e-6
+    qk_eps: float = 1e-6
+    wfmt: int = WFMT_BF16
+
+    @property
+    def inner(self) -> int:
+        return self.heads * self.head_dim
+
+
+H3_DIMS = Dims(hidden=5376, heads=56, head_dim=128, ffn=14336)
+TINY_DIMS = Dims(hidden=256, heads=4, head_dim=96, ffn=768, rope_split=(24, 36, 36))
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    dims: Dims
+    n_blocks: int
+    L: int
+    C: int
+    A: int
+    V: Tuple[int, int, int]
+
+    @property
+    def n_rows(self) -> int:
+        return self.L + self.C + self.A + self.V[0] * self.V[1] * self.V[2]
+
+
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("tiny_2blk_n164", TINY_DIMS, 2, 16, 0, 20, (2, 8, 8)),
+        Workload("h3_1blk_n1192", H3_DIMS, 1, 128, 0, 40, (1, 32, 32)),
+        Workload("h3_50blk_n6437", H3_DIMS, 50, 256, 0, 37, (6, 32, 32)),
+        Workload("h3_50blk_n7461", H3_DIMS, 50, 256, 1024, 37, (6, 32, 32)),
+        Workload("h3_50blk_n49840", H3_DIMS, 50, 256, 1024, 200, (31, 30, 52)),
+        Workload("h3_1blk_n1192_int8",
+                 dataclasses.replace(H3_DIMS, wfmt=WFMT_INT8_G32), 1, 128, 0, 40, (1, 32, 32)),
+    ]
+}
+
+
+def _rng(seed: int, block: int, name: str) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, block, _TID[name]])))
+
+
+# ---------------------------------------------------------------- bf16 packing
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest, ties to even) and return the bit patterns."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def quantize_int8_g32(w_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Symmetric INT8 codes with one bf16 scale per 32 consecutive K elements.
+
+    ``w_bits`` is a bf16 weight [out, in] (bit patterns); returns (q int8
+    [out, in], s bf16 bits [out, in/32]).
+    """
+    out_f, in_f = w_bits.shape
+    assert in_f % 32 == 0
+    w = bf16_bits_to_f32(w_bits).astype(np.float64).reshape(out_f, in_f // 32, 32)
+    amax = np.abs(w).max(axis=2)
+    s_bits = f32_to_bf16_bits((amax / 127.0).astype(np.float32))
+    s = bf16_bits_to_f32(s_bits).astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s > 0, np.rint(w / np.where(s > 0, s, 1.0)), 0.0)
+    q = np.clip(q, -127, 127).astype(np.int8).reshape(out_f, in_f)
+    return q, s_bits
+
+
+# ---------------------------------------------------------------- geometry
+def packed_layout(wl: Workload) -> Tuple[np.ndarray, np.ndarray]:
+    """Modality tags int32 [N] and rotary positions float32 [N, 3] of the packed rows."""
+    rows_t, rows_p = [], []
+    L, C, A = wl.L, wl.C, wl.A
+    f, gh, gw = wl.V
+    idx = np.arange(L, dtype=np.float64)
+    rows_t.append(np.full(L, TAG_TEXT, np.int32))
+    rows_p.append(np.stack([idx, idx, idx], axis=1))
+    if C:
+        c = np.arange(C)
+        rows_t.append(np.full(C, TAG_TEXT, np.int32))
+        rows_p.append(np.stack([np.zeros(C), (c // 32).astype(np.float64),
+                                (c % 32).astype(np.float64)], axis=1))
+    k = np.arange(A, dtype=np.float64)
+    rows_t.append(np.full(A, TAG_AUDIO, np.int32))
+    rows_p.append(np.stack([k, k, k], axis=1))
+    ff, yy, xx = np.meshgrid(np.arange(f), np.arange(gh), np.arange(gw), indexing="ij")
+    rows_t.append(np.full(f * gh * gw, TAG_VIDEO, np.int32))
+    rows_p.append(np.stack([ff.ravel() * (20.0 / 3.0), yy.ravel().astype(np.float64),
+                            xx.ravel().astype(np.float64)], axis=1))
+    tags = np.concatenate(rows_t)
+    pos = np.concatenate(rows_p).astype(np.float32)
+    assert tags.shape[0] == wl.n_rows
+    return tags, np.ascontiguousarray(pos)
+
+
+# ---------------------------------------------------------------- tensors
+def make_x(wl_or_n, dims: Dims, seed: int = 0) -> np.ndarray:
+    n = wl_or_n.n_rows if isinstance(wl_or_n, Workload) else int(wl_or_n)
+    return _rng(seed, 0, "x").standard_normal((n, dims.hidden), dtype=np.float32)
+
+
+def _normal_bf16(seed, block, name, shape, var) -> np.ndarray:
+    a = _rng(seed, block, name).standard_normal(shape, dtype=np.float32)
+    return f32_to_bf16_bits(a * np.float32(np.sqrt(var)))
+
+
+def make_table(dims: Dims, n_blocks: int, seed: int = 0) -> np.ndarray:
+    """Modulation table bf16 bits [n_blocks, n_tags, 6, D] ~ N(0, 0.1)."""
+    return np.stack([_normal_bf16(seed, b, "table", (dims.n_tags, 6, dims.hidden), 0.1)
+                     for b in range(n_blocks)])
+
+
+def make_block_weights(dims: Dims, block: int, seed: int = 0,
+                       biases: bool = True, norms: bool = True) -> Dict[str, Optional[np.ndarray]]:
+    """Host weights of one block in PyTorch Linear layout W[out][in].
+
+    bf16 layers: ``w_*`` are uint16 bit patterns.  INT8 layers (dims.wfmt == 1):
+    ``w_*`` are int8 codes and ``s_*`` are bf16 scale bits [out, in/32]; both
+    are derived from the same seeded bf16 draw the bf16 build would use.
+    Rows of ``w_qkv`` are interleaved per head: [h0: q, k, v][h1: q, k, v]...
+    and ``w_fc1`` stacks [gate; value].
+    """
+    D, Di, F, d = dims.hidden, dims.inner, dims.ffn, dims.head_dim
+    shapes = {"qkv": (3 * Di, D), "out": (D, Di), "fc1": (2 * F, D), "fc2": (D, F)}
+    w: Dict[str, Optional[np.ndarray]] = {}
+    for k, (o, i) in shapes.items():
+        bits = _normal_bf16(seed, block, "w_" + k, (o, i), 1.0 / i)
+        if dims.wfmt == WFMT_INT8_G32:
+            w["w_" + k], w["s_" + k] = quantize_int8_g32(bits)
+        else:
+            w["w_" + k], w["s_" + k] = bits, None
+        w["b_" + k] = _normal_bf16(seed, block, "b_" + k, (o,), 1.0 / i) if biases else None
+    if norms:
+        for k in ("q_norm", "k_norm"):
+            g = 1.0 + 0.1 * _rng(seed, block, k).standard_normal(d, dtype=np.float32)
+            w[k] = f32_to_bf16_bits(g)
+    else:
+        w["q_norm"] = w["k_norm"] = None
+    return w
+
+
+def make_inputs(wl: Workload, seed: int = 0, n_blocks: Optional[int] = None,
+                biases: bool = True, norms: bool = True):
+    """Everything one forward of ``wl`` needs, on the host (small workloads only)."""
+    nb = wl.n_blocks if n_blocks is None else n_blocks
+    tags, pos = packed_layout(wl)
+    x = make_x(wl, wl.dims, seed)
+    table = make_table(wl.dims, nb, seed)
+    weights = [make_block_weights(wl.dims, b, seed, biases, norms) for b in range(nb)]
+    return x, tags, pos, table, weights
+
+
+def make_device_inputs(wl: Workload, seed: int = 0, device: str = "cuda",
+                       n_blocks: Optional[int] = None):
+    """Same distributions as :func:`make_inputs`, drawn on the device by torch.
+
+    Used where the host generator would take minutes (50 blocks of 5376-wide
+    weights = 19.3e9 draws).  The streams differ from the host generator's, so
+    inputs made here are only for timing and for properties that hold for any
+    input; parity against the oracle always uses :func:`make_inputs`.
+    """
+    import torch
+
+    nb = wl.n_blocks if n_blocks is None else n_blocks
+    dims = wl.dims
+    D, Di, F, d = dims.hidden, dims.inner, dims.ffn, dims.head_dim
+    g = torch.Generator(device=device)
+    tags, pos = packed_layout(wl)
+    g.manual_seed(seed * 1000003 + 1)
+    x = torch.randn(wl.n_rows, D, generator=g, device=device, dtype=torch.float32)
+    t_tags = torch.from_numpy(tags).to(device)
+    t_pos = torch.from_numpy(pos).to(device)
+    table = (torch.randn(nb, dims.n_tags, 6, D, generator=g, device=device)
+             * float(np.sqrt(0.1))).to(torch.bfloat16)
+    shapes = {"qkv": (3 * Di, D), "out": (D, Di), "fc1": (2 * F, D), "fc2": (D, F)}
+    blocks = []
+    for b in range(nb):
+        g.manual_seed(seed * 1000003 + 7919 * (b + 1))
+        wb = {}
+        for k, (o, i) in shapes.items():
+            w = torch.randn(o, i, generator=g, device=device) * float(1.0 / np.sqrt(i))
+            if dims.wfmt == WFMT_INT8_G32:
+                wb["w_" + k], wb["s_" + k] = _quantize_int8_g32_torch(w.to(torch.bfloat16))
+            else:
+                wb["w_" + k], wb["s_" + k] = w.to(torch.bfloat16), None
+            del w
+            wb["b_" + k] = (torch.randn(o, generator=g, device=device)
+                            * float(1.0 / np.sqrt(i))).to(torch.bfloat16)
+        for k in ("q_norm", "k_norm"):
+            wb[k] = (1.0 + 0.1 * torch.randn(d, generator=g, device=device)).to(torch.bfloat16)
+        blocks.append(wb)
+    return x, t_tags, t_pos, table, blocks
+
+
+def _quantize_int8_g32_torch(w_bf16):
+    import torch
+
+    o, i = w_bf16.shape
+    w = w_bf16.float().view(o, i // 32, 32)
+    s = (w.abs().amax(dim=2) / 127.0).to(torch.bfloat16)
+    sf = s.float().unsqueeze(-1)
+    q = torch.where(sf > 0, torch.round(w / torch.where(sf > 0, sf, torch.ones_like(sf))),
+                    torch.zeros_like(w))
+    return q.clamp_(-127, 127).to(torch.int8).view(o, i).contiguous(), s.contiguous()
