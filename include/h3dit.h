@@ -1,0 +1,190 @@
+/*
+ * h3dit.h -- C ABI of the MI355X (gfx950) MiniMax-H3 DiT block forward.
+ *
+ * What is computed (page titles and sections):
+ *   One DiT block, run 50 times per denoising forward, over one packed
+ *   sequence [text | conditions | audio | video]: full self-attention, no
+ *   cross-attention, modality entering only through a per-row AdaLN tag that
+ *   reads a precomputed per-timestep modulation table
+ *   ("minimax-h3-mlx README", sections "Architecture" and "AdaLN precompute").
+ *   Per block and row r with tag m:
+ *     h   = LN(x) * (1 + scale1[m]) + shift1[m]
+ *     q,k,v = split_per_head(h W_qkv^T + b_qkv)        (rows interleaved per head)
+ *     q,k = RoPE3D(RMSNorm(q) * g_q), RoPE3D(RMSNorm(k) * g_k)
+ *     o   = softmax(q k^T / sqrt(d)) v                  (all rows, no mask)
+ *     x  += gate1[m] * (o W_out^T + b_out)
+ *     h2  = LN(x) * (1 + scale2[m]) + shift2[m]
+ *     x  += gate2[m] * (swiglu(h2 W_fc1^T + b_fc1) W_fc2^T + b_fc2)
+ *   ("minimax-h3-mlx README", "Validation" for the QKV interleave and the
+ *   fused [gate; value] fc1; "AdaLN: measure, do not reason" for the six
+ *   modulation tensors; "H3-metal" digest, "Checkpoint layout and media
+ *   pipeline" for QK normalisation before RoPE.)
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, 16-byte aligned, owned by the
+ *     caller.  The library allocates no device memory and keeps no pointer
+ *     after a call returns.  bf16 values are passed as uint16_t bit patterns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *     the call returns before it completes.  Calls that share a workspace or
+ *     an output buffer must be ordered by the caller (same stream).
+ *   - Every argument is checked on the host before anything is enqueued.  On
+ *     an error nothing is enqueued, a negative h3_status is returned and
+ *     h3_last_error() (thread-local) describes it.  There is no fallback to
+ *     another implementation: unsupported shapes are errors.
+ *   - Matrix layouts are row-major.  Linear weights use the PyTorch layout
+ *     W[out][in].  n_pad = h3_padded_rows(n_rows) (a multiple of 256).
+ *   - Modality tags must lie in [0, n_tags); rows are not checked on device.
+ *
+ * Supported shapes: hidden % 256 == 0 and hidden <= 8192; head_dim in
+ * {96, 128}; ffn % 128 == 0; rope_split entries even and summing to
+ * head_dim; 1 <= n_tags <= 8; 1 <= n_rows <= 2^24.
+ */
+#ifndef H3DIT_H
+#define H3DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define H3DIT_API __attribute__((visibility("default")))
+
+typedef enum h3_status {
+  H3_OK = 0,
+  H3_ERR_INVALID_ARG = -1, /* null / misaligned pointer, bad size or field */
+  H3_ERR_UNSUPPORTED = -2, /* well-formed but outside the supported shapes */
+  H3_ERR_WORKSPACE = -3,   /* workspace smaller than h3_workspace_size()  */
+  H3_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed   */
+  H3_ERR_NO_DEVICE = -5    /* no usable GPU                                */
+} h3_status;
+
+typedef enum h3_wfmt {
+  H3_W_BF16 = 0,     /* weights bf16 [out][in]                                    */
+  H3_W_INT8_G32 = 1  /* weights int8 [out][in] + bf16 scales [out][in/32]:
+                        W = bf16(q * s), one scale per 32 consecutive K elements  */
+} h3_wfmt;
+
+typedef struct h3_dims {
+  int32_t hidden;        /* D: 5376 for H3                                     */
+  int32_t heads;         /* H: 56                                              */
+  int32_t head_dim;      /* d: 128 (96 or 128 supported)                       */
+  int32_t ffn;           /* F: 14336 (SwiGLU width)                            */
+  int32_t n_tags;        /* T: modality groups in the table (3)                */
+  int32_t rope_split[3]; /* head_dim channels given to the t, h, w axes        */
+  float rope_theta;      /* rotary base (10000)                                */
+  float ln_eps;          /* AdaLN layer-norm epsilon (1e-6)                    */
+  float qk_eps;          /* QK RMSNorm epsilon (1e-6)                          */
+  int32_t wfmt;          /* h3_wfmt of the four linear layers                  */
+} h3_dims;
+
+/* Device pointers of one block's weights.  w_qkv [3*H*d][D] rows interleaved
+ * per head ([h0: q,k,v][h1: q,k,v]...), w_out [D][H*d], w_fc1 [2F][D] stacked
+ * [gate; value], w_fc2 [D][F].  s_* are the INT8 scales (ignored for bf16).
+ * Biases b_* (bf16 [out]) and the QK-norm gains q_norm / k_norm (bf16 [d])
+ * may be NULL, meaning 0 and 1. */
+typedef struct h3_block_weights {
+  const void *w_qkv, *w_out, *w_fc1, *w_fc2;
+  const uint16_t *s_qkv, *s_out, *s_fc1, *s_fc2;
+  const uint16_t *b_qkv, *b_out, *b_fc1, *b_fc2;
+  const uint16_t *q_norm, *k_norm;
+} h3_block_weights;
+
+/* ------------------------------------------------------------------------ */
+/* Whole-path entry points                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Rows rounded up to the kernels' row tile (256).  Pure. */
+H3DIT_API int64_t h3_padded_rows(int64_t n_rows);
+
+/* Bytes of scratch a forward over n_rows needs.  Pure: touches no device.
+ * Returns 0 if dims or n_rows are invalid (h3_last_error() says why). */
+H3DIT_API size_t h3_workspace_size(const h3_dims* dims, int64_t n_rows);
+
+/* One DiT block in place.
+ *   x          fp32 [n_rows][D]   residual stream, read and overwritten
+ *   tag        int32 [n_rows]     modality tag of each packed row
+ *   positions  fp32 [n_rows][3]   (t, h, w) rotary coordinates of each row
+ *   mod_table  bf16 [T][6][D]     this block's modulation vectors, in the
+ *                                 order shift1, scale1, gate1, shift2,
+ *                                 scale2, gate2 (minimax-h3-mlx README,
+ *                                 "AdaLN precompute": 18*D per timestep)
+ *   weights    host pointer to one h3_block_weights (device pointers inside)
+ *   workspace  device scratch of at least h3_workspace_size() bytes       */
+H3DIT_API h3_status h3_dit_block_forward(const h3_dims* dims, float* x, const int32_t* tag,
+                                         const float* positions, const uint16_t* mod_table,
+                                         const h3_block_weights* weights, int64_t n_rows,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* One denoising forward: blocks 0..n_blocks-1 in order, in place on x.
+ *   mod_table  bf16 [n_blocks][T][6][D]
+ *   weights    host array of n_blocks h3_block_weights
+ * The rotary table is built once and shared by all blocks. */
+H3DIT_API h3_status h3_dit_forward(const h3_dims* dims, float* x_packed, const int32_t* tag,
+                                   const float* positions, const uint16_t* mod_table,
+                                   const h3_block_weights* weights, int32_t n_blocks,
+                                   int64_t n_rows, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* Message of the last error on this thread ("" if none).  Never NULL. */
+H3DIT_API const char* h3_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Step entry points: each runs one step of the block on caller buffers.     */
+/* They are the kernels h3_dit_block_forward launches, exposed for parity   */
+/* tests and per-step timing.                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Rotary table: cs fp32 [n_pad][d/2][2] = (cos, sin) of the angle of every
+ * channel pair; pair j of axis a (width d_a) turns by
+ * positions[r][a] * theta^(-2j/d_a).  Rows >= n_rows get angle 0.
+ * ("minimax-h3-mlx README", "Architecture": 3D MM-RoPE.) */
+H3DIT_API h3_status h3_rope_table(const h3_dims* dims, const float* positions, int64_t n_rows,
+                                  float* cs, void* stream);
+
+/* AdaLN norm-modulate: h bf16 [n_rows][D] = LN(x) * (1 + scale) + shift with
+ * (shift, scale) = mod_table[tag][3*which + 0 / 1]; which = 0 before
+ * attention, 1 before the MLP.  LN: no affine, biased variance, ln_eps. */
+H3DIT_API h3_status h3_adaln_modulate(const h3_dims* dims, const float* x, const int32_t* tag,
+                                      const uint16_t* mod_table, int32_t which, int64_t n_rows,
+                                      uint16_t* h, void* stream);
+
+/* Fused QKV projection + per-head RMSNorm + RoPE + head-major scatter.
+ *   h   bf16 [n_rows][D]
+ *   cs  the rotary table from h3_rope_table
+ *   q   bf16 [H][n_pad][d], pre-multiplied by log2(e)/sqrt(d)
+ *   k   bf16 [H][n_pad][d]
+ *   vt  bf16 [H][d][n_pad]  (v transposed: keys contiguous)
+ * Rows n_rows..n_pad-1 of q, k and vt are written as zeros. */
+H3DIT_API h3_status h3_qkv_rope(const h3_dims* dims, const uint16_t* h,
+                                const h3_block_weights* weights, const float* cs, int64_t n_rows,
+                                uint16_t* q, uint16_t* k, uint16_t* vt, void* stream);
+
+/* Full attention over all n_rows keys (no mask): o bf16 [n_rows][H*d], head
+ * h in columns [h*d, (h+1)*d).  q, k, vt as written by h3_qkv_rope. */
+H3DIT_API h3_status h3_attention(const h3_dims* dims, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* vt, int64_t n_rows, uint16_t* o, void* stream);
+
+/* x fp32 [n_rows][D] += gate1[tag] * (o W_out^T + b_out);  o bf16 [n_rows][H*d]. */
+H3DIT_API h3_status h3_out_proj_residual(const h3_dims* dims, const uint16_t* o,
+                                         const h3_block_weights* weights,
+                                         const uint16_t* mod_table, const int32_t* tag,
+                                         int64_t n_rows, float* x, void* stream);
+
+/* a bf16 [n_rows][F] = silu(z[:, :F]) * z[:, F:],  z = h2 W_fc1^T + b_fc1. */
+H3DIT_API h3_status h3_mlp_fc1_swiglu(const h3_dims* dims, const uint16_t* h2,
+                                      const h3_block_weights* weights, int64_t n_rows,
+                                      uint16_t* a, void* stream);
+
+/* x fp32 [n_rows][D] += gate2[tag] * (a W_fc2^T + b_fc2);  a bf16 [n_rows][F]. */
+H3DIT_API h3_status h3_mlp_fc2_residual(const h3_dims* dims, const uint16_t* a,
+                                        const h3_block_weights* weights,
+                                        const uint16_t* mod_table, const int32_t* tag,
+                                        int64_t n_rows, float* x, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3DIT_H */

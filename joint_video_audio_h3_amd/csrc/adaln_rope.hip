@@ -1,0 +1,116 @@
+// AdaLN norm-modulate and the rotary angle table (gfx950).
+//
+// adaln_kernel: one wavefront per packed row.  The fp32 row stays in registers
+// (D/256 float4 per lane), mean and biased variance are two exact passes over
+// those registers with wavefront butterfly sums, and the row's (shift, scale)
+// pair is gathered from the per-tag modulation table:
+//   h = LN(x) * (1 + scale[tag]) + shift[tag]      -> bf16
+// (minimax-h3-mlx README, "AdaLN: measure, do not reason": x*(1+scale)+shift
+// for the norms; "AdaLN precompute": the table replaces the projection.)
+// HBM traffic per row: 4*D bytes read + 2*D bytes written.
+//
+// rope_kernel: cos/sin of pos[r][axis] * theta^(-2j/d_axis) for every channel
+// pair, evaluated in double precision once per forward (3D MM-RoPE,
+// minimax-h3-mlx README, "Architecture").
+#include "h3_device.h"
+#include "launch.h"
+
+namespace h3 {
+
+template <int VPL>  // float4 vectors per lane: ceil(D / 256)
+__global__ __launch_bounds__(256) void adaln_kernel(AdalnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.n) return;
+  const int nv = a.D >> 2;
+  const float4* xr = reinterpret_cast<const float4*>(a.x + (size_t)row * a.D);
+  float4 v[VPL];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int j = lane + 64 * i;
+    if (j < nv) {
+      v[i] = xr[j];
+    } else {
+      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  }
+  const float mean = wave_sum(s) / (float)a.D;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int j = lane + 64 * i;
+    if (j < nv) {
+      const float dx = v[i].x - mean, dy = v[i].y - mean, dz = v[i].z - mean, dw = v[i].w - mean;
+      q += (dx * dx + dy * dy) + (dz * dz + dw * dw);
+    }
+  }
+  const float var = wave_sum(q) / (float)a.D;
+  const float rstd = 1.0f / sqrtf(var + a.eps);
+  const int t = a.tag[row];
+  const u16x4* sh = reinterpret_cast<const u16x4*>(a.table + ((size_t)t * 6 + a.k_shift) * a.D);
+  const u16x4* sc = reinterpret_cast<const u16x4*>(a.table + ((size_t)t * 6 + a.k_scale) * a.D);
+  uint2* hr = reinterpret_cast<uint2*>(a.h + (size_t)row * a.D);
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int j = lane + 64 * i;
+    if (j < nv) {
+      const u16x4 s4 = sh[j], c4 = sc[j];
+      const float o0 = (v[i].x - mean) * rstd * (1.0f + bf2f(c4[0])) + bf2f(s4[0]);
+      const float o1 = (v[i].y - mean) * rstd * (1.0f + bf2f(c4[1])) + bf2f(s4[1]);
+      const float o2 = (v[i].z - mean) * rstd * (1.0f + bf2f(c4[2])) + bf2f(s4[2]);
+      const float o3 = (v[i].w - mean) * rstd * (1.0f + bf2f(c4[3])) + bf2f(s4[3]);
+      hr[j] = make_uint2(pack2bf(o0, o1), pack2bf(o2, o3));
+    }
+  }
+}
+
+#define H3_ADALN_CASE(V) \
+  case V: adaln_kernel<V><<<grid, 256, 0, s>>>(a); break;
+
+hipError_t launch_adaln(const AdalnArgs& a, hipStream_t s) {
+  const int vpl = (a.D / 4 + 63) / 64;
+  const dim3 grid((a.n + 3) / 4);
+  switch (vpl) {
+    H3_ADALN_CASE(1) H3_ADALN_CASE(2) H3_ADALN_CASE(3) H3_ADALN_CASE(4)
+    H3_ADALN_CASE(5) H3_ADALN_CASE(6) H3_ADALN_CASE(7) H3_ADALN_CASE(8)
+    H3_ADALN_CASE(9) H3_ADALN_CASE(10) H3_ADALN_CASE(11) H3_ADALN_CASE(12)
+    H3_ADALN_CASE(13) H3_ADALN_CASE(14) H3_ADALN_CASE(15) H3_ADALN_CASE(16)
+    H3_ADALN_CASE(17) H3_ADALN_CASE(18) H3_ADALN_CASE(19) H3_ADALN_CASE(20)
+    H3_ADALN_CASE(21) H3_ADALN_CASE(22) H3_ADALN_CASE(23) H3_ADALN_CASE(24)
+    H3_ADALN_CASE(25) H3_ADALN_CASE(26) H3_ADALN_CASE(27) H3_ADALN_CASE(28)
+    H3_ADALN_CASE(29) H3_ADALN_CASE(30) H3_ADALN_CASE(31) H3_ADALN_CASE(32)
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
+  const int half = a.d / 2;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)a.n_pad * half) return;
+  const int row = (int)(idx / half);
+  const int p = (int)(idx % half);
+  int axis, j, width;
+  if (p < a.split0 / 2) {
+    axis = 0; j = p; width = a.split0;
+  } else if (p < (a.split0 + a.split1) / 2) {
+    axis = 1; j = p - a.split0 / 2; width = a.split1;
+  } else {
+    axis = 2; j = p - (a.split0 + a.split1) / 2; width = a.split2;
+  }
+  const double pos = row < a.n ? (double)a.pos[(size_t)row * 3 + axis] : 0.0;
+  const double ang = pos * pow(a.theta, -2.0 * (double)j / (double)width);
+  double sn, cn;
+  sincos(ang, &sn, &cn);
+  reinterpret_cast<float2*>(a.cs)[idx] = make_float2((float)cn, (float)sn);
+}
+
+hipError_t launch_rope_table(const RopeArgs& a, hipStream_t s) {
+  const int64_t total = (int64_t)a.n_pad * (a.d / 2);
+  rope_kernel<<<dim3((unsigned)((total + 255) / 256)), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace h3

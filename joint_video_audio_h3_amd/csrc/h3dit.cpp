@@ -1,0 +1,458 @@
+// C ABI of the H3 DiT block forward: argument checks, workspace carve-up and
+// the launch sequence of one block / one forward.  All checks happen on the
+// host before the first launch; nothing is enqueued on an error.
+#include "../../include/h3dit.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <algorithm>
+#include <cstring>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+h3_status fail(h3_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxRows = int64_t(1) << 24;
+
+int64_t pad_rows(int64_t n) { return (n + 255) / 256 * 256; }
+
+h3_status check_dims(const h3_dims* d) {
+  if (!d) return fail(H3_ERR_INVALID_ARG, "dims is NULL");
+  if (d->hidden <= 0 || d->heads <= 0 || d->head_dim <= 0 || d->ffn <= 0 || d->n_tags <= 0)
+    return fail(H3_ERR_INVALID_ARG, "dims fields must be positive");
+  if (d->hidden % 256 != 0 || d->hidden > 8192)
+    return fail(H3_ERR_UNSUPPORTED, "hidden=%d: need a multiple of 256, at most 8192", d->hidden);
+  if (d->head_dim != 96 && d->head_dim != 128)
+    return fail(H3_ERR_UNSUPPORTED, "head_dim=%d: supported 96 or 128", d->head_dim);
+  if ((d->heads * d->head_dim) % 64 != 0)
+    return fail(H3_ERR_UNSUPPORTED, "heads*head_dim=%d must be a multiple of 64",
+                d->heads * d->head_dim);
+  if (d->ffn % 128 != 0) return fail(H3_ERR_UNSUPPORTED, "ffn=%d must be a multiple of 128", d->ffn);
+  if (d->n_tags > 8) return fail(H3_ERR_UNSUPPORTED, "n_tags=%d: at most 8", d->n_tags);
+  int sum = 0;
+  for (int i = 0; i < 3; ++i) {
+    if (d->rope_split[i] < 0 || d->rope_split[i] % 2 != 0)
+      return fail(H3_ERR_INVALID_ARG, "rope_split[%d]=%d must be even and >= 0", i, d->rope_split[i]);
+    sum += d->rope_split[i];
+  }
+  if (sum != d->head_dim)
+    return fail(H3_ERR_INVALID_ARG, "rope_split sums to %d, head_dim is %d", sum, d->head_dim);
+  if (!(d->rope_theta > 0.f) || !(d->ln_eps >= 0.f) || !(d->qk_eps >= 0.f) ||
+      !std::isfinite(d->rope_theta))
+    return fail(H3_ERR_INVALID_ARG, "rope_theta must be > 0 and epsilons >= 0");
+  if (d->wfmt != H3_W_BF16 && d->wfmt != H3_W_INT8_G32)
+    return fail(H3_ERR_INVALID_ARG, "wfmt=%d unknown", d->wfmt);
+  return H3_OK;
+}
+
+h3_status check_rows(int64_t n) {
+  if (n <= 0 || n > kMaxRows) return fail(H3_ERR_INVALID_ARG, "n_rows=%lld out of [1, 2^24]", (long long)n);
+  return H3_OK;
+}
+
+#define H3_NEED(ptr, name)                                                          \
+  do {                                                                              \
+    if (!(ptr)) return fail(H3_ERR_INVALID_ARG, "%s is NULL", name);               \
+    if (!al16(ptr)) return fail(H3_ERR_INVALID_ARG, "%s is not 16-byte aligned", name); \
+  } while (0)
+#define H3_OPT(ptr, name)                                                           \
+  do {                                                                              \
+    if ((ptr) && !al16(ptr)) return fail(H3_ERR_INVALID_ARG, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+h3_status check_linear(const h3_dims* d, const void* w, const uint16_t* s, const uint16_t* b,
+                       const char* wn, const char* sn, const char* bn) {
+  H3_NEED(w, wn);
+  if (d->wfmt == H3_W_INT8_G32) H3_NEED(s, sn);
+  H3_OPT(b, bn);
+  return H3_OK;
+}
+
+h3_status check_weights(const h3_dims* d, const h3_block_weights* w, bool qkv, bool out, bool fc1,
+                        bool fc2) {
+  if (!w) return fail(H3_ERR_INVALID_ARG, "weights is NULL");
+  h3_status st;
+  if (qkv && (st = check_linear(d, w->w_qkv, w->s_qkv, w->b_qkv, "w_qkv", "s_qkv", "b_qkv")) != H3_OK)
+    return st;
+  if (out && (st = check_linear(d, w->w_out, w->s_out, w->b_out, "w_out", "s_out", "b_out")) != H3_OK)
+    return st;
+  if (fc1 && (st = check_linear(d, w->w_fc1, w->s_fc1, w->b_fc1, "w_fc1", "s_fc1", "b_fc1")) != H3_OK)
+    return st;
+  if (fc2 && (st = check_linear(d, w->w_fc2, w->s_fc2, w->b_fc2, "w_fc2", "s_fc2", "b_fc2")) != H3_OK)
+    return st;
+  if (qkv) {
+    H3_OPT(w->q_norm, "q_norm");
+    H3_OPT(w->k_norm, "k_norm");
+  }
+  return H3_OK;
+}
+
+h3_status check_device() {
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return fail(H3_ERR_NO_DEVICE, "no HIP device available (%s)", hipGetErrorString(e));
+  }
+  return H3_OK;
+}
+
+h3_status hip_ok(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(H3_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return H3_OK;
+}
+
+// ---------------------------------------------------------------- workspace
+struct Arena {
+  float* cs;
+  uint16_t *h, *q, *k, *vt, *o, *a;
+  size_t bytes;
+};
+
+size_t up256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Lifetimes inside a block: cs (whole forward); h (norm1 -> QKV, then norm2 ->
+// FC1); q/k/vt (QKV -> attention); o (attention -> out-proj); a (FC1 -> FC2)
+// reuses the q/k/vt arena, which is dead once attention has run.
+Arena carve(const h3_dims& d, int64_t n, char* base) {
+  const size_t np = (size_t)pad_rows(n);
+  const size_t D = d.hidden, Di = (size_t)d.heads * d.head_dim, F = d.ffn;
+  Arena a{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += up256(bytes);
+    return p;
+  };
+  a.cs = reinterpret_cast<float*>(take(np * d.head_dim * 4));
+  a.h = reinterpret_cast<uint16_t*>(take(np * D * 2));
+  const size_t head_buf = np * Di * 2;
+  const size_t qkv_bytes = std::max(3 * up256(head_buf), up256(np * F * 2));
+  char* qkv = take(qkv_bytes);
+  a.q = reinterpret_cast<uint16_t*>(qkv);
+  a.k = reinterpret_cast<uint16_t*>(qkv ? qkv + up256(head_buf) : nullptr);
+  a.vt = reinterpret_cast<uint16_t*>(qkv ? qkv + 2 * up256(head_buf) : nullptr);
+  a.a = reinterpret_cast<uint16_t*>(qkv);
+  a.o = reinterpret_cast<uint16_t*>(take(np * Di * 2));
+  a.bytes = off;
+  return a;
+}
+
+// ---------------------------------------------------------------- launches
+h3::GemmArgs gemm_base(const h3_dims& d, const uint16_t* A, const void* B, const uint16_t* Bs,
+                       const uint16_t* bias, int M, int K, int n_out) {
+  h3::GemmArgs g{};
+  g.A = A;
+  g.B = B;
+  g.Bs = Bs;
+  g.bias = bias;
+  g.M = M;
+  g.K = K;
+  g.n_out = n_out;
+  return g;
+}
+
+hipError_t do_rope(const h3_dims& d, const float* pos, int64_t n, float* cs, hipStream_t s) {
+  h3::RopeArgs r{};
+  r.pos = pos;
+  r.cs = cs;
+  r.n = (int)n;
+  r.n_pad = (int)pad_rows(n);
+  r.d = d.head_dim;
+  r.split0 = d.rope_split[0];
+  r.split1 = d.rope_split[1];
+  r.split2 = d.rope_split[2];
+  r.theta = d.rope_theta;
+  return h3::launch_rope_table(r, s);
+}
+
+hipError_t do_adaln(const h3_dims& d, const float* x, const int32_t* tag, const uint16_t* table,
+                    int which, int64_t n, uint16_t* h, hipStream_t s) {
+  h3::AdalnArgs a{};
+  a.x = x;
+  a.tag = tag;
+  a.table = table;
+  a.h = h;
+  a.n = (int)n;
+  a.D = d.hidden;
+  a.k_shift = 3 * which;
+  a.k_scale = 3 * which + 1;
+  a.eps = d.ln_eps;
+  return h3::launch_adaln(a, s);
+}
+
+hipError_t do_qkv(const h3_dims& d, const uint16_t* h, const h3_block_weights& w, const float* cs,
+                  int64_t n, uint16_t* q, uint16_t* k, uint16_t* vt, hipStream_t s) {
+  const int Di = d.heads * d.head_dim;
+  h3::GemmArgs g = gemm_base(d, h, w.w_qkv, w.s_qkv, w.b_qkv, (int)n, d.hidden, 3 * Di);
+  g.q = q;
+  g.k = k;
+  g.vt = vt;
+  g.n_pad = (int)pad_rows(n);
+  g.heads = d.heads;
+  g.head_dim = d.head_dim;
+  g.gq = w.q_norm;
+  g.gk = w.k_norm;
+  g.cs = cs;
+  g.qk_eps = d.qk_eps;
+  g.q_scale = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
+  return h3::launch_gemm(h3::EPI_QKV, d.wfmt, g, s);
+}
+
+hipError_t do_attn(const h3_dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* vt,
+                   int64_t n, uint16_t* o, hipStream_t s) {
+  h3::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.vt = vt;
+  a.o = o;
+  a.n = (int)n;
+  a.n_pad = (int)pad_rows(n);
+  a.heads = d.heads;
+  a.head_dim = d.head_dim;
+  return h3::launch_attention(a, s);
+}
+
+hipError_t do_resid(const h3_dims& d, const uint16_t* A, const void* W, const uint16_t* S,
+                    const uint16_t* b, int K, const uint16_t* table, int kgate, const int32_t* tag,
+                    int64_t n, float* x, hipStream_t s) {
+  h3::GemmArgs g = gemm_base(d, A, W, S, b, (int)n, K, d.hidden);
+  g.x = x;
+  g.ldx = d.hidden;
+  g.gate_tab = table + (size_t)kgate * d.hidden;
+  g.tag = tag;
+  g.tag_stride = 6 * d.hidden;
+  return h3::launch_gemm(h3::EPI_RESID, d.wfmt, g, s);
+}
+
+hipError_t do_fc1(const h3_dims& d, const uint16_t* h2, const h3_block_weights& w, int64_t n,
+                  uint16_t* a, hipStream_t s) {
+  h3::GemmArgs g = gemm_base(d, h2, w.w_fc1, w.s_fc1, w.b_fc1, (int)n, d.hidden, 2 * d.ffn);
+  g.out = a;
+  g.ffn = d.ffn;
+  return h3::launch_gemm(h3::EPI_SWIGLU, d.wfmt, g, s);
+}
+
+h3_status run_block(const h3_dims& d, float* x, const int32_t* tag, const uint16_t* table,
+                    const h3_block_weights& w, int64_t n, const Arena& ar, hipStream_t s) {
+  const int Di = d.heads * d.head_dim;
+  h3_status st;
+  if ((st = hip_ok(do_adaln(d, x, tag, table, 0, n, ar.h, s), "adaln (attention)")) != H3_OK) return st;
+  if ((st = hip_ok(do_qkv(d, ar.h, w, ar.cs, n, ar.q, ar.k, ar.vt, s), "qkv+rope")) != H3_OK) return st;
+  if ((st = hip_ok(do_attn(d, ar.q, ar.k, ar.vt, n, ar.o, s), "attention")) != H3_OK) return st;
+  if ((st = hip_ok(do_resid(d, ar.o, w.w_out, w.s_out, w.b_out, Di, table, 2, tag, n, x, s),
+                   "out-proj+gate")) != H3_OK)
+    return st;
+  if ((st = hip_ok(do_adaln(d, x, tag, table, 1, n, ar.h, s), "adaln (mlp)")) != H3_OK) return st;
+  if ((st = hip_ok(do_fc1(d, ar.h, w, n, ar.a, s), "fc1+swiglu")) != H3_OK) return st;
+  if ((st = hip_ok(do_resid(d, ar.a, w.w_fc2, w.s_fc2, w.b_fc2, d.ffn, table, 5, tag, n, x, s),
+                   "fc2+gate")) != H3_OK)
+    return st;
+  return H3_OK;
+}
+
+h3_status check_forward_common(const h3_dims* dims, const float* x, const int32_t* tag,
+                               const float* pos, const uint16_t* table, int64_t n, void* ws,
+                               size_t ws_bytes) {
+  h3_status st;
+  if ((st = check_dims(dims)) != H3_OK) return st;
+  if ((st = check_rows(n)) != H3_OK) return st;
+  H3_NEED(x, "x");
+  H3_NEED(tag, "modality_tag");
+  H3_NEED(pos, "positions");
+  H3_NEED(table, "mod_table");
+  H3_NEED(ws, "workspace");
+  const size_t need = carve(*dims, n, nullptr).bytes;
+  if (ws_bytes < need)
+    return fail(H3_ERR_WORKSPACE, "workspace is %zu bytes, %zu needed", ws_bytes, need);
+  return H3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t h3_padded_rows(int64_t n_rows) { return n_rows <= 0 ? 0 : pad_rows(n_rows); }
+
+size_t h3_workspace_size(const h3_dims* dims, int64_t n_rows) {
+  if (check_dims(dims) != H3_OK || check_rows(n_rows) != H3_OK) return 0;
+  return carve(*dims, n_rows, nullptr).bytes;
+}
+
+const char* h3_last_error(void) { return g_err.c_str(); }
+
+h3_status h3_dit_block_forward(const h3_dims* dims, float* x, const int32_t* tag,
+                               const float* positions, const uint16_t* mod_table,
+                               const h3_block_weights* weights, int64_t n_rows, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_forward_common(dims, x, tag, positions, mod_table, n_rows, workspace,
+                                 workspace_bytes)) != H3_OK)
+    return st;
+  if ((st = check_weights(dims, weights, true, true, true, true)) != H3_OK) return st;
+  if ((st = check_device()) != H3_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const Arena ar = carve(*dims, n_rows, static_cast<char*>(workspace));
+  if ((st = hip_ok(do_rope(*dims, positions, n_rows, ar.cs, s), "rope table")) != H3_OK) return st;
+  return run_block(*dims, x, tag, mod_table, *weights, n_rows, ar, s);
+}
+
+h3_status h3_dit_forward(const h3_dims* dims, float* x, const int32_t* tag, const float* positions,
+                         const uint16_t* mod_table, const h3_block_weights* weights,
+                         int32_t n_blocks, int64_t n_rows, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_forward_common(dims, x, tag, positions, mod_table, n_rows, workspace,
+                                 workspace_bytes)) != H3_OK)
+    return st;
+  if (n_blocks <= 0) return fail(H3_ERR_INVALID_ARG, "n_blocks=%d must be positive", n_blocks);
+  if (!weights) return fail(H3_ERR_INVALID_ARG, "weights is NULL");
+  for (int b = 0; b < n_blocks; ++b) {
+    if ((st = check_weights(dims, &weights[b], true, true, true, true)) != H3_OK) {
+      std::string m = g_err;
+      return fail(st, "block %d: %s", b, m.c_str());
+    }
+  }
+  if ((st = check_device()) != H3_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const Arena ar = carve(*dims, n_rows, static_cast<char*>(workspace));
+  if ((st = hip_ok(do_rope(*dims, positions, n_rows, ar.cs, s), "rope table")) != H3_OK) return st;
+  const size_t tstride = (size_t)dims->n_tags * 6 * dims->hidden;
+  for (int b = 0; b < n_blocks; ++b) {
+    if ((st = run_block(*dims, x, tag, mod_table + b * tstride, weights[b], n_rows, ar, s)) != H3_OK) {
+      std::string m = g_err;
+      return fail(st, "block %d: %s", b, m.c_str());
+    }
+  }
+  return H3_OK;
+}
+
+h3_status h3_rope_table(const h3_dims* dims, const float* positions, int64_t n_rows, float* cs,
+                        void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_dims(dims)) != H3_OK || (st = check_rows(n_rows)) != H3_OK) return st;
+  H3_NEED(positions, "positions");
+  H3_NEED(cs, "cs");
+  if ((st = check_device()) != H3_OK) return st;
+  return hip_ok(do_rope(*dims, positions, n_rows, cs, reinterpret_cast<hipStream_t>(stream)),
+                "rope table");
+}
+
+h3_status h3_adaln_modulate(const h3_dims* dims, const float* x, const int32_t* tag,
+                            const uint16_t* mod_table, int32_t which, int64_t n_rows, uint16_t* h,
+                            void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_dims(dims)) != H3_OK || (st = check_rows(n_rows)) != H3_OK) return st;
+  H3_NEED(x, "x");
+  H3_NEED(tag, "modality_tag");
+  H3_NEED(mod_table, "mod_table");
+  H3_NEED(h, "h");
+  if (which != 0 && which != 1) return fail(H3_ERR_INVALID_ARG, "which=%d must be 0 or 1", which);
+  if ((st = check_device()) != H3_OK) return st;
+  return hip_ok(do_adaln(*dims, x, tag, mod_table, which, n_rows, h,
+                         reinterpret_cast<hipStream_t>(stream)),
+                "adaln");
+}
+
+h3_status h3_qkv_rope(const h3_dims* dims, const uint16_t* h, const h3_block_weights* weights,
+                      const float* cs, int64_t n_rows, uint16_t* q, uint16_t* k, uint16_t* vt,
+                      void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_dims(dims)) != H3_OK || (st = check_rows(n_rows)) != H3_OK) return st;
+  if ((st = check_weights(dims, weights, true, false, false, false)) != H3_OK) return st;
+  H3_NEED(h, "h");
+  H3_NEED(cs, "cs");
+  H3_NEED(q, "q");
+  H3_NEED(k, "k");
+  H3_NEED(vt, "vt");
+  if ((st = check_device()) != H3_OK) return st;
+  return hip_ok(do_qkv(*dims, h, *weights, cs, n_rows, q, k, vt, reinterpret_cast<hipStream_t>(stream)),
+                "qkv+rope");
+}
+
+h3_status h3_attention(const h3_dims* dims, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* vt, int64_t n_rows, uint16_t* o, void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_dims(dims)) != H3_OK || (st = check_rows(n_rows)) != H3_OK) return st;
+  H3_NEED(q, "q");
+  H3_NEED(k, "k");
+  H3_NEED(vt, "vt");
+  H3_NEED(o, "o");
+  if ((st = check_device()) != H3_OK) return st;
+  return hip_ok(do_attn(*dims, q, k, vt, n_rows, o, reinterpret_cast<hipStream_t>(stream)),
+                "attention");
+}
+
+h3_status h3_out_proj_residual(const h3_dims* dims, const uint16_t* o,
+                               const h3_block_weights* weights, const uint16_t* mod_table,
+                               const int32_t* tag, int64_t n_rows, float* x, void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_dims(dims)) != H3_OK || (st = check_rows(n_rows)) != H3_OK) return st;
+  if ((st = check_weights(dims, weights, false, true, false, false)) != H3_OK) return st;
+  H3_NEED(o, "o");
+  H3_NEED(mod_table, "mod_table");
+  H3_NEED(tag, "modality_tag");
+  H3_NEED(x, "x");
+  if ((st = check_device()) != H3_OK) return st;
+  return hip_ok(do_resid(*dims, o, weights->w_out, weights->s_out, weights->b_out,
+                         dims->heads * dims->head_dim, mod_table, 2, tag, n_rows, x,
+                         reinterpret_cast<hipStream_t>(stream)),
+                "out-proj+gate");
+}
+
+h3_status h3_mlp_fc1_swiglu(const h3_dims* dims, const uint16_t* h2, const h3_block_weights* weights,
+                            int64_t n_rows, uint16_t* a, void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_dims(dims)) != H3_OK || (st = check_rows(n_rows)) != H3_OK) return st;
+  if ((st = check_weights(dims, weights, false, false, true, false)) != H3_OK) return st;
+  H3_NEED(h2, "h2");
+  H3_NEED(a, "a");
+  if ((st = check_device()) != H3_OK) return st;
+  return hip_ok(do_fc1(*dims, h2, *weights, n_rows, a, reinterpret_cast<hipStream_t>(stream)),
+                "fc1+swiglu");
+}
+
+h3_status h3_mlp_fc2_residual(const h3_dims* dims, const uint16_t* a,
+                              const h3_block_weights* weights, const uint16_t* mod_table,
+                              const int32_t* tag, int64_t n_rows, float* x, void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_dims(dims)) != H3_OK || (st = check_rows(n_rows)) != H3_OK) return st;
+  if ((st = check_weights(dims, weights, false, false, false, true)) != H3_OK) return st;
+  H3_NEED(a, "a");
+  H3_NEED(mod_table, "mod_table");
+  H3_NEED(tag, "modality_tag");
+  H3_NEED(x, "x");
+  if ((st = check_device()) != H3_OK) return st;
+  return hip_ok(do_resid(*dims, a, weights->w_fc2, weights->s_fc2, weights->b_fc2, dims->ffn,
+                         mod_table, 5, tag, n_rows, x, reinterpret_cast<hipStream_t>(stream)),
+                "fc2+gate");
+}
+
+}  // extern "C"

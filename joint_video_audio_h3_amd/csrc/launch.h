@@ -1,0 +1,55 @@
+// Host-side launchers of the gfx950 kernels (one per step of the block).
+// Shapes are validated by the C-ABI layer before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h3 {
+
+struct RopeArgs {
+  const float* pos;     // [n][3]
+  float* cs;            // [n_pad][d/2][2]
+  int n, n_pad, d;
+  int split0, split1, split2;
+  double theta;
+};
+hipError_t launch_rope_table(const RopeArgs& a, hipStream_t s);
+
+struct AdalnArgs {
+  const float* x;        // [n][D]
+  const int32_t* tag;    // [n]
+  const uint16_t* table; // [T][6][D]
+  uint16_t* h;           // [n][D]
+  int n, D, k_shift, k_scale;
+  float eps;
+};
+hipError_t launch_adaln(const AdalnArgs& a, hipStream_t s);
+
+enum Epi { EPI_RESID = 0, EPI_SWIGLU = 1, EPI_QKV = 2 };
+
+struct GemmArgs {
+  const uint16_t* A;      // [M][K] bf16
+  const void* B;          // [Nw][K] bf16 or int8
+  const uint16_t* Bs;     // [Nw][K/32] bf16 scales (int8 only)
+  const uint16_t* bias;   // [Nw] or null
+  int M, K;
+  int n_out;              // GEMM output columns (= B rows used)
+  // EPI_RESID: x[M][ldx] += gate_tab[tag*6*D + col] * (acc + bias)
+  float* x; int ldx;
+  const uint16_t* gate_tab; const int32_t* tag; int tag_stride;
+  // EPI_SWIGLU: out[M][ffn] = silu(gate) * value, gate rows [0,ffn), value rows [ffn, 2ffn)
+  uint16_t* out; int ffn;
+  // EPI_QKV
+  uint16_t *q, *k, *vt; int n_pad, heads, head_dim;
+  const uint16_t *gq, *gk; const float* cs; float qk_eps, q_scale;
+};
+hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const uint16_t *q, *k, *vt;  // [H][n_pad][d], [H][n_pad][d], [H][d][n_pad]
+  uint16_t* o;                 // [n][H*d]
+  int n, n_pad, heads, head_dim;
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+}  // namespace h3

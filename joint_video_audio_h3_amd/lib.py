@@ -1,0 +1,207 @@
+"""ctypes binding of libh3dit.so (the C ABI declared in include/h3dit.h).
+
+Argument marshalling only: every step of the block runs in the HIP kernels
+behind the C ABI.  torch is used for device memory and streams -- tensors are
+passed by ``data_ptr()`` and the current HIP stream by its handle.  There is no
+CPU path: if the library is missing, :func:`load` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence
+
+from .build import LIB_PATH
+
+c_i32, c_i64, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+H3_OK, H3_ERR_INVALID_ARG, H3_ERR_UNSUPPORTED, H3_ERR_WORKSPACE, H3_ERR_HIP, H3_ERR_NO_DEVICE = 0, -1, -2, -3, -4, -5
+
+
+class H3Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"h3dit status {status}: {message}")
+        self.status = status
+
+
+class H3Dims(ctypes.Structure):
+    _fields_ = [("hidden", c_i32), ("heads", c_i32), ("head_dim", c_i32), ("ffn", c_i32),
+                ("n_tags", c_i32), ("rope_split", c_i32 * 3), ("rope_theta", c_f32),
+                ("ln_eps", c_f32), ("qk_eps", c_f32), ("wfmt", c_i32)]
+
+
+WEIGHT_FIELDS = ["w_qkv", "w_out", "w_fc1", "w_fc2", "s_qkv", "s_out", "s_fc1", "s_fc2",
+                 "b_qkv", "b_out", "b_fc1", "b_fc2", "q_norm", "k_norm"]
+
+
+class H3BlockWeights(ctypes.Structure):
+    _fields_ = [(n, c_vp) for n in WEIGHT_FIELDS]
+
+
+# name -> (restype, argtypes), mirroring include/h3dit.h
+_SIGS = {
+    "h3_padded_rows": (c_i64, [c_i64]),
+    "h3_workspace_size": (c_sz, [ctypes.POINTER(H3Dims), c_i64]),
+    "h3_last_error": (ctypes.c_char_p, []),
+    "h3_dit_block_forward": (c_i32, [ctypes.POINTER(H3Dims), c_vp, c_vp, c_vp, c_vp,
+                                     ctypes.POINTER(H3BlockWeights), c_i64, c_vp, c_sz, c_vp]),
+    "h3_dit_forward": (c_i32, [ctypes.POINTER(H3Dims), c_vp, c_vp, c_vp, c_vp,
+                               ctypes.POINTER(H3BlockWeights), c_i32, c_i64, c_vp, c_sz, c_vp]),
+    "h3_rope_table": (c_i32, [ctypes.POINTER(H3Dims), c_vp, c_i64, c_vp, c_vp]),
+    "h3_adaln_modulate": (c_i32, [ctypes.POINTER(H3Dims), c_vp, c_vp, c_vp, c_i32, c_i64, c_vp, c_vp]),
+    "h3_qkv_rope": (c_i32, [ctypes.POINTER(H3Dims), c_vp, ctypes.POINTER(H3BlockWeights), c_vp,
+                            c_i64, c_vp, c_vp, c_vp, c_vp]),
+    "h3_attention": (c_i32, [ctypes.POINTER(H3Dims), c_vp, c_vp, c_vp, c_i64, c_vp, c_vp]),
+    "h3_out_proj_residual": (c_i32, [ctypes.POINTER(H3Dims), c_vp, ctypes.POINTER(H3BlockWeights),
+                                     c_vp, c_vp, c_i64, c_vp, c_vp]),
+    "h3_mlp_fc1_swiglu": (c_i32, [ctypes.POINTER(H3Dims), c_vp, ctypes.POINTER(H3BlockWeights),
+                                  c_i64, c_vp, c_vp]),
+    "h3_mlp_fc2_residual": (c_i32, [ctypes.POINTER(H3Dims), c_vp, ctypes.POINTER(H3BlockWeights),
+                                    c_vp, c_vp, c_i64, c_vp, c_vp]),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (no fallback: raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "(the H3 forward has no CPU path)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().h3_last_error().decode()
+
+
+def _check(status: int):
+    if status != H3_OK:
+        raise H3Error(status, last_error())
+
+
+def make_dims(d) -> H3Dims:
+    """H3Dims from any object with the h3_dims field names (e.g. synth.Dims)."""
+    s = H3Dims()
+    s.hidden, s.heads, s.head_dim, s.ffn, s.n_tags = d.hidden, d.heads, d.head_dim, d.ffn, d.n_tags
+    s.rope_split[:] = list(d.rope_split)
+    s.rope_theta, s.ln_eps, s.qk_eps, s.wfmt = d.rope_theta, d.ln_eps, d.qk_eps, d.wfmt
+    return s
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def make_weights(block: Dict) -> H3BlockWeights:
+    """H3BlockWeights from a dict of device tensors (missing / None = NULL)."""
+    w = H3BlockWeights()
+    for n in WEIGHT_FIELDS:
+        setattr(w, n, _ptr(block.get(n)))
+    return w
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return int(stream) if isinstance(stream, int) else stream.cuda_stream
+
+
+def padded_rows(n: int) -> int:
+    return load().h3_padded_rows(n)
+
+
+def workspace_size(dims, n_rows: int) -> int:
+    sz = load().h3_workspace_size(ctypes.byref(make_dims(dims)), n_rows)
+    if sz == 0:
+        raise H3Error(H3_ERR_INVALID_ARG, last_error())
+    return sz
+
+
+def alloc_workspace(dims, n_rows: int, device="cuda"):
+    import torch
+    return torch.empty(workspace_size(dims, n_rows), dtype=torch.uint8, device=device)
+
+
+def dit_block_forward(dims, x, tag, positions, mod_table, block: Dict, workspace, stream=None):
+    d = make_dims(dims)
+    w = make_weights(block)
+    _check(load().h3_dit_block_forward(ctypes.byref(d), x.data_ptr(), tag.data_ptr(),
+                                       positions.data_ptr(), mod_table.data_ptr(), ctypes.byref(w),
+                                       x.shape[0], workspace.data_ptr(), workspace.numel(),
+                                       _stream(stream)))
+
+
+def dit_forward(dims, x, tag, positions, mod_table, blocks: Sequence[Dict], workspace, stream=None):
+    d = make_dims(dims)
+    arr = (H3BlockWeights * len(blocks))(*[make_weights(b) for b in blocks])
+    _check(load().h3_dit_forward(ctypes.byref(d), x.data_ptr(), tag.data_ptr(), positions.data_ptr(),
+                                 mod_table.data_ptr(), arr, len(blocks), x.shape[0],
+                                 workspace.data_ptr(), workspace.numel(), _stream(stream)))
+
+
+def rope_table(dims, positions, n_rows, cs, stream=None):
+    _check(load().h3_rope_table(ctypes.byref(make_dims(dims)), positions.data_ptr(), n_rows,
+                                cs.data_ptr(), _stream(stream)))
+
+
+def adaln_modulate(dims, x, tag, mod_table, which, h, stream=None):
+    _check(load().h3_adaln_modulate(ctypes.byref(make_dims(dims)), x.data_ptr(), tag.data_ptr(),
+                                    mod_table.data_ptr(), which, x.shape[0], h.data_ptr(),
+                                    _stream(stream)))
+
+
+def qkv_rope(dims, h, block, cs, n_rows, q, k, vt, stream=None):
+    w = make_weights(block)
+    _check(load().h3_qkv_rope(ctypes.byref(make_dims(dims)), h.data_ptr(), ctypes.byref(w),
+                              cs.data_ptr(), n_rows, q.data_ptr(), k.data_ptr(), vt.data_ptr(),
+                              _stream(stream)))
+
+
+def attention(dims, q, k, vt, n_rows, o, stream=None):
+    _check(load().h3_attention(ctypes.byref(make_dims(dims)), q.data_ptr(), k.data_ptr(),
+                               vt.data_ptr(), n_rows, o.data_ptr(), _stream(stream)))
+
+
+def out_proj_residual(dims, o, block, mod_table, tag, x, stream=None):
+    w = make_weights(block)
+    _check(load().h3_out_proj_residual(ctypes.byref(make_dims(dims)), o.data_ptr(), ctypes.byref(w),
+                                       mod_table.data_ptr(), tag.data_ptr(), x.shape[0],
+                                       x.data_ptr(), _stream(stream)))
+
+
+def mlp_fc1_swiglu(dims, h2, block, a, stream=None):
+    w = make_weights(block)
+    _check(load().h3_mlp_fc1_swiglu(ctypes.byref(make_dims(dims)), h2.data_ptr(), ctypes.byref(w),
+                                    h2.shape[0], a.data_ptr(), _stream(stream)))
+
+
+def mlp_fc2_residual(dims, a, block, mod_table, tag, x, stream=None):
+    w = make_weights(block)
+    _check(load().h3_mlp_fc2_residual(ctypes.byref(make_dims(dims)), a.data_ptr(), ctypes.byref(w),
+                                      mod_table.data_ptr(), tag.data_ptr(), x.shape[0],
+                                      x.data_ptr(), _stream(stream)))
+
+
+def to_device_block(block: Dict, device="cuda") -> Dict:
+    """Host weight dict (numpy: uint16 bf16 bits / int8 / None) -> device tensors."""
+    import numpy as np
+    import torch
+    out = {}
+    for k, v in block.items():
+        if v is None:
+            out[k] = None
+        elif v.dtype == np.uint16:
+            out[k] = torch.from_numpy(v.view(np.int16)).to(device)
+        else:
+            out[k] = torch.from_numpy(v).to(device)
+    return out

@@ -46,6 +46,7 @@ import numpy as np
 _TID = {
     "x": 0, "w_qkv": 1, "b_qkv": 2, "w_out": 3, "b_out": 4, "w_fc1": 5,
     "b_fc1": 6, "w_fc2": 7, "b_fc2": 8, "q_norm": 9, "k_norm": 10, "table": 11,
+    "h": 12, "o": 13, "a": 14, "q": 15, "k": 16, "v": 17, "tags": 18, "pos": 19,
 }
 TAG_TEXT, TAG_AUDIO, TAG_VIDEO = 0, 1, 2
 WFMT_BF16, WFMT_INT8_G32 = 0, 1
@@ -164,6 +165,25 @@ def packed_layout(wl: Workload) -> Tuple[np.ndarray, np.ndarray]:
 
 
 # ---------------------------------------------------------------- tensors
+def make_activation_bf16(n: int, width: int, name: str, seed: int = 0, std: float = 1.0) -> np.ndarray:
+    """bf16 bits [n, width] ~ N(0, std^2): stand-alone input of one step ('h', 'o', 'a', ...)."""
+    a = _rng(seed, 0, name).standard_normal((n, width), dtype=np.float32)
+    return f32_to_bf16_bits(a * np.float32(std))
+
+
+def make_tags(n: int, n_tags: int = 3, seed: int = 0) -> np.ndarray:
+    """Random modality tags int32 [n] (for steps tested away from a packed layout)."""
+    return _rng(seed, 0, "tags").integers(0, n_tags, n).astype(np.int32)
+
+
+def make_positions(n: int, seed: int = 0) -> np.ndarray:
+    """Random rotary coordinates float32 [n, 3] in [0, 250), fractional and integral mixed."""
+    r = _rng(seed, 0, "pos")
+    p = r.uniform(0, 250, (n, 3))
+    p[::2] = np.floor(p[::2])
+    return p.astype(np.float32)
+
+
 def make_x(wl_or_n, dims: Dims, seed: int = 0) -> np.ndarray:
     n = wl_or_n.n_rows if isinstance(wl_or_n, Workload) else int(wl_or_n)
     return _rng(seed, 0, "x").standard_normal((n, dims.hidden), dtype=np.float32)

@@ -5,7 +5,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 its Python binding) never touches it.
 """
 from .h3_block import (  # noqa: F401
-    MOD_NAMES, adaln_modulate, apply_rope, attention, bf16_to_f64, block_forward,
+    MOD_NAMES, adaln_modulate, apply_rope, attention, bf16_to_f64, bias, block_forward,
     block_steps, build_mod_table, dequant_int8_g32, dit_forward, layer_norm,
     merge_heads, modulation_from_table, modulation_live, qkv_split, rms_norm,
     rope_angles, round_to_bf16, silu, swiglu, weight,

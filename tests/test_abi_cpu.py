@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, computes workspace sizes, and rejects bad arguments on the
+host before any launch.  No compute entry point is ever called with arguments
+that could pass validation while a GPU is present."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from joint_video_audio_h3_amd import lib, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h3dit.h")
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lib.LIB_PATH):
+        pytest.skip("libh3dit.so not built")
+    return lib.load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    return re.findall(r"H3DIT_API\s+[\w\s\*]+?\b(h3_\w+)\s*\(", src)
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(lib._SIGS), "binding and header disagree"
+
+
+def test_struct_layouts_match_header():
+    assert ctypes.sizeof(lib.H3Dims) == 4 * 12
+    assert ctypes.sizeof(lib.H3BlockWeights) == 8 * 14
+
+
+def test_padded_rows_and_workspace(L):
+    assert lib.padded_rows(1) == 256 and lib.padded_rows(256) == 256 and lib.padded_rows(257) == 512
+    d = synth.H3_DIMS
+    n = 49840
+    np_ = lib.padded_rows(n)
+    ws = lib.workspace_size(d, n)
+    # rope cos/sin + h + q,k,v^T (a aliases them) + o, each rounded up to 256 B
+    expect = np_ * 128 * 4 + np_ * 5376 * 2 + 3 * np_ * 7168 * 2 + np_ * 7168 * 2
+    assert ws == expect
+    assert 3.3e9 < ws < 3.6e9
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("hidden", 300, lib.H3_ERR_UNSUPPORTED),
+    ("head_dim", 64, lib.H3_ERR_UNSUPPORTED),
+    ("ffn", 100, lib.H3_ERR_UNSUPPORTED),
+    ("n_tags", 0, lib.H3_ERR_INVALID_ARG),
+    ("n_tags", 9, lib.H3_ERR_UNSUPPORTED),
+    ("wfmt", 7, lib.H3_ERR_INVALID_ARG),
+])
+def test_bad_dims_rejected(L, field, value, code):
+    d = lib.make_dims(synth.H3_DIMS)
+    setattr(d, field, value)
+    assert L.h3_workspace_size(ctypes.byref(d), 100) == 0
+    st = L.h3_attention(ctypes.byref(d), FAKE, FAKE, FAKE, 100, FAKE, None)
+    assert st == code, lib.last_error()
+    assert lib.last_error()
+
+
+def test_bad_rope_split_rejected(L):
+    d = lib.make_dims(synth.H3_DIMS)
+    d.rope_split[:] = [32, 48, 46]
+    st = L.h3_rope_table(ctypes.byref(d), FAKE, 10, FAKE, None)
+    assert st == lib.H3_ERR_INVALID_ARG and "rope_split" in lib.last_error()
+    d.rope_split[:] = [33, 47, 48]
+    assert L.h3_rope_table(ctypes.byref(d), FAKE, 10, FAKE, None) == lib.H3_ERR_INVALID_ARG
+
+
+def _block_call(L, d, w, n=100, ws_bytes=None, x=FAKE, ws=FAKE):
+    ws_bytes = L.h3_workspace_size(ctypes.byref(d), max(n, 1)) if ws_bytes is None else ws_bytes
+    return L.h3_dit_block_forward(ctypes.byref(d), x, FAKE, FAKE, FAKE, ctypes.byref(w), n, ws,
+                                  ws_bytes, None)
+
+
+def _full_weights():
+    w = lib.H3BlockWeights()
+    for f in ("w_qkv", "w_out", "w_fc1", "w_fc2"):
+        setattr(w, f, FAKE)
+    return w
+
+
+def test_argument_errors_before_launch(L):
+    d = lib.make_dims(synth.H3_DIMS)
+    w = _full_weights()
+    assert _block_call(L, d, w, n=0) == lib.H3_ERR_INVALID_ARG
+    assert _block_call(L, d, w, x=None) == lib.H3_ERR_INVALID_ARG
+    assert "x is NULL" in lib.last_error()
+    assert _block_call(L, d, w, x=FAKE + 4) == lib.H3_ERR_INVALID_ARG
+    assert "aligned" in lib.last_error()
+    assert _block_call(L, d, w, ws_bytes=1024) == lib.H3_ERR_WORKSPACE
+    w.w_fc2 = None
+    assert _block_call(L, d, w) == lib.H3_ERR_INVALID_ARG and "w_fc2" in lib.last_error()
+    # INT8 weights need their scales
+    d8 = lib.make_dims(synth.WORKLOADS["h3_1blk_n1192_int8"].dims)
+    assert _block_call(L, d8, _full_weights()) == lib.H3_ERR_INVALID_ARG
+    assert "s_qkv" in lib.last_error()
+    bad_which = L.h3_adaln_modulate(ctypes.byref(d), FAKE, FAKE, FAKE, 2, 10, FAKE, None)
+    assert bad_which == lib.H3_ERR_INVALID_ARG
+    arr = (lib.H3BlockWeights * 2)(_full_weights(), lib.H3BlockWeights())
+    ws = L.h3_workspace_size(ctypes.byref(d), 100)
+    st = L.h3_dit_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, arr, 2, 100, FAKE, ws, None)
+    assert st == lib.H3_ERR_INVALID_ARG and "block 1" in lib.last_error()
+    assert L.h3_dit_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, arr, 0, 100, FAKE, ws, None) \
+        == lib.H3_ERR_INVALID_ARG
+
+
+def test_no_device_reported(L):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; this case is only meaningful without one")
+    d = lib.make_dims(synth.H3_DIMS)
+    st = _block_call(L, d, _full_weights())
+    assert st == lib.H3_ERR_NO_DEVICE, lib.last_error()
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    with pytest.raises(RuntimeError, match="no CPU path"):
+        saved = lib._lib
+        lib._lib = None
+        try:
+            lib.load(str(tmp_path / "nope.so"))
+        finally:
+            lib._lib = saved

@@ -1,0 +1,121 @@
+"""Whole-block and full-depth parity of the HIP path against the oracle (GPU),
+plus properties that hold at any size.
+
+The contract: rel-L2 <= 1e-2 on the block output and <= 3e-2 after the full
+depth (bf16 weights, fp32 accumulation).  The update x_out - x_in is also
+compared, since the residual x_in dominates x_out.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from joint_video_audio_h3_amd import lib, synth
+from tests.gpu_util import TOL_BLOCK, TOL_DEPTH, dev, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    lib.load()
+
+
+def _run_forward(wl, x, tags, pos, table, weights, n_blocks):
+    dims = wl.dims
+    n = x.shape[0]
+    xd = dev(x)
+    blocks = [lib.to_device_block(w) for w in weights[:n_blocks]]
+    ws = lib.alloc_workspace(dims, n)
+    if n_blocks == 1:
+        lib.dit_block_forward(dims, xd, dev(tags), dev(pos), dev(table[0]), blocks[0], ws)
+    else:
+        lib.dit_forward(dims, xd, dev(tags), dev(pos), dev(table[:n_blocks]), blocks, ws)
+    torch.cuda.synchronize()
+    return xd.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("wname", ["tiny_2blk_n164", "h3_1blk_n1192", "h3_1blk_n1192_int8"])
+def test_block_parity(wname):
+    wl = synth.WORKLOADS[wname]
+    say("block parity", wname)
+    x, tags, pos, table, weights = synth.make_inputs(wl, seed=0, n_blocks=1)
+    got = _run_forward(wl, x, tags, pos, table, weights, 1)
+    ref = oracle.block_forward(x, tags, pos, table[0], weights[0], wl.dims)
+    e_out, e_delta = rel_l2(got, ref), rel_l2(got - x, ref - x)
+    say(f"  rel-L2 x_out {e_out:.3e}  update {e_delta:.3e}")
+    assert e_out < TOL_BLOCK
+    assert e_delta < 2 * TOL_BLOCK
+
+
+@pytest.mark.parametrize("n", [1, 77, 300])
+def test_block_parity_ragged_rows(n):
+    """Packed sequences that are not a multiple of any tile (and a single row)."""
+    dims = synth.TINY_DIMS
+    say("block ragged", n)
+    x = synth.make_x(n, dims, seed=9)
+    tags = synth.make_tags(n, dims.n_tags, seed=9)
+    pos = synth.make_positions(n, seed=9)
+    table = synth.make_table(dims, 1, seed=9)
+    w = synth.make_block_weights(dims, 0, seed=9)
+    wl = synth.Workload("ragged", dims, 1, n, 0, 0, (0, 0, 0))
+    got = _run_forward(wl, x, tags, pos, table, [w], 1)
+    ref = oracle.block_forward(x, tags, pos, table[0], w, dims)
+    assert rel_l2(got, ref) < TOL_BLOCK
+    assert rel_l2(got - x, ref - x) < 2 * TOL_BLOCK
+
+
+def test_depth_parity_tiny():
+    wl = synth.WORKLOADS["tiny_2blk_n164"]
+    say("depth parity", wl.name)
+    x, tags, pos, table, weights = synth.make_inputs(wl, seed=0)
+    got = _run_forward(wl, x, tags, pos, table, weights, wl.n_blocks)
+    ref = oracle.dit_forward(x, tags, pos, table, lambda b: weights[b], wl.n_blocks, wl.dims)
+    assert rel_l2(got, ref) < TOL_DEPTH
+    assert rel_l2(got - x, ref - x) < TOL_DEPTH
+
+
+def test_depth_parity_h3_width_three_blocks():
+    """Three full-width blocks (N=1192): error growth along the depth loop."""
+    wl = synth.WORKLOADS["h3_1blk_n1192"]
+    say("depth parity h3 x3")
+    x, tags, pos, table, weights = synth.make_inputs(wl, seed=1, n_blocks=3)
+    got = _run_forward(wl, x, tags, pos, table, weights, 3)
+    ref = oracle.dit_forward(x, tags, pos, table, lambda b: weights[b], 3, wl.dims)
+    e = rel_l2(got, ref)
+    say(f"  rel-L2 after 3 blocks {e:.3e}")
+    assert e < TOL_DEPTH
+
+
+def test_gates_zero_is_bit_exact_identity():
+    wl = synth.WORKLOADS["h3_1blk_n1192"]
+    say("gates zero")
+    x, tags, pos, table, weights = synth.make_inputs(wl, seed=2, n_blocks=1)
+    t = table.copy()
+    t[:, :, 2] = 0
+    t[:, :, 5] = 0
+    got = _run_forward(wl, x, tags, pos, t, weights, 1)
+    np.testing.assert_array_equal(got, x.astype(np.float64))
+
+
+def test_permutation_equivariance_and_determinism():
+    wl = synth.WORKLOADS["h3_1blk_n1192"]
+    say("permutation")
+    x, tags, pos, table, weights = synth.make_inputs(wl, seed=3, n_blocks=1)
+    a = _run_forward(wl, x, tags, pos, table, weights, 1)
+    a2 = _run_forward(wl, x, tags, pos, table, weights, 1)
+    np.testing.assert_array_equal(a, a2)          # same bits run to run
+    perm = np.random.default_rng(0).permutation(len(tags))
+    b = _run_forward(wl, x[perm], tags[perm], pos[perm], table, weights, 1)
+    assert rel_l2(b, a[perm]) < 1e-3
+    assert rel_l2(b - x[perm], a[perm] - x[perm]) < 1e-2
+
+
+def test_global_position_shift_invariance():
+    wl = synth.WORKLOADS["tiny_2blk_n164"]
+    say("position shift")
+    x, tags, pos, table, weights = synth.make_inputs(wl, seed=4, n_blocks=1)
+    a = _run_forward(wl, x, tags, pos, table, weights, 1)
+    b = _run_forward(wl, x, tags, pos + np.float32([16, 8, 4]), table, weights, 1)
+    assert rel_l2(b - x, a - x) < 1e-2
