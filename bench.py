@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the MiniMax-H3 DiT forward on one MI355X.
+
+A step is one denoising forward: the 50-block DiT over one packed sequence,
+inputs and weights resident in HBM, run through the C ABI (h3_dit_forward).
+Primary workload: N = 49,840 packed rows (L 256 | C 1024 | A 200 | V 31x30x52);
+secondary: N = 6,437 (L 256 | A 37 | V 6x32x32).  Both use the same 50 blocks
+of synthetic bf16 weights (random init, H3 shapes).
+
+Printed: one JSON line with packed tokens/s per forward, the per-step kernel
+times (HIP events on the launch stream) with their TFLOP/s and fraction of the
+bf16 MFMA peak, the roofline of the dominant kernel, and the CPU oracle timed
+on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from joint_video_audio_h3_amd import perf_model, synth  # noqa: E402
+
+PEAK = perf_model.PEAK_BF16_TFLOPS
+HBM = perf_model.PEAK_HBM_GBS
+# HBM traffic of the dominant kernels from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE,
+# bytes per launch after the copy-kernel calibration (see profiles/); None when
+# the kernel changed after the counters were taken.
+TRAFFIC_BYTES = {}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def _time_launches(fn, reps, torch):
+    """Average duration (ms) of `fn` over `reps` launches, bracketed by HIP events
+    on the current stream (the stream the C ABI launches on)."""
+    fn()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def step_breakdown(lib, dims, wl_rows, table, block, reps, torch):
+    """Per-kernel times of one block's steps on the block-0 weights."""
+    x, tags, pos = wl_rows
+    n = x.shape[0]
+    D, Di, F, H, d = dims.hidden, dims.inner, dims.ffn, dims.heads, dims.head_dim
+    np_ = lib.padded_rows(n)
+    dev = x.device
+    cs = torch.empty(np_, d // 2, 2, dtype=torch.float32, device=dev)
+    h = torch.empty(n, D, dtype=torch.int16, device=dev)
+    q = torch.empty(H, np_, d, dtype=torch.int16, device=dev)
+    k = torch.empty_like(q)
+    vt = torch.empty(H, d, np_, dtype=torch.int16, device=dev)
+    o = torch.empty(n, Di, dtype=torch.int16, device=dev)
+    a = torch.empty(n, F, dtype=torch.int16, device=dev)
+    xs = x.clone()
+    t0 = table[0]
+    lib.rope_table(dims, pos, n, cs)
+    w = perf_model.block_work(n, D, Di, F)
+    steps = {
+        "adaln": (lambda: lib.adaln_modulate(dims, xs, tags, t0, 0, h), None, w.norm_bytes),
+        "qkv_rope": (lambda: lib.qkv_rope(dims, h, block, cs, n, q, k, vt), w.qkv_flop, None),
+        "attention": (lambda: lib.attention(dims, q, k, vt, n, o), w.attn_flop, None),
+        "out_proj_resid": (lambda: lib.out_proj_residual(dims, o, block, t0, tags, xs), w.out_flop, None),
+        "fc1_swiglu": (lambda: lib.mlp_fc1_swiglu(dims, h, block, a), w.fc1_flop, None),
+        "fc2_resid": (lambda: lib.mlp_fc2_residual(dims, a, block, t0, tags, xs), w.fc2_flop, None),
+    }
+    out = {}
+    for name, (fn, flop, nbytes) in steps.items():
+        ms = _time_launches(fn, reps, torch)
+        r = {"ms": round(ms, 4)}
+        if flop:
+            tf = flop / (ms * 1e-3) / 1e12
+            r.update(tflops=round(tf, 1), mfma_frac=round(tf / PEAK, 4))
+        if nbytes:
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            r.update(gbs=round(gbs, 1), hbm_frac=round(gbs / HBM, 4))
+        out[name] = r
+    gemm_flop = w.linear_flop
+    gemm_ms = sum(out[s]["ms"] for s in ("qkv_rope", "out_proj_resid", "fc1_swiglu", "fc2_resid"))
+    out["gemms_total"] = {"ms": round(gemm_ms, 4), "tflops": round(gemm_flop / gemm_ms / 1e9, 1),
+                          "mfma_frac": round(gemm_flop / gemm_ms / 1e9 / PEAK, 4)}
+    return out, w
+
+
+def run_forward(lib, dims, rows, table, blocks, ws, steps, warmup, torch):
+    x, tags, pos = rows
+    fwd = lambda: lib.dit_forward(dims, x, tags, pos, table, blocks, ws)
+    for i in range(warmup):
+        fwd()
+        torch.cuda.synchronize()
+        log(f"warmup forward {i + 1}/{warmup} done")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fwd()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    assert bool(torch.isfinite(x).all()), "non-finite output"
+    return dt / steps
+
+
+def cpu_baseline(n_target, n_blocks, dims_h3):
+    """The oracle as it stands, on a bounded sample: one full block of the same
+    model width at N=1192 rows, its attention step timed on its own; both parts
+    scaled to the target forward by the work model (linear ~ N, attention ~ N^2)."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    wl = synth.WORKLOADS["h3_1blk_n1192"]
+    x, tags, pos, table, weights = synth.make_inputs(wl, seed=0, n_blocks=1)
+    n = wl.n_rows
+    t0 = time.perf_counter()
+    st = oracle.block_steps(x, tags, pos, table[0], weights[0], wl.dims)
+    t_block = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.attention(st["q"], st["k"], st["v"])
+    t_attn = time.perf_counter() - t0
+    t_rest = max(t_block - t_attn, 1e-9)
+    t_fwd = n_blocks * (t_rest * n_target / n + t_attn * (n_target / n) ** 2)
+    return {"value": round(n_target / t_fwd, 4), "unit": "packed tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": (f"one float64 oracle block at N={n} (H3 width) took {t_block:.1f} s, its "
+                       f"attention {t_attn:.1f} s; scaled to the {n_blocks}-block N={n_target} "
+                       f"forward (linear part x N, attention x N^2)")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="h3_50blk_n49840")
+    ap.add_argument("--secondary", default="h3_50blk_n6437", help="'none' to skip")
+    ap.add_argument("--secondary-steps", type=int, default=5)
+    ap.add_argument("--breakdown-reps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from joint_video_audio_h3_amd import lib
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    lib.load()
+    wl = synth.WORKLOADS[args.workload]
+    dims = wl.dims
+    log(f"generating {wl.n_blocks} blocks of weights on the device")
+    table, blocks = synth.make_device_weights(dims, wl.n_blocks, seed=0)
+    torch.cuda.synchronize()
+
+    def measure(wlx, steps, warmup):
+        rows = synth.make_device_rows(wlx, seed=0)
+        ws = lib.alloc_workspace(dims, wlx.n_rows)
+        sec = run_forward(lib, dims, rows, table[:wlx.n_blocks], blocks[:wlx.n_blocks], ws,
+                          steps, warmup, torch)
+        log(f"{wlx.name}: {sec * 1e3:.1f} ms per forward")
+        bd, w = step_breakdown(lib, dims, synth.make_device_rows(wlx, seed=1), table, blocks[0],
+                               args.breakdown_reps, torch)
+        del ws
+        return sec, bd, w
+
+    sec, bd, w = measure(wl, args.steps, args.warmup)
+    n = wl.n_rows
+    flop_fwd = wl.n_blocks * w.total_flop
+    dom = max(("attention", "fc1_swiglu", "qkv_rope", "fc2_resid", "out_proj_resid"),
+              key=lambda s: bd[s]["ms"])
+    dom_flop = {"attention": w.attn_flop, "fc1_swiglu": w.fc1_flop, "qkv_rope": w.qkv_flop,
+                "fc2_resid": w.fc2_flop, "out_proj_resid": w.out_flop}[dom]
+    ach = dom_flop / (bd[dom]["ms"] * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK, 4),
+                "traffic": TRAFFIC_BYTES.get((wl.name, dom))}
+    result = {
+        "metric": "packed tokens/s per DiT forward (+ MFMA util)",
+        "value": round(n / sec, 2),
+        "unit": "packed tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (random-init weights of the H3 shapes, N(0,1) latents)",
+        "config": {"workload": wl.name, "n_rows": n, "blocks": wl.n_blocks, "hidden": dims.hidden,
+                   "heads": dims.heads, "head_dim": dims.head_dim, "ffn": dims.ffn,
+                   "packed": {"L": wl.L, "C": wl.C, "A": wl.A, "V": list(wl.V)}},
+        "forward_tflops": round(flop_fwd / sec / 1e12, 1),
+        "forward_mfma_frac": round(flop_fwd / sec / 1e12 / PEAK, 4),
+        "per_step_kernels": bd,
+        "roofline": roofline,
+    }
+    if args.secondary != "none":
+        wl2 = synth.WORKLOADS[args.secondary]
+        sec2, bd2, w2 = measure(wl2, args.secondary_steps, 1)
+        result["secondary"] = {
+            "workload": wl2.name, "n_rows": wl2.n_rows, "value": round(wl2.n_rows / sec2, 2),
+            "unit": "packed tokens/s", "ms_per_step": round(sec2 * 1e3, 2),
+            "steps": args.secondary_steps,
+            "forward_tflops": round(wl2.n_blocks * w2.total_flop / sec2 / 1e12, 1),
+            "forward_mfma_frac": round(wl2.n_blocks * w2.total_flop / sec2 / 1e12 / PEAK, 4),
+            "per_step_kernels": bd2,
+        }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(n, wl.n_blocks, dims)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

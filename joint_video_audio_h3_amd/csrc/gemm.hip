@@ -4,14 +4,25 @@
 //   C[M][n_out] = A[M][K] . B[n_out][K]^T       (A = activations, B = weights,
 //                                                 both K-contiguous)
 //
-// Tiling: BM x BN block tile, BK = 64, WM x WN wavefronts, each owning a
-// (BM/WM) x (BN/WN) sub-tile computed with v_mfma_f32_32x32x16_bf16 (fp32
-// accumulators).  A and B tiles are staged through registers into a
-// double-buffered LDS ring (row stride 72 bf16 = 144 B, which keeps the
-// 16-byte fragment reads of a 16-lane group on distinct banks).  One barrier
-// per K step.  Block ids are remapped so that each XCD (blocks are dealt
-// round-robin to the 8 XCDs) walks a contiguous run of the grouped tile order,
-// and consecutive tiles on an XCD share the same weight tile in its L2.
+// bf16 weights (gemm_direct_kernel): 256 x 256 block tile (256 x 192 for the
+// 96-wide heads of the small model), four wavefronts in 2 x 2, each owning a
+// 128 x 128 (x 96) sub-tile of v_mfma_f32_32x32x16_bf16 accumulators.  Tiles
+// move HBM/L2 -> LDS with global_load_lds_dwordx4 (no staging registers), in
+// a 4-deep ring of BK = 32 stages: three stages are in flight while one is
+// consumed, with one barrier per stage.  LDS rows are 64 B (4 chunks of 16 B)
+// and chunk c of row r is stored at position c ^ f(r), f(r) = ((r>>1)^(r>>3))&3,
+// which keeps each 16-byte fragment read conflict-free whether the LDS serves
+// 8 or 16 lanes per cycle; the permutation is applied by choosing which
+// global chunk each lane of a load fetches.
+//
+// INT8 weights (gemm_staged_kernel): same MFMA tiling with eight wavefronts;
+// 16-byte chunks of int8 codes go through registers, where they are
+// dequantised to bf16(q * s) (one bf16 scale per 32 K elements) on their way
+// into a double-buffered LDS ring, so the MFMA loop is unchanged.
+//
+// Block ids are remapped so that each XCD (blocks are dealt round-robin to the
+// 8 XCDs) walks a contiguous run of a grouped tile order in which consecutive
+// tiles share the same weight tile in that XCD's L2.
 //
 // MFMA 32x32 accumulator layout: lane l, register v holds
 //   row = 8*(v/4) + 4*(l/32) + (v%4),   col = l%32.
@@ -36,175 +47,66 @@
 //             pipeline" and "Metal 4 and TensorOps paths": fused
 //             QK-normalisation/RoPE, Q/K/V routed straight to head-major
 //             attention inputs).
-//  INT8 (wfmt 1): B is int8 with one bf16 scale per 32 K elements; each
-//             16-byte chunk of codes is dequantised to bf16(q*s) on its way
-//             into LDS, so the MFMA loop is the same as the bf16 path's.
 #include "h3_device.h"
 #include "launch.h"
 
 namespace h3 {
 
-constexpr int BK = 64;
-constexpr int LDK = BK + 8;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
-template <int BM, int BN, int WM, int WN, int EPI, int WF, int SEC>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int A_CH = BM * 8 / NT;
-  constexpr int B_CH = WF == 0 ? BN * 8 / NT : BN * 4 / NT;
-  static_assert(A_CH * NT == BM * 8 && B_CH > 0, "tile/thread mismatch");
-  static_assert(EPI != EPI_QKV || TN == SEC, "QKV wave tile must be one head section");
-  static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU needs paired gate/value tiles");
+// Wait until at most N vector-memory operations of this wave are outstanding.
+// Written as asm with a memory clobber so no LDS access moves across it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDK];
-  __shared__ int s_tag[EPI == EPI_RESID ? BM : 1];
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds + 16*l (M0 holds the wave-uniform LDS address).  Issued as asm so the
+// compiler's wait insertion does not drain every in-flight stage before each
+// LDS read; completion is tracked explicitly with wait_vmcnt.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(la) : "memory");
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+struct TileCoord {
+  int tm, tn;
+};
 
-  // ---- tile coordinates: XCD-aware remap, then grouped order along M
+template <int EPI, int BM, int BN>
+__device__ __forceinline__ TileCoord tile_coord(const GemmArgs& p) {
   const int tiles_m = (EPI == EPI_QKV) ? p.n_pad / BM : (p.M + BM - 1) / BM;
   const int tiles_n = (p.n_out + BN - 1) / BN;
   const int total = tiles_m * tiles_n;
-  int pid;
-  {
-    const int raw = blockIdx.x;
-    const int per = total / 8, rem = total % 8;
-    const int xcd = raw % 8, local = raw / 8;
-    pid = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-  }
+  const int raw = blockIdx.x;
+  const int per = total / 8, rem = total % 8;
+  const int xcd = raw % 8, local = raw / 8;
+  const int pid = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
   constexpr int GROUP_M = 8;
   const int in_group = GROUP_M * tiles_n;
   const int first_m = (pid / in_group) * GROUP_M;
   const int gsz = min(tiles_m - first_m, GROUP_M);
-  const int tm = first_m + (pid % in_group) % gsz;
-  const int tn = (pid % in_group) / gsz;
-  const int m0 = tm * BM;
-  const int n0 = tn * BN;
+  return {first_m + (pid % in_group) % gsz, (pid % in_group) / gsz};
+}
 
-  if (EPI == EPI_RESID) {
-    for (int i = tid; i < BM; i += NT) s_tag[i] = p.tag[min(m0 + i, p.M - 1)];
+// Weight row feeding tile column r of tile tn (SwiGLU pairs gate and value rows per wave).
+template <int EPI, int BN, int TN>
+__device__ __forceinline__ int weight_row(const GemmArgs& p, int tn, int r) {
+  if (EPI == EPI_SWIGLU) {
+    const int w = r / TN, cc = r % TN, half = TN / 2;
+    const int base = tn * (BN / 2) + w * half;
+    return cc < half ? base + cc : p.ffn + base + cc - half;
   }
+  return min(tn * BN + r, p.n_out - 1);
+}
 
-  // ---- per-thread global source rows
-  const int K = p.K;
-  const uint16_t* a_src[A_CH];
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + i * NT;
-    const int r = min(m0 + c / 8, p.M - 1);
-    a_src[i] = p.A + (size_t)r * K + (c % 8) * 8;
-  }
-  constexpr int B_PER_ROW = WF == 0 ? 8 : 4;
-  const uint8_t* b_src[B_CH];
-  const uint16_t* s_src[B_CH];
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + i * NT;
-    const int r = c / B_PER_ROW;
-    int brow;
-    if (EPI == EPI_SWIGLU) {
-      const int w = r / TN, cc = r % TN, half = TN / 2;
-      const int base = tn * (BN / 2) + w * half;
-      brow = cc < half ? base + cc : p.ffn + base + cc - half;
-    } else {
-      brow = min(n0 + r, p.n_out - 1);
-    }
-    if (WF == 0) {
-      b_src[i] = reinterpret_cast<const uint8_t*>(p.B) + ((size_t)brow * K + (c % 8) * 8) * 2;
-    } else {
-      b_src[i] = reinterpret_cast<const uint8_t*>(p.B) + (size_t)brow * K + (c % 4) * 16;
-      s_src[i] = p.Bs + (size_t)brow * (K / 32) + (c % 4) / 2;
-    }
-  }
-
-  uint4 ra[A_CH];
-  uint4 rb[B_CH];
-  uint16_t rs[WF == 1 ? B_CH : 1];
-
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      if (WF == 0) {
-        rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + (size_t)k0 * 2);
-      } else {
-        rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + k0);
-        rs[i] = s_src[i][k0 / 32];
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-    uint16_t* As = smem + buf * (BM + BN) * LDK;
-    uint16_t* Bsm = As + BM * LDK;
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int c = tid + i * NT;
-      *reinterpret_cast<uint4*>(As + (c / 8) * LDK + (c % 8) * 8) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int c = tid + i * NT;
-      if (WF == 0) {
-        *reinterpret_cast<uint4*>(Bsm + (c / 8) * LDK + (c % 8) * 8) = rb[i];
-      } else {
-        const float s = bf2f(rs[i]);
-        const uint32_t w[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
-        uint32_t o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t word = w[e / 2];
-          const int sh = (e % 2) * 16;
-          const float lo = (float)(int8_t)((word >> sh) & 0xff) * s;
-          const float hi = (float)(int8_t)((word >> (sh + 8)) & 0xff) * s;
-          o[e] = pack2bf(lo, hi);
-        }
-        uint16_t* dst = Bsm + (c / 4) * LDK + (c % 4) * 16;
-        *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-        *reinterpret_cast<uint4*>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
-      }
-    }
-  };
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
-
-  const int KT = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  const int lrow = lane & 31, lk = (lane >> 5) * 8;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const uint16_t* As = smem + cur * (BM + BN) * LDK + (wm * TM + lrow) * LDK + lk;
-    const uint16_t* Bsm = smem + cur * (BM + BN) * LDK + BM * LDK + (wn * TN + lrow) * LDK + lk;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * LDK + kk * 16);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(Bsm + j * 32 * LDK + kk * 16);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
-    }
-    if (kt + 1 < KT) sstore(cur ^ 1);
-    __syncthreads();
-  }
-
-  // ---------------------------------------------------------------- epilogues
+template <int BM, int BN, int WM, int WN, int EPI, int SEC, int FM, int FN>
+__device__ __forceinline__ void epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], int m0, int n0,
+                                         int tn, int wm, int wn, int lane, const int* s_tag) {
+  constexpr int TM = BM / WM, TN = BN / WN;
   const int hl = lane >> 5;     // half-wave: rows 4..7 of each group of 8
   const int lc = lane & 31;     // column within a 32-wide MFMA tile
   const int row_base = m0 + wm * TM;
@@ -310,31 +212,282 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int WF, int SEC>
-static hipError_t run(const GemmArgs& a, hipStream_t s) {
-  const int tiles_m = (EPI == EPI_QKV) ? a.n_pad / BM : (a.M + BM - 1) / BM;
+// ============================================================ bf16: direct-to-LDS
+constexpr int DBK = 32;          // K elements per stage
+constexpr int DSTAGES = 4;       // LDS ring depth
+constexpr int DROW = DBK * 2;    // bytes per LDS row (64)
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+template <int EPI, int SEC, int BN>
+__global__ __launch_bounds__(256) void gemm_direct_kernel(GemmArgs p) {
+  constexpr int BM = 256, WM = 2, WN = 2;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int NA = BM / 16, NB = BN / 16;   // 1 KB (16-row) loads per stage
+  constexpr int NI = (NA + NB) / 4;           // per wavefront
+  constexpr int STAGE = (BM + BN) * DROW;
+  static_assert((NA + NB) % 4 == 0, "loads must split evenly over the waves");
+  static_assert(EPI != EPI_QKV || TN == SEC, "QKV wave tile must be one head section");
+  static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU needs paired gate/value tiles");
+
+  // one LDS array per ring slot, so every load and fragment read below names its
+  // buffer statically (the K loop is unrolled by the ring depth)
+  __shared__ __attribute__((aligned(1024))) char ring0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char ring1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char ring2[STAGE];
+  __shared__ __attribute__((aligned(1024))) char ring3[STAGE];
+  __shared__ int s_tag[EPI == EPI_RESID ? BM : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const TileCoord tc = tile_coord<EPI, BM, BN>(p);
+  const int m0 = tc.tm * BM, n0 = tc.tn * BN;
+  if (EPI == EPI_RESID) {
+    for (int i = tid; i < BM; i += 256) s_tag[i] = p.tag[min(m0 + i, p.M - 1)];
+  }
+
+  // per-lane source of each of this wave's NI loads; lane l fills row 16*j + l/4,
+  // LDS position l%4, which holds global chunk (l%4) ^ f(row)
+  const int K = p.K;
+  const uint16_t* src[NI];
+  int ldso[NI];
+#pragma unroll
+  for (int s = 0; s < NI; ++s) {
+    const int j = wave + 4 * s;
+    const int r = 16 * (j < NA ? j : j - NA) + lane / 4;
+    const int chunk = (lane & 3) ^ swz(r);
+    if (j < NA) {
+      src[s] = p.A + (size_t)min(m0 + r, p.M - 1) * K + chunk * 8;
+      ldso[s] = j * 1024;
+    } else {
+      const int brow = weight_row<EPI, BN, TN>(p, tc.tn, r);
+      src[s] = reinterpret_cast<const uint16_t*>(p.B) + (size_t)brow * K + chunk * 8;
+      ldso[s] = BM * DROW + (j - NA) * 1024;
+    }
+  }
+  auto issue = [&](int kt, char* buf) {
+#pragma unroll
+    for (int s = 0; s < NI; ++s)
+      dma16(src[s] + kt * DBK, buf + ldso[s]);
+  };
+
+  // fragment offsets inside a stage: row (lane%32) of each 32-row tile, chunk
+  // 2*kk + lane/32 at its swizzled position
+  const int fr = lane & 31, h = lane >> 5;
+  int foff[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) foff[kk] = fr * DROW + (((2 * kk + h) ^ swz(fr)) * 16);
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+  auto compute = [&](const char* buf) {
+    const char* As = buf + (wm * TM) * DROW;
+    const char* Bs = buf + (BM + wn * TN) * DROW;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * DROW + foff[kk]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + j * 32 * DROW + foff[kk]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+    }
+  };
+  // one ring step: wait for this wave's loads of stage kt (the `ahead` later
+  // stages may stay in flight), barrier so every wave's loads have landed and
+  // every wave is done with the slot about to be refilled, refill it with stage
+  // kt + 3, then consume stage kt.
+  auto step = [&](int kt, const char* cur, char* refill, int KT) {
+    const int ahead = KT - 1 - kt;
+    if (ahead >= 2) {
+      wait_vmcnt<2 * NI>();
+    } else if (ahead == 1) {
+      wait_vmcnt<NI>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (kt + 3 < KT) issue(kt + 3, refill);
+    compute(cur);
+  };
+
+  const int KT = K / DBK;   // a multiple of 4 (K % 128 == 0)
+  issue(0, ring0);
+  issue(1, ring1);
+  issue(2, ring2);
+  for (int kt = 0; kt < KT; kt += 4) {
+    step(kt + 0, ring0, ring3, KT);
+    step(kt + 1, ring1, ring0, KT);
+    step(kt + 2, ring2, ring1, KT);
+    step(kt + 3, ring3, ring2, KT);
+  }
+  __syncthreads();
+  epilogue<BM, BN, WM, WN, EPI, SEC>(p, acc, m0, n0, tc.tn, wm, wn, lane, s_tag);
+}
+
+// ============================================================ INT8: staged dequant
+constexpr int SBK = 64;
+constexpr int SLDK = SBK + 8;   // padded LDS row (bf16): 144 B
+
+template <int EPI, int SEC, int BN>
+__global__ __launch_bounds__(512) void gemm_staged_kernel(GemmArgs p) {
+  constexpr int BM = 256, WM = 4, WN = 2, NT = 512;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int A_CH = BM * 8 / NT;           // 16-byte bf16 chunks per thread
+  constexpr int B_CH = (BN * 4 + NT - 1) / NT; // 16-byte int8 chunks per thread (last round partial)
+  static_assert(A_CH * NT == BM * 8, "tile/thread mismatch");
+  static_assert(EPI != EPI_QKV || TN == SEC, "QKV wave tile must be one head section");
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * SLDK];
+  __shared__ int s_tag[EPI == EPI_RESID ? BM : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const TileCoord tc = tile_coord<EPI, BM, BN>(p);
+  const int m0 = tc.tm * BM, n0 = tc.tn * BN;
+  if (EPI == EPI_RESID) {
+    for (int i = tid; i < BM; i += NT) s_tag[i] = p.tag[min(m0 + i, p.M - 1)];
+  }
+  const int K = p.K;
+  const uint16_t* a_src[A_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int c = tid + i * NT;
+    a_src[i] = p.A + (size_t)min(m0 + c / 8, p.M - 1) * K + (c % 8) * 8;
+  }
+  const int8_t* b_src[B_CH];
+  const uint16_t* s_src[B_CH];
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int c = min(tid + i * NT, BN * 4 - 1);
+    const int brow = weight_row<EPI, BN, TN>(p, tc.tn, c / 4);
+    b_src[i] = reinterpret_cast<const int8_t*>(p.B) + (size_t)brow * K + (c % 4) * 16;
+    s_src[i] = p.Bs + (size_t)brow * (K / 32) + (c % 4) / 2;
+  }
+  uint4 ra[A_CH], rb[B_CH];
+  uint16_t rs[B_CH];
+  auto gload = [&](int kt) {
+    const int k0 = kt * SBK;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + k0);
+      rs[i] = s_src[i][k0 / 32];
+    }
+  };
+  auto sstore = [&](int buf) {
+    uint16_t* As = smem + buf * (BM + BN) * SLDK;
+    uint16_t* Bsm = As + BM * SLDK;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = tid + i * NT;
+      *reinterpret_cast<uint4*>(As + (c / 8) * SLDK + (c % 8) * 8) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = tid + i * NT;
+      if (c >= BN * 4) break;
+      const float sc = bf2f(rs[i]);
+      const uint32_t w4[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
+      uint32_t o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t word = w4[e / 2];
+        const int sh = (e % 2) * 16;
+        const float lo = (float)(int8_t)((word >> sh) & 0xff) * sc;
+        const float hi = (float)(int8_t)((word >> (sh + 8)) & 0xff) * sc;
+        o[e] = pack2bf(lo, hi);
+      }
+      uint16_t* dst = Bsm + (c / 4) * SLDK + (c % 4) * 16;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+  const int KT = K / SBK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int lrow = lane & 31, lk = (lane >> 5) * 8;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+    const uint16_t* As = smem + cur * (BM + BN) * SLDK + (wm * TM + lrow) * SLDK + lk;
+    const uint16_t* Bsm = smem + cur * (BM + BN) * SLDK + BM * SLDK + (wn * TN + lrow) * SLDK + lk;
+#pragma unroll
+    for (int kk = 0; kk < SBK / 16; ++kk) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * SLDK + kk * 16);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(Bsm + j * 32 * SLDK + kk * 16);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+    }
+    if (kt + 1 < KT) sstore(cur ^ 1);
+    __syncthreads();
+  }
+  epilogue<BM, BN, WM, WN, EPI, SEC>(p, acc, m0, n0, tc.tn, wm, wn, lane, s_tag);
+}
+
+// ============================================================ dispatch
+template <int BM, int BN>
+static dim3 grid_for(int epi, const GemmArgs& a) {
+  const int tiles_m = epi == EPI_QKV ? a.n_pad / BM : (a.M + BM - 1) / BM;
   const int tiles_n = (a.n_out + BN - 1) / BN;
-  gemm_kernel<BM, BN, WM, WN, EPI, WF, SEC><<<dim3(tiles_m * tiles_n), WM * WN * 64, 0, s>>>(a);
+  return dim3(tiles_m * tiles_n);
+}
+
+template <int EPI, int SEC, int BN>
+static hipError_t run_direct(const GemmArgs& a, hipStream_t s) {
+  gemm_direct_kernel<EPI, SEC, BN><<<grid_for<256, BN>(EPI, a), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <int WF>
-static hipError_t dispatch(int epi, const GemmArgs& a, hipStream_t s) {
-  switch (epi) {
-    case EPI_RESID:
-      return run<256, 256, 2, 2, EPI_RESID, WF, 0>(a, s);
-    case EPI_SWIGLU:
-      return run<256, 256, 2, 2, EPI_SWIGLU, WF, 0>(a, s);
-    case EPI_QKV:
-      if (a.head_dim == 128) return run<256, 256, 2, 2, EPI_QKV, WF, 128>(a, s);
-      if (a.head_dim == 96) return run<256, 192, 2, 2, EPI_QKV, WF, 96>(a, s);
-      return hipErrorInvalidValue;
-  }
-  return hipErrorInvalidValue;
+template <int EPI, int SEC, int BN>
+static hipError_t run_staged(const GemmArgs& a, hipStream_t s) {
+  gemm_staged_kernel<EPI, SEC, BN><<<grid_for<256, BN>(EPI, a), 512, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
-  return wfmt == 0 ? dispatch<0>(epi, a, s) : dispatch<1>(epi, a, s);
+  if (a.K % 128 != 0) return hipErrorInvalidValue;
+  if (wfmt == 0) {
+    switch (epi) {
+      case EPI_RESID: return run_direct<EPI_RESID, 0, 256>(a, s);
+      case EPI_SWIGLU: return run_direct<EPI_SWIGLU, 0, 256>(a, s);
+      case EPI_QKV:
+        if (a.head_dim == 128) return run_direct<EPI_QKV, 128, 256>(a, s);
+        if (a.head_dim == 96) return run_direct<EPI_QKV, 96, 192>(a, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  switch (epi) {
+    case EPI_RESID: return run_staged<EPI_RESID, 0, 256>(a, s);
+    case EPI_SWIGLU: return run_staged<EPI_SWIGLU, 0, 256>(a, s);
+    case EPI_QKV:
+      if (a.head_dim == 128) return run_staged<EPI_QKV, 128, 256>(a, s);
+      if (a.head_dim == 96) return run_staged<EPI_QKV, 96, 192>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace h3

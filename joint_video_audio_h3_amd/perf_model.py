@@ -55,5 +55,5 @@ def forward_flop(n: int, n_blocks: int, hidden: int, inner: int, ffn: int) -> fl
 
 
 # MI355X published peaks (dense; AMD product specification)
-PEAK_BF16_TFLOPS = 2516.6
+PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0

@@ -38,6 +38,7 @@ Readings (stated once, used everywhere):
 from __future__ import annotations
 
 import dataclasses
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, Optional, Tuple
 
 import numpy as np
@@ -110,9 +111,12 @@ def _rng(seed: int, block: int, name: str) -> np.random.Generator:
 # ---------------------------------------------------------------- bf16 packing
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16 (nearest, ties to even) and return the bit patterns."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = u + 0x7FFF + ((u >> 16) & 1)
-    return (u >> 16).astype(np.uint16)
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u >> 16) & 1          # finite inputs only: u + 0x8000 stays below 2^32
+    r += 0x7FFF
+    r += u
+    r >>= 16
+    return r.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -213,12 +217,17 @@ def make_block_weights(dims: Dims, block: int, seed: int = 0,
     D, Di, F, d = dims.hidden, dims.inner, dims.ffn, dims.head_dim
     shapes = {"qkv": (3 * Di, D), "out": (D, Di), "fc1": (2 * F, D), "fc2": (D, F)}
     w: Dict[str, Optional[np.ndarray]] = {}
-    for k, (o, i) in shapes.items():
+
+    def one(k):
+        o, i = shapes[k]
         bits = _normal_bf16(seed, block, "w_" + k, (o, i), 1.0 / i)
-        if dims.wfmt == WFMT_INT8_G32:
-            w["w_" + k], w["s_" + k] = quantize_int8_g32(bits)
-        else:
-            w["w_" + k], w["s_" + k] = bits, None
+        return quantize_int8_g32(bits) if dims.wfmt == WFMT_INT8_G32 else (bits, None)
+
+    # independent streams per tensor: drawing them concurrently changes no value
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        drawn = dict(zip(shapes, ex.map(one, shapes)))
+    for k, (o, i) in shapes.items():
+        w["w_" + k], w["s_" + k] = drawn[k]
         w["b_" + k] = _normal_bf16(seed, block, "b_" + k, (o,), 1.0 / i) if biases else None
     if norms:
         for k in ("q_norm", "k_norm"):
@@ -240,31 +249,36 @@ def make_inputs(wl: Workload, seed: int = 0, n_blocks: Optional[int] = None,
     return x, tags, pos, table, weights
 
 
-def make_device_inputs(wl: Workload, seed: int = 0, device: str = "cuda",
-                       n_blocks: Optional[int] = None):
-    """Same distributions as :func:`make_inputs`, drawn on the device by torch.
+def make_device_rows(wl: Workload, seed: int = 0, device: str = "cuda"):
+    """x fp32 [N, D] ~ N(0, 1) drawn on the device, plus the packed tags and positions."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 1000003 + 1)
+    tags, pos = packed_layout(wl)
+    x = torch.randn(wl.n_rows, wl.dims.hidden, generator=g, device=device, dtype=torch.float32)
+    return x, torch.from_numpy(tags).to(device), torch.from_numpy(pos).to(device)
+
+
+def make_device_weights(dims: Dims, n_blocks: int, seed: int = 0, device: str = "cuda"):
+    """Modulation table and per-block weights with the host generator's
+    distributions, drawn on the device by torch.
 
     Used where the host generator would take minutes (50 blocks of 5376-wide
     weights = 19.3e9 draws).  The streams differ from the host generator's, so
-    inputs made here are only for timing and for properties that hold for any
-    input; parity against the oracle always uses :func:`make_inputs`.
+    inputs made here serve timing and properties that hold for any input;
+    parity against the oracle always uses :func:`make_inputs`.
     """
     import torch
 
-    nb = wl.n_blocks if n_blocks is None else n_blocks
-    dims = wl.dims
     D, Di, F, d = dims.hidden, dims.inner, dims.ffn, dims.head_dim
     g = torch.Generator(device=device)
-    tags, pos = packed_layout(wl)
-    g.manual_seed(seed * 1000003 + 1)
-    x = torch.randn(wl.n_rows, D, generator=g, device=device, dtype=torch.float32)
-    t_tags = torch.from_numpy(tags).to(device)
-    t_pos = torch.from_numpy(pos).to(device)
-    table = (torch.randn(nb, dims.n_tags, 6, D, generator=g, device=device)
+    g.manual_seed(seed * 1000003 + 2)
+    table = (torch.randn(n_blocks, dims.n_tags, 6, D, generator=g, device=device)
              * float(np.sqrt(0.1))).to(torch.bfloat16)
     shapes = {"qkv": (3 * Di, D), "out": (D, Di), "fc1": (2 * F, D), "fc2": (D, F)}
     blocks = []
-    for b in range(nb):
+    for b in range(n_blocks):
         g.manual_seed(seed * 1000003 + 7919 * (b + 1))
         wb = {}
         for k, (o, i) in shapes.items():
@@ -279,7 +293,7 @@ def make_device_inputs(wl: Workload, seed: int = 0, device: str = "cuda",
         for k in ("q_norm", "k_norm"):
             wb[k] = (1.0 + 0.1 * torch.randn(d, generator=g, device=device)).to(torch.bfloat16)
         blocks.append(wb)
-    return x, t_tags, t_pos, table, blocks
+    return table, blocks
 
 
 def _quantize_int8_g32_torch(w_bf16):
