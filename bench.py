@@ -51,7 +51,7 @@ def _time_launches(fn, reps, torch):
     return s.elapsed_time(e) / reps
 
 
-def step_breakdown(lib, dims, wl_rows, table, block, reps, torch):
+def step_breakdown(lib, dims, wl_rows, table, block, reps, torch, only=None):
     """Per-kernel times of one block's steps on the block-0 weights."""
     x, tags, pos = wl_rows
     n = x.shape[0]
@@ -78,6 +78,13 @@ def step_breakdown(lib, dims, wl_rows, table, block, reps, torch):
         "fc2_resid": (lambda: lib.mlp_fc2_residual(dims, a, block, t0, tags, xs), w.fc2_flop, None),
     }
     out = {}
+    if only:
+        # inputs of the later steps come from running the earlier ones once
+        for name, (fn, _, _) in steps.items():
+            if name == only:
+                break
+            fn()
+        steps = {only: steps[only]}
     for name, (fn, flop, nbytes) in steps.items():
         ms = _time_launches(fn, reps, torch)
         r = {"ms": round(ms, 4)}
@@ -88,6 +95,8 @@ def step_breakdown(lib, dims, wl_rows, table, block, reps, torch):
             gbs = nbytes / (ms * 1e-3) / 1e9
             r.update(gbs=round(gbs, 1), hbm_frac=round(gbs / HBM, 4))
         out[name] = r
+    if only:
+        return out, w
     gemm_flop = w.linear_flop
     gemm_ms = sum(out[s]["ms"] for s in ("qkv_rope", "out_proj_resid", "fc1_swiglu", "fc2_resid"))
     out["gemms_total"] = {"ms": round(gemm_ms, 4), "tflops": round(gemm_flop / gemm_ms / 1e9, 1),
@@ -153,6 +162,9 @@ def main():
     ap.add_argument("--secondary-steps", type=int, default=5)
     ap.add_argument("--breakdown-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-step", default=None,
+                    help="time just one step kernel (adaln, qkv_rope, attention, out_proj_resid, "
+                         "fc1_swiglu, fc2_resid) on one block's weights, e.g. under a counter run")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -167,6 +179,12 @@ def main():
     lib.load()
     wl = synth.WORKLOADS[args.workload]
     dims = wl.dims
+    if args.only_step:
+        table, blocks = synth.make_device_weights(dims, 1, seed=0)
+        bd, _ = step_breakdown(lib, dims, synth.make_device_rows(wl, seed=1), table, blocks[0],
+                               args.breakdown_reps, torch, only=args.only_step)
+        print(json.dumps({"workload": wl.name, "step": args.only_step, **bd[args.only_step]}))
+        return
     log(f"generating {wl.n_blocks} blocks of weights on the device")
     table, blocks = synth.make_device_weights(dims, wl.n_blocks, seed=0)
     torch.cuda.synchronize()

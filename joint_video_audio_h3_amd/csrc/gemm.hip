@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(GemmArgs p) {
       ldso[s] = BM * DROW + (j - NA) * 1024;
     }
   }
-  auto issue = [&](int kt, char* buf) {
+  auto issue = [&](int kt, char* buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < NI; ++s)
       dma16(src[s] + kt * DBK, buf + ldso[s]);
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-  auto compute = [&](const char* buf) {
+  auto compute = [&](const char* buf) __attribute__((always_inline)) {
     const char* As = buf + (wm * TM) * DROW;
     const char* Bs = buf + (BM + wn * TN) * DROW;
 #pragma unroll
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(GemmArgs p) {
   // stages may stay in flight), barrier so every wave's loads have landed and
   // every wave is done with the slot about to be refilled, refill it with stage
   // kt + 3, then consume stage kt.
-  auto step = [&](int kt, const char* cur, char* refill, int KT) {
+  auto step = [&](int kt, const char* cur, char* refill, int KT) __attribute__((always_inline)) {
     const int ahead = KT - 1 - kt;
     if (ahead >= 2) {
       wait_vmcnt<2 * NI>();
