@@ -30,7 +30,7 @@ HBM = perf_model.PEAK_HBM_GBS
 # HBM traffic of the dominant kernels from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE,
 # bytes per launch after the copy-kernel calibration (see profiles/); None when
 # the kernel changed after the counters were taken.
-TRAFFIC_BYTES = {}
+TRAFFIC_BYTES = {("h3_50blk_n49840", "attention"): 73.68e9}
 
 
 def log(*a):
@@ -162,6 +162,9 @@ def main():
     ap.add_argument("--secondary-steps", type=int, default=5)
     ap.add_argument("--breakdown-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="with --only-step: first run a 1 GiB device-to-device copy three times, "
+                         "the known-size reference for HBM byte counters")
     ap.add_argument("--only-step", default=None,
                     help="time just one step kernel (adaln, qkv_rope, attention, out_proj_resid, "
                          "fc1_swiglu, fc2_resid) on one block's weights, e.g. under a counter run")
@@ -180,6 +183,13 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     dims = wl.dims
     if args.only_step:
+        if args.copy_calibration:
+            src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
         table, blocks = synth.make_device_weights(dims, 1, seed=0)
         bd, _ = step_breakdown(lib, dims, synth.make_device_rows(wl, seed=1), table, blocks[0],
                                args.breakdown_reps, torch, only=args.only_step)
