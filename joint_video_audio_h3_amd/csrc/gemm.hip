@@ -9,11 +9,10 @@
 // 128 x 128 (x 96) sub-tile of v_mfma_f32_32x32x16_bf16 accumulators.  Tiles
 // move HBM/L2 -> LDS with global_load_lds_dwordx4 (no staging registers), in
 // a 4-deep ring of BK = 32 stages: three stages are in flight while one is
-// consumed, with one barrier per stage.  LDS rows are 64 B (4 chunks of 16 B)
-// and chunk c of row r is stored at position c ^ f(r), f(r) = ((r>>1)^(r>>3))&3,
-// which keeps each 16-byte fragment read conflict-free whether the LDS serves
-// 8 or 16 lanes per cycle; the permutation is applied by choosing which
-// global chunk each lane of a load fetches.
+// consumed.  LDS rows are 64 B (4 chunks of 16 B) and chunk c of row r is
+// stored at position c ^ f(r), f(r) = (r ^ (r>>2)) & 3, which measures free of
+// LDS bank conflicts for the 16-byte fragment reads; the permutation is applied
+// by choosing which global chunk each lane of a load fetches.
 //
 // INT8 weights (gemm_staged_kernel): same MFMA tiling with eight wavefronts;
 // 16-byte chunks of int8 codes go through registers, where they are
@@ -212,15 +211,63 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN
   }
 }
 
+// Gated residual through LDS: each wavefront stages one 32-row slab of its
+// accumulator tile at a time (fp32, padded rows), then reads it back as
+// float4 along rows, so x is read and written in 16-byte coalesced pieces,
+// the gate in 8-byte pieces, and the bias is loaded once per lane.
+constexpr int RSTRIDE = 136;   // floats per staged row (128 + 8 of padding)
+
+template <int TM, int TN, int FM, int FN>
+__device__ __forceinline__ void resid_epilogue_lds(const GemmArgs& p, f32x16 (&acc)[FM][FN],
+                                                   int row0, int col0, int tag_row0, int lane,
+                                                   float* stage, const int* s_tag) {
+  static_assert(TN == 128, "one float4 per lane covers a 128-wide row");
+  const int hl = lane >> 5, lc = lane & 31;
+  const int gcol = col0 + 4 * lc;
+  const bool col_ok = gcol < p.n_out;   // n_out % 4 == 0, so a float4 is all in or all out
+  float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (p.bias && col_ok) {
+    const u16x4 bb = *reinterpret_cast<const u16x4*>(p.bias + gcol);
+    b4 = make_float4(bf2f(bb[0]), bf2f(bb[1]), bf2f(bb[2]), bf2f(bb[3]));
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        stage[(8 * (v / 4) + 4 * hl + (v % 4)) * RSTRIDE + j * 32 + lc] = acc[i][j][v];
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int r = 2 * it + hl;
+      const int row = row0 + i * 32 + r;
+      const float4 a = *reinterpret_cast<const float4*>(stage + r * RSTRIDE + 4 * lc);
+      if (row < p.M && col_ok) {
+        const int t = s_tag[tag_row0 + i * 32 + r];
+        const u16x4 g = *reinterpret_cast<const u16x4*>(p.gate_tab + (size_t)t * p.tag_stride + gcol);
+        float4* xp = reinterpret_cast<float4*>(p.x + (size_t)row * p.ldx + gcol);
+        float4 x = *xp;
+        x.x += bf2f(g[0]) * (a.x + b4.x);
+        x.y += bf2f(g[1]) * (a.y + b4.y);
+        x.z += bf2f(g[2]) * (a.z + b4.z);
+        x.w += bf2f(g[3]) * (a.w + b4.w);
+        *xp = x;
+      }
+    }
+  }
+}
+
 // ============================================================ bf16: direct-to-LDS
 constexpr int DBK = 32;          // K elements per stage
 constexpr int DSTAGES = 4;       // LDS ring depth
 constexpr int DROW = DBK * 2;    // bytes per LDS row (64)
 
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Chosen by measuring SQ_LDS_BANK_CONFLICT on this exact fragment-read pattern:
+// ((r>>1)^(r>>3))&3 conflicts on half of the LDS cycles, this one on none.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 2)) & 3; }
 
 template <int EPI, int SEC, int BN>
-__global__ __launch_bounds__(256) void gemm_direct_kernel(GemmArgs p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_direct_kernel(GemmArgs p) {
   constexpr int BM = 256, WM = 2, WN = 2;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
@@ -231,12 +278,7 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(GemmArgs p) {
   static_assert(EPI != EPI_QKV || TN == SEC, "QKV wave tile must be one head section");
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU needs paired gate/value tiles");
 
-  // one LDS array per ring slot, so every load and fragment read below names its
-  // buffer statically (the K loop is unrolled by the ring depth)
-  __shared__ __attribute__((aligned(1024))) char ring0[STAGE];
-  __shared__ __attribute__((aligned(1024))) char ring1[STAGE];
-  __shared__ __attribute__((aligned(1024))) char ring2[STAGE];
-  __shared__ __attribute__((aligned(1024))) char ring3[STAGE];
+  __shared__ __attribute__((aligned(1024))) char ring[DSTAGES * STAGE];
   __shared__ int s_tag[EPI == EPI_RESID ? BM : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -266,10 +308,10 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(GemmArgs p) {
       ldso[s] = BM * DROW + (j - NA) * 1024;
     }
   }
-  auto issue = [&](int kt, char* buf) __attribute__((always_inline)) {
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    char* buf = ring + (kt % DSTAGES) * STAGE;
 #pragma unroll
-    for (int s = 0; s < NI; ++s)
-      dma16(src[s] + kt * DBK, buf + ldso[s]);
+    for (int s = 0; s < NI; ++s) dma16(src[s] + kt * DBK, buf + ldso[s]);
   };
 
   // fragment offsets inside a stage: row (lane%32) of each 32-row tile, chunk
@@ -285,52 +327,74 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-  auto compute = [&](const char* buf) __attribute__((always_inline)) {
-    const char* As = buf + (wm * TM) * DROW;
-    const char* Bs = buf + (BM + wn * TN) * DROW;
+  // fragments of one 16-wide k step: A rows (wm*TM + 32i + lane%32), B rows likewise
+  auto read_frags = [&](int kt, int kk, bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) __attribute__((always_inline)) {
+    const char* buf = ring + (kt % DSTAGES) * STAGE;
+    const char* As = buf + (wm * TM) * DROW + foff[kk];
+    const char* Bs = buf + (BM + wn * TN) * DROW + foff[kk];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 af[FM], bfr[FN];
+    for (int i = 0; i < FM; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * DROW);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * DROW + foff[kk]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + j * 32 * DROW + foff[kk]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
-    }
+    for (int j = 0; j < FN; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(Bs + j * 32 * DROW);
   };
-  // one ring step: wait for this wave's loads of stage kt (the `ahead` later
-  // stages may stay in flight), barrier so every wave's loads have landed and
-  // every wave is done with the slot about to be refilled, refill it with stage
-  // kt + 3, then consume stage kt.
-  auto step = [&](int kt, const char* cur, char* refill, int KT) __attribute__((always_inline)) {
-    const int ahead = KT - 1 - kt;
-    if (ahead >= 2) {
-      wait_vmcnt<2 * NI>();
-    } else if (ahead == 1) {
+  auto mfmas = [&](const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+  };
+  // keep the LDS reads of the next k step behind the first MFMA of the current
+  // one: they arrive under the remaining MFMAs, and no more than 15 LDS reads
+  // are ever outstanding (the range the wait counter expresses)
+  auto interleave = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - 1, 0);
+  };
+
+  // Software pipeline over stages of BK = 32 (two 16-wide k steps each).  At
+  // the top of iteration kt, stage kt is visible in LDS and its first k step's
+  // fragments are loaded.  The barrier sits between the two k steps: stage
+  // kt+1 must have landed for every wave, and every wave must be done reading
+  // stage kt-1, whose slot is then refilled with stage kt+3.
+  const int KT = K / DBK;
+  issue(0);
+  if (KT > 1) issue(1);
+  if (KT > 2) issue(2);
+  if (KT > 2) {
+    wait_vmcnt<2 * NI>();
+  } else if (KT > 1) {
+    wait_vmcnt<NI>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  __builtin_amdgcn_s_barrier();
+  bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  read_frags(0, 0, fa0, fb0);
+  for (int kt = 0; kt < KT; ++kt) {
+    read_frags(kt, 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    interleave();
+    if (kt + 2 < KT) {
       wait_vmcnt<NI>();
     } else {
       wait_vmcnt<0>();
     }
     __builtin_amdgcn_s_barrier();
-    if (kt + 3 < KT) issue(kt + 3, refill);
-    compute(cur);
-  };
-
-  const int KT = K / DBK;   // a multiple of 4 (K % 128 == 0)
-  issue(0, ring0);
-  issue(1, ring1);
-  issue(2, ring2);
-  for (int kt = 0; kt < KT; kt += 4) {
-    step(kt + 0, ring0, ring3, KT);
-    step(kt + 1, ring1, ring0, KT);
-    step(kt + 2, ring2, ring1, KT);
-    step(kt + 3, ring3, ring2, KT);
+    if (kt + 3 < KT) issue(kt + 3);
+    // unconditional (past the last stage it reads a stale slot, unused), so the
+    // reads stay in one block with the MFMAs they are interleaved with
+    read_frags(kt + 1, 0, fa0, fb0);
+    mfmas(fa1, fb1);
+    interleave();
   }
   __syncthreads();
-  epilogue<BM, BN, WM, WN, EPI, SEC>(p, acc, m0, n0, tc.tn, wm, wn, lane, s_tag);
+  if constexpr (EPI == EPI_RESID) {
+    resid_epilogue_lds<TM, TN, FM, FN>(p, acc, m0 + wm * TM, n0 + wn * TN, wm * TM, lane,
+                                       reinterpret_cast<float*>(ring) + wave * 32 * RSTRIDE, s_tag);
+  } else {
+    epilogue<BM, BN, WM, WN, EPI, SEC>(p, acc, m0, n0, tc.tn, wm, wn, lane, s_tag);
+  }
 }
 
 // ============================================================ INT8: staged dequant
