@@ -260,6 +260,15 @@ def make_device_rows(wl: Workload, seed: int = 0, device: str = "cuda"):
     return x, torch.from_numpy(tags).to(device), torch.from_numpy(pos).to(device)
 
 
+def make_device_activation(n: int, width: int, seed: int, std: float = 1.0, device: str = "cuda"):
+    """bf16 [n, width] ~ N(0, std^2) drawn on the device (large stand-alone step inputs)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 1000003 + 3)
+    return (torch.randn(n, width, generator=g, device=device) * std).to(torch.bfloat16)
+
+
 def make_device_weights(dims: Dims, n_blocks: int, seed: int = 0, device: str = "cuda"):
     """Modulation table and per-block weights with the host generator's
     distributions, drawn on the device by torch.

@@ -1,0 +1,212 @@
+"""Parity at the benchmark's full sizes, in the launch configuration bench.py
+times (GPU).
+
+At N = 49,840 and N = 6,437 the float64 oracle cannot redo whole steps in a
+test, so every step runs in full on the GPU and the oracle recomputes sampled
+outputs one by one from the same inputs: sampled rows for the row-local steps,
+sampled (head, query) pairs over all keys for attention.  Inputs this large are
+drawn on the device by torch's seeded generator and copied to the host for the
+oracle; no value the HIP path computes is ever an oracle input.  The 50-block
+forwards are checked through properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from joint_video_audio_h3_amd import lib, synth
+from tests.gpu_util import (TOL_ATTN, TOL_BF16_OUT, TOL_BLOCK, TOL_RESID_DELTA, dev, host_bf16,
+                            rel_l2, say)
+
+pytestmark = pytest.mark.gpu
+H3 = synth.H3_DIMS
+SIZES = [6437, 49840]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    lib.load()
+
+
+@pytest.fixture(scope="module")
+def block_weights():
+    host = synth.make_block_weights(H3, 0, seed=11)
+    return host, lib.to_device_block(host)
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _rows(n, k=24, seed=0):
+    r = np.random.default_rng(seed).choice(n, size=k - 3, replace=False)
+    return np.unique(np.concatenate([r, [0, n // 2, n - 1]]))
+
+
+@pytest.mark.parametrize("n", SIZES)
+def test_fullsize_adaln(n):
+    say("fullsize adaln", n)
+    x = synth.make_device_rows(synth.Workload("f", H3, 1, n, 0, 0, (0, 0, 0)), seed=5)[0]
+    tags = torch.from_numpy(synth.make_tags(n, 3, seed=5)).cuda()
+    table = synth.make_table(H3, 1, seed=5)[0]
+    h = torch.empty(n, H3.hidden, dtype=torch.int16, device="cuda")
+    lib.adaln_modulate(H3, x, tags, dev(table), 0, h)
+    torch.cuda.synchronize()
+    rows = _rows(n)
+    xr = x[rows].cpu().numpy()
+    m = oracle.modulation_from_table(table, tags.cpu().numpy()[rows])
+    ref = oracle.adaln_modulate(xr, m["shift1"], m["scale1"], H3.ln_eps)
+    assert rel_l2(host_bf16(h[rows]), ref) < TOL_BF16_OUT
+
+
+@pytest.mark.parametrize("n", SIZES)
+def test_fullsize_qkv_rope(n, block_weights):
+    say("fullsize qkv", n)
+    host, devw = block_weights
+    h = synth.make_device_activation(n, H3.hidden, seed=6)
+    pos = synth.make_positions(n, seed=6)
+    np_ = lib.padded_rows(n)
+    cs = torch.empty(np_, 64, 2, dtype=torch.float32, device="cuda")
+    lib.rope_table(H3, dev(pos), n, cs)
+    q = torch.empty(H3.heads, np_, 128, dtype=torch.int16, device="cuda")
+    k = torch.empty_like(q)
+    vt = torch.empty(H3.heads, 128, np_, dtype=torch.int16, device="cuda")
+    lib.qkv_rope(H3, h, devw, cs, n, q, k, vt)
+    torch.cuda.synchronize()
+    rows = _rows(n, 16)
+    hh = oracle.bf16_to_f64(_bits(h[rows]))
+    u = hh @ oracle.weight(host, "qkv").T + oracle.bias(host, "qkv", 3 * H3.inner)
+    rq, rk, rv = oracle.qkv_split(u, H3.heads, 128)
+    ang = oracle.rope_angles(pos[rows], H3.rope_split, H3.rope_theta)
+    rq = oracle.apply_rope(oracle.rms_norm(rq, oracle.bf16_to_f64(host["q_norm"]), H3.qk_eps), ang)
+    rk = oracle.apply_rope(oracle.rms_norm(rk, oracle.bf16_to_f64(host["k_norm"]), H3.qk_eps), ang)
+    qs = np.log2(np.e) / np.sqrt(128)
+    ridx = torch.from_numpy(rows).cuda()
+    assert rel_l2(host_bf16(q[:, ridx]) / qs, rq) < TOL_BF16_OUT
+    assert rel_l2(host_bf16(k[:, ridx]), rk) < TOL_BF16_OUT
+    assert rel_l2(host_bf16(vt[:, :, ridx]).transpose(0, 2, 1), rv) < TOL_BF16_OUT
+    # pad rows are zeros
+    assert int(q[:, n:].abs().sum()) == 0 and int(vt[:, :, n:].abs().sum()) == 0
+
+
+@pytest.mark.parametrize("n", SIZES)
+def test_fullsize_attention(n):
+    say("fullsize attention", n)
+    H, d = H3.heads, 128
+    np_ = lib.padded_rows(n)
+    qs = float(np.log2(np.e) / np.sqrt(d))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    q = torch.zeros(H, np_, d, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros_like(q)
+    v = torch.zeros_like(q)
+    q[:, :n] = (torch.randn(H, n, d, generator=g, device="cuda") * qs).to(torch.bfloat16)
+    k[:, :n] = torch.randn(H, n, d, generator=g, device="cuda").to(torch.bfloat16)
+    v[:, :n] = torch.randn(H, n, d, generator=g, device="cuda").to(torch.bfloat16)
+    vt = v.transpose(1, 2).contiguous()
+    o = torch.empty(n, H * d, dtype=torch.int16, device="cuda")
+    lib.attention(H3, q.view(torch.int16), k.view(torch.int16), vt.view(torch.int16), n, o)
+    torch.cuda.synchronize()
+    heads = [0, 17, 55]
+    rows = _rows(n, 12, seed=1)
+    got = host_bf16(o[torch.from_numpy(rows).cuda()])
+    for hd in heads:
+        qh = oracle.bf16_to_f64(_bits(q[hd, :n][rows])) / qs
+        kh = oracle.bf16_to_f64(_bits(k[hd, :n]))
+        vh = oracle.bf16_to_f64(_bits(v[hd, :n]))
+        ref = oracle.attention(qh[None], kh[None], vh[None])[0]
+        assert rel_l2(got[:, hd * d:(hd + 1) * d], ref) < TOL_ATTN, hd
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("which", ["out", "fc2"])
+def test_fullsize_gated_residual(n, which, block_weights):
+    say("fullsize residual", which, n)
+    host, devw = block_weights
+    K = H3.inner if which == "out" else H3.ffn
+    a = synth.make_device_activation(n, K, seed=8, std=0.3)
+    x = synth.make_device_rows(synth.Workload("f", H3, 1, n, 0, 0, (0, 0, 0)), seed=8)[0]
+    x0 = x.clone()
+    tags = synth.make_tags(n, 3, seed=8)
+    table = synth.make_table(H3, 1, seed=8)[0]
+    fn = lib.out_proj_residual if which == "out" else lib.mlp_fc2_residual
+    fn(H3, a.view(torch.int16), devw, dev(table), dev(tags), x)
+    torch.cuda.synchronize()
+    rows = _rows(n, 16, seed=2)
+    ridx = torch.from_numpy(rows).cuda()
+    got = (x[ridx] - x0[ridx]).cpu().numpy().astype(np.float64)
+    name = "out" if which == "out" else "fc2"
+    g = oracle.modulation_from_table(table, tags[rows])["gate1" if which == "out" else "gate2"]
+    ref = g * (oracle.bf16_to_f64(_bits(a[ridx])) @ oracle.weight(host, name).T
+               + oracle.bias(host, name, H3.hidden))
+    assert rel_l2(got, ref) < TOL_RESID_DELTA
+
+
+@pytest.mark.parametrize("n", SIZES)
+def test_fullsize_fc1_swiglu(n, block_weights):
+    say("fullsize fc1", n)
+    host, devw = block_weights
+    h2 = synth.make_device_activation(n, H3.hidden, seed=9)
+    a = torch.empty(n, H3.ffn, dtype=torch.int16, device="cuda")
+    lib.mlp_fc1_swiglu(H3, h2.view(torch.int16), devw, a)
+    torch.cuda.synchronize()
+    rows = _rows(n, 16, seed=3)
+    ridx = torch.from_numpy(rows).cuda()
+    z = oracle.bf16_to_f64(_bits(h2[ridx])) @ oracle.weight(host, "fc1").T + oracle.bias(host, "fc1", 2 * H3.ffn)
+    assert rel_l2(host_bf16(a[ridx]), oracle.swiglu(z, H3.ffn)) < TOL_BF16_OUT
+
+
+def test_fullsize_block_n6437_sampled_rows(block_weights):
+    """The whole block at N = 6,437 (the 50-block workload's packed layout),
+    compared on sampled output rows; keys and values use every row."""
+    wl = synth.WORKLOADS["h3_50blk_n6437"]
+    say("fullsize block", wl.n_rows)
+    host, devw = block_weights
+    tags, pos = synth.packed_layout(wl)
+    x = synth.make_x(wl, H3, seed=12)
+    table = synth.make_table(H3, 1, seed=12)
+    xd = dev(x)
+    ws = lib.alloc_workspace(H3, wl.n_rows)
+    lib.dit_block_forward(H3, xd, dev(tags), dev(pos), dev(table[0]), devw, ws)
+    torch.cuda.synchronize()
+    rows = _rows(wl.n_rows, 24, seed=4)
+    got = xd.cpu().numpy().astype(np.float64)[rows]
+    ref = oracle.block_forward(x, tags, pos, table[0], host, H3, q_rows=rows)
+    xr = x[rows].astype(np.float64)
+    assert rel_l2(got, ref) < TOL_BLOCK
+    assert rel_l2(got - xr, ref - xr) < 2 * TOL_BLOCK
+
+
+@pytest.fixture(scope="module")
+def fifty_blocks():
+    table, blocks = synth.make_device_weights(H3, 50, seed=3)
+    yield table, blocks
+    del table, blocks
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("wname", ["h3_50blk_n6437", "h3_50blk_n49840"])
+def test_full_depth_properties(wname, fifty_blocks):
+    """The 50-block forward at full size: finite, bit-identical run to run, and
+    with every residual gate zero it returns x unchanged, bit for bit."""
+    wl = synth.WORKLOADS[wname]
+    say("full depth", wname)
+    table, blocks = fifty_blocks
+    x, tags, pos = synth.make_device_rows(wl, seed=4)
+    ws = lib.alloc_workspace(H3, wl.n_rows)
+    a = x.clone()
+    b = x.clone()
+    lib.dit_forward(H3, a, tags, pos, table, blocks, ws)
+    lib.dit_forward(H3, b, tags, pos, table, blocks, ws)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(a).all())
+    assert torch.equal(a, b)
+    assert float((a - x).abs().max()) > 0.1
+    t0 = table.clone()
+    t0[:, :, 2] = 0
+    t0[:, :, 5] = 0
+    c = x.clone()
+    lib.dit_forward(H3, c, tags, pos, t0, blocks, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(c, x)
