@@ -89,6 +89,10 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs p) {
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) qf[qs][ds] = *reinterpret_cast<const bf16x8*>(qp + ds * 16);
   }
+  // Land the Q loads now (vmcnt(0) via the builtin, which the compiler's wait
+  // bookkeeping understands): otherwise it keeps them "pending" into the key
+  // loop and its vmcnt waits there would also wait for the K/V tiles in flight.
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
 
   // DMA sources: K slots fill 4 rows of 256 B per load (lane -> row l/16,
   // position l%16 holding chunk (l%16)^kswz(row)); V^T slots fill 8 rows of

@@ -257,6 +257,90 @@ __device__ __forceinline__ void resid_epilogue_lds(const GemmArgs& p, f32x16 (&a
   }
 }
 
+// QKV epilogue through LDS (head_dim 128): each wavefront owns one 128-wide
+// section (q, k or v of one head) and stages it 32 rows at a time.
+//  q, k: lanes (row = l % 32, half = l / 32) read 64 values of a row as float4,
+//        the RMS needs one cross-half add, rotary pairs sit inside each float4,
+//        and the bf16 row half (128 B) is written with 16-byte stores.
+//  v:    each lane takes two columns and writes 32 consecutive keys of V^T
+//        (64 B) with 16-byte stores.
+constexpr int QSTRIDE = 136;   // floats per staged row
+
+template <int TM, int FM, int FN>
+__device__ __forceinline__ void qkv_epilogue_lds(const GemmArgs& p, f32x16 (&acc)[FM][FN],
+                                                 int row0, int sec, int lane, float* stage) {
+  static_assert(FN == 4, "one 128-wide head section per wavefront");
+  const int kind = sec % 3, head = sec / 3;
+  const int hl = lane >> 5, lc = lane & 31;
+  float bias_c[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) bias_c[j] = p.bias ? bf2f(p.bias[sec * 128 + j * 32 + lc]) : 0.f;
+  const uint16_t* gam = kind == 0 ? p.gq : p.gk;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        stage[(8 * (v / 4) + 4 * hl + (v % 4)) * QSTRIDE + j * 32 + lc] = acc[i][j][v] + bias_c[j];
+    const int slab = row0 + i * 32;
+    if (kind < 2) {
+      const int r = lc, c0 = 64 * hl;
+      const int row = slab + r;
+      const float* src = stage + r * QSTRIDE + c0;
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float4 u = *reinterpret_cast<const float4*>(src + 4 * k);
+        ss += (u.x * u.x + u.y * u.y) + (u.z * u.z + u.w * u.w);
+      }
+      ss += __shfl_xor(ss, 32, 64);
+      const float rn = 1.0f / sqrtf(ss / 128.0f + p.qk_eps);
+      const float sc = kind == 0 ? rn * p.q_scale : rn;
+      const float4* cs = reinterpret_cast<const float4*>(p.cs + (size_t)row * 128 + c0);
+      uint16_t* dst = (kind == 0 ? p.q : p.k) + ((size_t)head * p.n_pad + row) * 128 + c0;
+      const bool valid = row < p.M;
+#pragma unroll
+      for (int k = 0; k < 16; k += 2) {
+        uint32_t w[4];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int c = 4 * (k + kk);
+          const float4 u = *reinterpret_cast<const float4*>(src + c);
+          const float4 t = cs[k + kk];   // (cos, sin) of the two pairs in u
+          float g0 = 1.f, g1 = 1.f, g2 = 1.f, g3 = 1.f;
+          if (gam) {
+            const u16x4 gg = *reinterpret_cast<const u16x4*>(gam + c0 + c);
+            g0 = bf2f(gg[0]); g1 = bf2f(gg[1]); g2 = bf2f(gg[2]); g3 = bf2f(gg[3]);
+          }
+          const float a0 = u.x * g0, a1 = u.y * g1, b0 = u.z * g2, b1 = u.w * g3;
+          const float o0 = (a0 * t.x - a1 * t.y) * sc, o1 = (a0 * t.y + a1 * t.x) * sc;
+          const float o2 = (b0 * t.z - b1 * t.w) * sc, o3 = (b0 * t.w + b1 * t.z) * sc;
+          w[2 * kk] = valid ? pack2bf(o0, o1) : 0u;
+          w[2 * kk + 1] = valid ? pack2bf(o2, o3) : 0u;
+        }
+        *reinterpret_cast<uint4*>(dst + 4 * k) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    } else {
+      uint16_t* vt = p.vt + (size_t)head * 128 * p.n_pad + slab;
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int c = lane + 64 * cc;
+        uint32_t w[16];
+#pragma unroll
+        for (int r = 0; r < 32; r += 2) {
+          const float x0 = slab + r < p.M ? stage[r * QSTRIDE + c] : 0.f;
+          const float x1 = slab + r + 1 < p.M ? stage[(r + 1) * QSTRIDE + c] : 0.f;
+          w[r / 2] = pack2bf(x0, x1);
+        }
+        uint4* d = reinterpret_cast<uint4*>(vt + (size_t)c * p.n_pad);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) d[q4] = make_uint4(w[4 * q4], w[4 * q4 + 1], w[4 * q4 + 2], w[4 * q4 + 3]);
+      }
+    }
+  }
+}
+
 // ============================================================ bf16: direct-to-LDS
 constexpr int DBK = 32;          // K elements per stage
 constexpr int DSTAGES = 4;       // LDS ring depth
@@ -392,6 +476,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if constexpr (EPI == EPI_RESID) {
     resid_epilogue_lds<TM, TN, FM, FN>(p, acc, m0 + wm * TM, n0 + wn * TN, wm * TM, lane,
                                        reinterpret_cast<float*>(ring) + wave * 32 * RSTRIDE, s_tag);
+  } else if constexpr (EPI == EPI_QKV && SEC == 128) {
+    const int sec = (n0 + wn * TN) / SEC;
+    if (sec < 3 * p.heads)
+      qkv_epilogue_lds<TM, FM, FN>(p, acc, m0 + wm * TM, sec, lane,
+                                   reinterpret_cast<float*>(ring) + wave * 32 * QSTRIDE);
   } else {
     epilogue<BM, BN, WM, WN, EPI, SEC>(p, acc, m0, n0, tc.tn, wm, wn, lane, s_tag);
   }
