@@ -36,8 +36,9 @@
  *   - Modality tags must lie in [0, n_tags); rows are not checked on device.
  *
  * Supported shapes: hidden % 256 == 0 and hidden <= 8192; head_dim in
- * {96, 128}; ffn % 128 == 0; rope_split entries even and summing to
- * head_dim; 1 <= n_tags <= 8; 1 <= n_rows <= 2^24.
+ * {96, 128}; ffn % 128 == 0 and (ffn + 256) * hidden * 2 < 2^32; rope_split
+ * entries even and summing to head_dim; 1 <= n_tags <= 8;
+ * 1 <= n_rows <= 2^24.
  */
 #ifndef H3DIT_H
 #define H3DIT_H

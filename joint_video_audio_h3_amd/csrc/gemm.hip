@@ -7,12 +7,23 @@
 // bf16 weights (gemm_direct_kernel): 256 x 256 block tile (256 x 192 for the
 // 96-wide heads of the small model), four wavefronts in 2 x 2, each owning a
 // 128 x 128 (x 96) sub-tile of v_mfma_f32_32x32x16_bf16 accumulators.  Tiles
-// move HBM/L2 -> LDS with global_load_lds_dwordx4 (no staging registers), in
-// a 4-deep ring of BK = 32 stages: three stages are in flight while one is
-// consumed.  LDS rows are 64 B (4 chunks of 16 B) and chunk c of row r is
-// stored at position c ^ f(r), f(r) = (r ^ (r>>2)) & 3, which measures free of
-// LDS bank conflicts for the 16-byte fragment reads; the permutation is applied
-// by choosing which global chunk each lane of a load fetches.
+// move HBM/L2 -> LDS with global_load_lds_dwordx4 (no staging registers) in
+// stages of BK = 64, so each row segment is one full 128-byte line (measured to
+// stream at twice the rate of 64-byte segments).  The LDS ring holds five
+// half-stage slots (an A or a B half of a stage each, 32 KB): while one stage
+// is consumed, the next stage and half of the one after are in flight.  The
+// loads of a stage are spread over the MFMA stream, one after every MFMA
+// quarter of a k step: a burst stalls the issuing wave until the load path has
+// taken it, and with one wave per SIMD nothing else feeds the matrix core.  The
+// K loop is unrolled by the ring period (5) so every slot offset is a
+// compile-time immediate: loads take a wave-uniform SGPR base plus a per-lane
+// offset fixed for the whole loop, and fragment reads a per-lane base plus an
+// immediate, which keeps address arithmetic out of the loop.  Chunk c of LDS
+// row r is stored at position c ^ f(r), f(r) = (r ^ (r>>3)) & 7, measured free
+// of LDS bank conflicts for the 16-byte fragment reads; the permutation is
+// applied by choosing which global chunk each lane of a load fetches.  Fragment
+// reads of the next 16-wide k step are scheduled behind the current step's
+// first MFMA.
 //
 // INT8 weights (gemm_staged_kernel): same MFMA tiling with eight wavefronts;
 // 16-byte chunks of int8 codes go through registers, where they are
@@ -46,13 +57,14 @@
 //             pipeline" and "Metal 4 and TensorOps paths": fused
 //             QK-normalisation/RoPE, Q/K/V routed straight to head-major
 //             attention inputs).
+#include <type_traits>
+
 #include "h3_device.h"
 #include "launch.h"
 
 namespace h3 {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
 // Written as asm with a memory clobber so no LDS access moves across it.
@@ -60,15 +72,6 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
-// at lds + 16*l (M0 holds the wave-uniform LDS address).  Issued as asm so the
-// compiler's wait insertion does not drain every in-flight stage before each
-// LDS read; completion is tracked explicitly with wait_vmcnt.
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-  const uint32_t la = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(la) : "memory");
 }
 
 struct TileCoord {
@@ -219,8 +222,7 @@ constexpr int RSTRIDE = 136;   // floats per staged row (128 + 8 of padding)
 
 template <int TM, int TN, int FM, int FN>
 __device__ __forceinline__ void resid_epilogue_lds(const GemmArgs& p, f32x16 (&acc)[FM][FN],
-                                                   int row0, int col0, int tag_row0, int lane,
-                                                   float* stage, const int* s_tag) {
+                                                   int row0, int col0, int lane, float* stage) {
   static_assert(TN == 128, "one float4 per lane covers a 128-wide row");
   const int hl = lane >> 5, lc = lane & 31;
   const int gcol = col0 + 4 * lc;
@@ -243,7 +245,7 @@ __device__ __forceinline__ void resid_epilogue_lds(const GemmArgs& p, f32x16 (&a
       const int row = row0 + i * 32 + r;
       const float4 a = *reinterpret_cast<const float4*>(stage + r * RSTRIDE + 4 * lc);
       if (row < p.M && col_ok) {
-        const int t = s_tag[tag_row0 + i * 32 + r];
+        const int t = p.tag[row];
         const u16x4 g = *reinterpret_cast<const u16x4*>(p.gate_tab + (size_t)t * p.tag_stride + gcol);
         float4* xp = reinterpret_cast<float4*>(p.x + (size_t)row * p.ldx + gcol);
         float4 x = *xp;
@@ -342,147 +344,271 @@ __device__ __forceinline__ void qkv_epilogue_lds(const GemmArgs& p, f32x16 (&acc
 }
 
 // ============================================================ bf16: direct-to-LDS
-constexpr int DBK = 32;          // K elements per stage
-constexpr int DSTAGES = 4;       // LDS ring depth
-constexpr int DROW = DBK * 2;    // bytes per LDS row (64)
+constexpr int DBK = 64;          // K elements per stage
+constexpr int DROW = DBK * 2;    // bytes per LDS row: one full 128-byte line per row
+constexpr int HSLOT = 32768;     // one half stage (256 rows of A, or of B)
+constexpr int NSLOT = 5;         // ring of half-stage slots
 
-// Chosen by measuring SQ_LDS_BANK_CONFLICT on this exact fragment-read pattern:
-// ((r>>1)^(r>>3))&3 conflicts on half of the LDS cycles, this one on none.
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 2)) & 3; }
+// Chunk c of row r sits at position c ^ f(r); measured free of LDS bank
+// conflicts for the fragment reads (row lane%32 of each 32-row tile, chunk
+// 2*kk + lane/32).  Depends on bits 0..5 of r.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_t;
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t a) { return *(lds_bf16x8_t*)(size_t)a; }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr_t)p; }
+
+// 16 bytes per lane from sbase + voff (sbase wave-uniform, in SGPRs) straight
+// into LDS at lds + 16*lane (M0).  Asm keeps the compiler's wait insertion from
+// draining in-flight stages before LDS reads; completion is tracked with
+// wait_vmcnt.
+__device__ __forceinline__ void dma16s(uint32_t voff, const char* sbase, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+
+// lowest weight row a tile reads (the per-lane offsets are relative to it)
+template <int EPI, int BN>
+__device__ __forceinline__ int weight_row_base(int tn) {
+  return EPI == EPI_SWIGLU ? tn * (BN / 2) : tn * BN;
+}
+
+template <int V>
+using ic = std::integral_constant<int, V>;
 
 template <int EPI, int SEC, int BN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_direct_kernel(GemmArgs p) {
   constexpr int BM = 256, WM = 2, WN = 2;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int NA = BM / 16, NB = BN / 16;   // 1 KB (16-row) loads per stage
-  constexpr int NI = (NA + NB) / 4;           // per wavefront
-  constexpr int STAGE = (BM + BN) * DROW;
-  static_assert((NA + NB) % 4 == 0, "loads must split evenly over the waves");
+  constexpr int NA = BM / 32, NB = BN / 32;   // 1 KB (8-row) loads per half stage per wave
+  constexpr int NA2 = NA / 2, NB2 = NB / 2;
+  constexpr int NM = FM * FN, Q = NM / 4;
+  static_assert(BM % 32 == 0 && BN % 32 == 0 && BN <= 256, "half-stage split");
+  static_assert(NM % 4 == 0, "MFMA quarters");
   static_assert(EPI != EPI_QKV || TN == SEC, "QKV wave tile must be one head section");
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU needs paired gate/value tiles");
 
-  __shared__ __attribute__((aligned(1024))) char ring[DSTAGES * STAGE];
-  __shared__ int s_tag[EPI == EPI_RESID ? BM : 1];
+  __shared__ __attribute__((aligned(1024))) char ring[NSLOT * HSLOT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const TileCoord tc = tile_coord<EPI, BM, BN>(p);
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
-  if (EPI == EPI_RESID) {
-    for (int i = tid; i < BM; i += 256) s_tag[i] = p.tag[min(m0 + i, p.M - 1)];
-  }
-
-  // per-lane source of each of this wave's NI loads; lane l fills row 16*j + l/4,
-  // LDS position l%4, which holds global chunk (l%4) ^ f(row)
   const int K = p.K;
-  const uint16_t* src[NI];
-  int ldso[NI];
+  const uint32_t rowb = (uint32_t)K * 2;
+
+  // Loads: wave-uniform tile bases (SGPRs) advanced 128 B per stage, plus
+  // per-lane 32-bit offsets fixed for the whole K loop.  Load s of a half
+  // covers rows 8*(wave + 4s) .. +7; lane l fills row 8*(wave + 4s) + l/8,
+  // position l%8, which holds global chunk (l%8) ^ f(row).
+  const char* baseA = reinterpret_cast<const char*>(p.A) + (size_t)m0 * rowb;
+  const int b0 = weight_row_base<EPI, BN>(tc.tn);
+  const char* baseB = reinterpret_cast<const char*>(p.B) + (size_t)b0 * rowb;
+  uint32_t voA[NA], voB[NB];
 #pragma unroll
-  for (int s = 0; s < NI; ++s) {
-    const int j = wave + 4 * s;
-    const int r = 16 * (j < NA ? j : j - NA) + lane / 4;
-    const int chunk = (lane & 3) ^ swz(r);
-    if (j < NA) {
-      src[s] = p.A + (size_t)min(m0 + r, p.M - 1) * K + chunk * 8;
-      ldso[s] = j * 1024;
-    } else {
-      const int brow = weight_row<EPI, BN, TN>(p, tc.tn, r);
-      src[s] = reinterpret_cast<const uint16_t*>(p.B) + (size_t)brow * K + chunk * 8;
-      ldso[s] = BM * DROW + (j - NA) * 1024;
-    }
+  for (int s = 0; s < NA; ++s) {
+    const int r = 8 * (wave + 4 * s) + lane / 8;
+    voA[s] = (uint32_t)(min(m0 + r, p.M - 1) - m0) * rowb + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
   }
-  auto issue = [&](int kt) __attribute__((always_inline)) {
-    char* buf = ring + (kt % DSTAGES) * STAGE;
 #pragma unroll
-    for (int s = 0; s < NI; ++s) dma16(src[s] + kt * DBK, buf + ldso[s]);
+  for (int s = 0; s < NB; ++s) {
+    const int r = 8 * (wave + 4 * s) + lane / 8;
+    voB[s] = (uint32_t)(weight_row<EPI, BN, TN>(p, tc.tn, r) - b0) * rowb + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+  }
+  const uint32_t ring0 = lds_addr(ring);
+  // this wave's part of a slot; re-defined (empty asm) at each step so the
+  // per-load M0 values are formed next to their loads rather than hoisted
+  uint32_t mw = __builtin_amdgcn_readfirstlane(ring0 + wave * 1024);
+  // loads [lo, hi) of the A (B) half of stage ks into slot S
+  auto dmaA = [&](auto S_, int ks, int lo, int hi) __attribute__((always_inline)) {
+    constexpr int S = decltype(S_)::value;
+    const char* sb = baseA + (size_t)ks * (DBK * 2);
+#pragma unroll
+    for (int s = lo; s < hi; ++s) dma16s(voA[s], sb, mw + S * HSLOT + s * 4096);
+  };
+  auto dmaB = [&](auto S_, int ks, int lo, int hi) __attribute__((always_inline)) {
+    constexpr int S = decltype(S_)::value;
+    const char* sb = baseB + (size_t)ks * (DBK * 2);
+#pragma unroll
+    for (int s = lo; s < hi; ++s) dma16s(voB[s], sb, mw + S * HSLOT + s * 4096);
   };
 
-  // fragment offsets inside a stage: row (lane%32) of each 32-row tile, chunk
-  // 2*kk + lane/32 at its swizzled position
-  const int fr = lane & 31, h = lane >> 5;
-  int foff[2];
+  // Fragment reads: row lane%32 of each 32-row tile, chunk 2*kk + lane/32 at
+  // its swizzled position (bit 5 of the row, the tile parity, enters the
+  // swizzle).  Per-lane bases for three 64 KB windows of the ring, so every
+  // read is base + immediate.
+  const int fr = lane & 31, hl = lane >> 5;
+  uint32_t rA[3][2][4], rB[3][2][4];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) foff[kk] = fr * DROW + (((2 * kk + h) ^ swz(fr)) * 16);
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint32_t xa = fr * DROW + (((2 * kk + hl) ^ swz(fr + 32 * par)) * 16);
+      const int pb = ((wn * TN) / 32 + par) & 1;
+      const uint32_t xb = fr * DROW + (((2 * kk + hl) ^ swz(fr + 32 * pb)) * 16);
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+        rA[w][par][kk] = ring0 + w * 65536 + wm * TM * DROW + xa;
+        rB[w][par][kk] = ring0 + w * 65536 + wn * TN * DROW + xb;
+      }
+    }
+  auto read_frags = [&](auto SA_, auto SB_, int kk, bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) __attribute__((always_inline)) {
+    constexpr int SA = decltype(SA_)::value, SB = decltype(SB_)::value;
+    constexpr int WA = SA * HSLOT / 65536, WB = SB * HSLOT / 65536;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[i] = lds_read16(rA[WA][i & 1][kk] + (SA * HSLOT - WA * 65536) + i * 32 * DROW);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[j] = lds_read16(rB[WB][j & 1][kk] + (SB * HSLOT - WB * 65536) + j * 32 * DROW);
+  };
 
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
-
-  // fragments of one 16-wide k step: A rows (wm*TM + 32i + lane%32), B rows likewise
-  auto read_frags = [&](int kt, int kk, bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) __attribute__((always_inline)) {
-    const char* buf = ring + (kt % DSTAGES) * STAGE;
-    const char* As = buf + (wm * TM) * DROW + foff[kk];
-    const char* Bs = buf + (BM + wn * TN) * DROW + foff[kk];
+  auto mfma_range = [&](const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN], int q0, int q1) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * DROW);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(Bs + j * 32 * DROW);
+    for (int q = q0; q < q1; ++q) acc[q / FN][q % FN] = mfma32(fa[q / FN], fb[q % FN], acc[q / FN][q % FN]);
   };
-  auto mfmas = [&](const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
-  };
-  // keep the LDS reads of the next k step behind the first MFMA of the current
-  // one: they arrive under the remaining MFMAs, and no more than 15 LDS reads
-  // are ever outstanding (the range the wait counter expresses)
-  auto interleave = [&]() __attribute__((always_inline)) {
+  // One k step: the next k step's fragment reads go behind its first MFMA, and
+  // the group's loads are spread one part per MFMA quarter (a burst of loads
+  // stalls the issuing wave until the load path accepts them, and with one
+  // wave per SIMD nothing else feeds the matrix core meanwhile).
+  auto group = [&](const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN], auto&& reads, auto&& loads) __attribute__((always_inline)) {
+    reads();
+    mfma_range(fa, fb, 0, Q);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, Q - 1, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_barrier(0);
+      loads(q);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q < 3) mfma_range(fa, fb, (q + 1) * Q, (q + 2) * Q);
+    }
+  };
+  auto part = [](int lo, int hi, int q) __attribute__((always_inline)) { return lo + ((hi - lo) * q) / 4; };
+
+  bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  // Ring of five half-stage slots: the A half of stage s in slot 2s % 5, its B
+  // half in (2s+1) % 5.  Iteration kt computes stage kt; its four k-step groups
+  // issue, in order, the second half of stage kt+1's B loads, stage kt+2's A
+  // half (two groups), and, after the barrier that frees stage kt's slots, the
+  // first half of stage kt+2's B loads.  Before that barrier stage kt+1 must
+  // have landed, while stage kt+2's A half may stay in flight.  In the steady
+  // loop U = kt % 5 fixes every slot at compile time.
+  auto step = [&](auto U_, int kt) __attribute__((always_inline)) {
+    constexpr int U = decltype(U_)::value;
+    constexpr int SA = (2 * U) % 5, SB = (2 * U + 1) % 5;
+    constexpr int SA1 = (2 * U + 2) % 5, SB1 = (2 * U + 3) % 5;
+    constexpr int SA2 = (2 * U + 4) % 5, SB2 = (2 * U + 5) % 5;
+    asm volatile("" : "+s"(mw));
+    group(fa0, fb0, [&]() __attribute__((always_inline)) { read_frags(ic<SA>{}, ic<SB>{}, 1, fa1, fb1); },
+          [&](int q) __attribute__((always_inline)) { dmaB(ic<SB1>{}, kt + 1, part(NB2, NB, q), part(NB2, NB, q + 1)); });
+    group(fa1, fb1, [&]() __attribute__((always_inline)) { read_frags(ic<SA>{}, ic<SB>{}, 2, fa0, fb0); },
+          [&](int q) __attribute__((always_inline)) { dmaA(ic<SA2>{}, kt + 2, part(0, NA2, q), part(0, NA2, q + 1)); });
+    group(fa0, fb0, [&]() __attribute__((always_inline)) { read_frags(ic<SA>{}, ic<SB>{}, 3, fa1, fb1); },
+          [&](int q) __attribute__((always_inline)) { dmaA(ic<SA2>{}, kt + 2, part(NA2, NA, q), part(NA2, NA, q + 1)); });
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0): stage kt fully read
+    wait_vmcnt<NA>();
+    __builtin_amdgcn_s_barrier();
+    group(fa1, fb1, [&]() __attribute__((always_inline)) { read_frags(ic<SA1>{}, ic<SB1>{}, 0, fa0, fb0); },
+          [&](int q) __attribute__((always_inline)) { dmaB(ic<SB2>{}, kt + 2, part(0, NB2, q), part(0, NB2, q + 1)); });
   };
 
-  // Software pipeline over stages of BK = 32 (two 16-wide k steps each).  At
-  // the top of iteration kt, stage kt is visible in LDS and its first k step's
-  // fragments are loaded.  The barrier sits between the two k steps: stage
-  // kt+1 must have landed for every wave, and every wave must be done reading
-  // stage kt-1, whose slot is then refilled with stage kt+3.
+  // the same step with slots from the runtime phase and loads only where the
+  // stage exists (the last few stages of the K loop)
   const int KT = K / DBK;
-  issue(0);
-  if (KT > 1) issue(1);
-  if (KT > 2) issue(2);
-  if (KT > 2) {
-    wait_vmcnt<2 * NI>();
-  } else if (KT > 1) {
-    wait_vmcnt<NI>();
-  } else {
-    wait_vmcnt<0>();
-  }
-  __builtin_amdgcn_s_barrier();
-  bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  read_frags(0, 0, fa0, fb0);
-  for (int kt = 0; kt < KT; ++kt) {
-    read_frags(kt, 1, fa1, fb1);
-    mfmas(fa0, fb0);
-    interleave();
-    if (kt + 2 < KT) {
-      wait_vmcnt<NI>();
+  auto step_rt = [&](int kt) __attribute__((always_inline)) {
+    const uint32_t oa = (uint32_t)((2 * kt) % 5) * HSLOT, ob = (uint32_t)((2 * kt + 1) % 5) * HSLOT;
+    const uint32_t oa1 = (uint32_t)((2 * kt + 2) % 5) * HSLOT, ob1 = (uint32_t)((2 * kt + 3) % 5) * HSLOT;
+    const uint32_t oa2 = (uint32_t)((2 * kt + 4) % 5) * HSLOT, ob2 = (uint32_t)((2 * kt + 5) % 5) * HSLOT;
+    const bool n1 = kt + 1 < KT, n2 = kt + 2 < KT;
+    auto rd = [&](uint32_t xa_, uint32_t xb_, int kk, bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[i] = lds_read16(rA[0][i & 1][kk] + xa_ + i * 32 * DROW);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[j] = lds_read16(rB[0][j & 1][kk] + xb_ + j * 32 * DROW);
+    };
+    auto ld = [&](const char* base, const uint32_t (&vo)[NA > NB ? NA : NB], uint32_t slot, int ks, int lo, int hi) __attribute__((always_inline)) {
+      const char* sb = base + (size_t)ks * (DBK * 2);
+#pragma unroll
+      for (int s = lo; s < hi; ++s) dma16s(vo[s], sb, mw + slot + s * 4096);
+    };
+    (void)ld;
+    group(fa0, fb0, [&]() __attribute__((always_inline)) { rd(oa, ob, 1, fa1, fb1); },
+          [&](int q) __attribute__((always_inline)) {
+            if (n1) {
+              const char* sb = baseB + (size_t)(kt + 1) * (DBK * 2);
+#pragma unroll
+              for (int s = part(NB2, NB, q); s < part(NB2, NB, q + 1); ++s) dma16s(voB[s], sb, mw + ob1 + s * 4096);
+            }
+          });
+    group(fa1, fb1, [&]() __attribute__((always_inline)) { rd(oa, ob, 2, fa0, fb0); },
+          [&](int q) __attribute__((always_inline)) {
+            if (n2) {
+              const char* sb = baseA + (size_t)(kt + 2) * (DBK * 2);
+#pragma unroll
+              for (int s = part(0, NA2, q); s < part(0, NA2, q + 1); ++s) dma16s(voA[s], sb, mw + oa2 + s * 4096);
+            }
+          });
+    group(fa0, fb0, [&]() __attribute__((always_inline)) { rd(oa, ob, 3, fa1, fb1); },
+          [&](int q) __attribute__((always_inline)) {
+            if (n2) {
+              const char* sb = baseA + (size_t)(kt + 2) * (DBK * 2);
+#pragma unroll
+              for (int s = part(NA2, NA, q); s < part(NA2, NA, q + 1); ++s) dma16s(voA[s], sb, mw + oa2 + s * 4096);
+            }
+          });
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+    if (n2) {
+      wait_vmcnt<NA>();
     } else {
       wait_vmcnt<0>();
     }
     __builtin_amdgcn_s_barrier();
-    if (kt + 3 < KT) issue(kt + 3);
-    // unconditional (past the last stage it reads a stale slot, unused), so the
-    // reads stay in one block with the MFMAs they are interleaved with
-    read_frags(kt + 1, 0, fa0, fb0);
-    mfmas(fa1, fb1);
-    interleave();
+    group(fa1, fb1, [&]() __attribute__((always_inline)) { if (n1) rd(oa1, ob1, 0, fa0, fb0); },
+          [&](int q) __attribute__((always_inline)) {
+            if (n2) {
+              const char* sb = baseB + (size_t)(kt + 2) * (DBK * 2);
+#pragma unroll
+              for (int s = part(0, NB2, q); s < part(0, NB2, q + 1); ++s) dma16s(voB[s], sb, mw + ob2 + s * 4096);
+            }
+          });
+  };
+
+  dmaA(ic<0>{}, 0, 0, NA);
+  dmaB(ic<1>{}, 0, 0, NB);
+  if (KT > 1) {
+    dmaA(ic<2>{}, 1, 0, NA);
+    dmaB(ic<3>{}, 1, 0, NB2);
+    wait_vmcnt<NA + NB2>();
+  } else {
+    wait_vmcnt<0>();
   }
+  __builtin_amdgcn_s_barrier();
+  read_frags(ic<0>{}, ic<1>{}, 0, fa0, fb0);
+  int kt = 0;
+  for (; kt + 7 <= KT; kt += 5) {
+    step(ic<0>{}, kt);
+    step(ic<1>{}, kt + 1);
+    step(ic<2>{}, kt + 2);
+    step(ic<3>{}, kt + 3);
+    step(ic<4>{}, kt + 4);
+  }
+  for (; kt < KT; ++kt) step_rt(kt);
   __syncthreads();
   if constexpr (EPI == EPI_RESID) {
-    resid_epilogue_lds<TM, TN, FM, FN>(p, acc, m0 + wm * TM, n0 + wn * TN, wm * TM, lane,
-                                       reinterpret_cast<float*>(ring) + wave * 32 * RSTRIDE, s_tag);
+    resid_epilogue_lds<TM, TN, FM, FN>(p, acc, m0 + wm * TM, n0 + wn * TN, lane,
+                                       reinterpret_cast<float*>(ring) + wave * 32 * RSTRIDE);
   } else if constexpr (EPI == EPI_QKV && SEC == 128) {
     const int sec = (n0 + wn * TN) / SEC;
     if (sec < 3 * p.heads)
       qkv_epilogue_lds<TM, FM, FN>(p, acc, m0 + wm * TM, sec, lane,
                                    reinterpret_cast<float*>(ring) + wave * 32 * QSTRIDE);
   } else {
-    epilogue<BM, BN, WM, WN, EPI, SEC>(p, acc, m0, n0, tc.tn, wm, wn, lane, s_tag);
+    epilogue<BM, BN, WM, WN, EPI, SEC>(p, acc, m0, n0, tc.tn, wm, wn, lane, nullptr);
   }
 }
 
@@ -622,7 +748,7 @@ static hipError_t run_staged(const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
-  if (a.K % 128 != 0) return hipErrorInvalidValue;
+  if (a.K % 64 != 0) return hipErrorInvalidValue;
   if (wfmt == 0) {
     switch (epi) {
       case EPI_RESID: return run_direct<EPI_RESID, 0, 256>(a, s);

@@ -46,6 +46,10 @@ h3_status check_dims(const h3_dims* d) {
     return fail(H3_ERR_UNSUPPORTED, "heads*head_dim=%d must be a multiple of 64",
                 d->heads * d->head_dim);
   if (d->ffn % 128 != 0) return fail(H3_ERR_UNSUPPORTED, "ffn=%d must be a multiple of 128", d->ffn);
+  // the GEMM addresses a weight tile with 32-bit offsets from its first row
+  if ((int64_t)(d->ffn + 256) * d->hidden * 2 >= ((int64_t)1 << 32))
+    return fail(H3_ERR_UNSUPPORTED, "ffn=%d, hidden=%d: (ffn + 256) * hidden * 2 must be below 2^32",
+                d->ffn, d->hidden);
   if (d->n_tags > 8) return fail(H3_ERR_UNSUPPORTED, "n_tags=%d: at most 8", d->n_tags);
   int sum = 0;
   for (int i = 0; i < 3; ++i) {

@@ -56,6 +56,7 @@ def test_padded_rows_and_workspace(L):
     ("hidden", 300, lib.H3_ERR_UNSUPPORTED),
     ("head_dim", 64, lib.H3_ERR_UNSUPPORTED),
     ("ffn", 100, lib.H3_ERR_UNSUPPORTED),
+    ("ffn", 399360, lib.H3_ERR_UNSUPPORTED),   # weight tile offsets past 32 bits
     ("n_tags", 0, lib.H3_ERR_INVALID_ARG),
     ("n_tags", 9, lib.H3_ERR_UNSUPPORTED),
     ("wfmt", 7, lib.H3_ERR_INVALID_ARG),
