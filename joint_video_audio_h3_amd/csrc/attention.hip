@@ -5,59 +5,76 @@
 // packed sequence; "Performance": flash-style, the score matrix is never
 // materialised).
 //
-// Work split: a block of ATT_WAVES wavefronts takes 256 queries of one head;
-// each wavefront owns ATT_QS sub-tiles of 32 queries (sub-tiles of one wave
-// share every K and V fragment it reads from LDS) and walks all keys in tiles
-// of 64, processed as two 32-key halves.  With 8 waves x 32 queries a wave
-// needs ~170 registers, so two waves share each SIMD and one's softmax hides
-// behind the other's matrix work.  K and V^T tiles stream HBM/L2 -> LDS with
-// global_load_lds_dwordx4 into a 3-slot ring (two tiles in flight while one is
-// consumed), XOR-swizzled so the 16-byte fragment reads are bank-conflict free.
+// Work split: a block of 8 wavefronts takes 256 queries of one head; each
+// wavefront owns 32 queries and walks all keys in tiles of 64, processed as
+// two 32-key halves.  A wave needs under 256 registers, so two waves share each
+// SIMD and one's softmax runs beside the other's matrix work (VALU from one
+// wave co-issues with the other's MFMAs).  K and V^T tiles stream HBM/L2 ->
+// LDS with global_load_lds_dwordx4 into a 3-slot ring (two tiles in flight
+// while one is consumed), XOR-swizzled so the 16-byte fragment reads are
+// bank-conflict free.  The key loop is unrolled by the ring period so every
+// slot offset is an immediate: loads take an SGPR tile base plus a fixed
+// per-lane offset, fragment reads a per-lane base plus an immediate.
 //
 // Scores are computed transposed,  S^T[key][query] = K . Q^T  (MFMA A = K
 // rows, B = Q fragment), so every lane holds one query (lane % 32) and 16 of
-// its keys per 32-key sub-tile: the running max and sum need only the two
-// half-waves combined.  K rows are read from LDS in a permuted order chosen so
-// that accumulator register v of lane l holds key 16*(v/8) + 8*(l/32) + v%8;
-// the probabilities then already sit where the PV product wants its B operand:
+// its keys per 32-key half: K rows are read from LDS in a permuted order
+// chosen so that accumulator register v of lane l holds key
+// 16*(v/8) + 8*(l/32) + v%8, and the probabilities then already sit where the
+// PV product wants its B operand:
 //   O^T[dd][query] += V^T[dd][key] . P^T[key][query]
-// with V^T written by the QKV epilogue (keys contiguous).
+// with V^T written by the QKV epilogue (keys contiguous).  Both halves' score
+// products are issued before the first half's softmax, so a wave's own matrix
+// work runs under its exponentials.
 //
 // Softmax: q arrives pre-scaled by log2(e)/sqrt(d), so scores are in log2
 // units and p = exp2(s - m).  The reference point m of each query is folded
-// into the score accumulator's initial value (-m), and it is only raised when
-// a tile's scores exceed it by more than 8 (p <= 2^8, exact in fp32 and bf16
-// relative precision), so rescaling O is rare.  Row sums are fp32 per lane.
+// into the score accumulator's initial value (-m).  No per-tile maximum is
+// taken: p is rounded to bf16 for the PV product and summed from those bf16
+// pairs (v_dot2), and only when some lane's 16 probabilities of a half sum
+// above 2^8 (so that no p can exceed 2^8, or overflow) is the half's maximum
+// formed, m raised, O and the running sum rescaled and p recomputed.  After
+// the first tile this is rare.  The first half always sets m to its maximum.
 // Keys at or beyond n are masked in the last tile; padded rows of q/k/v^T are
 // zeros written by the QKV epilogue, so every operand is finite.
+#include <type_traits>
+
 #include "h3_device.h"
 #include "launch.h"
 
 namespace h3 {
 
 typedef __attribute__((address_space(3))) void* att_lds_t;
+typedef __attribute__((address_space(3))) const bf16x8 att_lds_bf16x8_t;
+typedef __bf16 att_bf16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ void att_dma16(const void* g, void* lds) {
-  const uint32_t la = (uint32_t)(uintptr_t)(att_lds_t)lds;
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(la) : "memory");
+__device__ __forceinline__ uint32_t att_lds_addr(const void* p) { return (uint32_t)(uintptr_t)(att_lds_t)p; }
+__device__ __forceinline__ bf16x8 att_read16(uint32_t a) { return *(att_lds_bf16x8_t*)(size_t)a; }
+// 16 bytes per lane from sbase + voff (sbase wave-uniform) into LDS at lds + 16*lane
+__device__ __forceinline__ void att_dma16s(uint32_t voff, const char* sbase, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void att_wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+template <int V>
+using att_ic = std::integral_constant<int, V>;
 
-constexpr int ATT_WAVES = 8;   // wavefronts per block
-constexpr int ATT_QS = 1;      // 32-query sub-tiles per wavefront
-constexpr int ATT_BQ = ATT_WAVES * 32 * ATT_QS;   // queries per block (256)
-constexpr int ATT_BKV = 64;    // keys per tile
-constexpr float ATT_RESCALE = 8.0f;   // raise m only when scores exceed it by > 2^8
+constexpr int ATT_WAVES = 8;            // wavefronts per block, 32 queries each
+constexpr int ATT_BQ = ATT_WAVES * 32;  // queries per block (256)
+constexpr int ATT_BKV = 64;             // keys per tile
+constexpr int ATT_SLOTS = 3;            // LDS ring depth (tiles)
+constexpr float ATT_RESCALE_SUM = 256.0f;   // a lane's 16 probabilities summing above 2^8
 
 __device__ __forceinline__ int att_sigma(int i) {   // MFMA row -> key within 32
   const int g = i >> 3, h = (i >> 2) & 1, c = i & 3;
   return 16 * (g >> 1) + 8 * h + 4 * (g & 1) + c;
 }
+// K rows hold 16 chunks of 16 B; V^T rows 8 chunks.  Both swizzles depend only
+// on the row modulo 32, so one per-lane base serves every 32-row tile.
 __device__ __forceinline__ int att_kswz(int r) { return (r ^ (((r >> 3) & 1) << 2)) & 15; }
-__device__ __forceinline__ int att_vswz(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int att_vswz(int r) { return ((r & 31) ^ ((r & 31) >> 3)) & 7; }
 
 template <int HD>
 __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs p) {
@@ -69,194 +86,230 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs p) {
   constexpr int VBYTES = HD * VROW;
   constexpr int STAGE = KBYTES + VBYTES;
   constexpr int NK = KBYTES / 1024, NV = VBYTES / 1024;   // 1 KB DMA loads per tile
-  constexpr int W = ATT_WAVES, QS = ATT_QS;
+  constexpr int W = ATT_WAVES;
   constexpr int NI = (NK + NV + W - 1) / W;               // per wavefront (last may idle)
-  constexpr int NIK = NK / W;                             // first NIK slots load K
+  constexpr int NIK = NK / W;                             // first NIK loads are K
   static_assert(NK % W == 0, "K loads must split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) char ring[3 * STAGE];
+  static_assert(ATT_SLOTS * STAGE < 2 * 65536, "two 64 KB read windows");
+  __shared__ __attribute__((aligned(1024))) char ring[ATT_SLOTS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.y;
-  const int q0 = blockIdx.x * ATT_BQ + wave * 32 * QS;
+  const int q0 = blockIdx.x * ATT_BQ + wave * 32;
   const int hl = lane >> 5, lq = lane & 31;
   const size_t hoff = (size_t)head * p.n_pad * HD;
 
-  // Q fragments (B operand): query q0 + 32*qs + lq, channels 16*ds + 8*hl .. +7
-  bf16x8 qf[QS][DS];
+  // Q fragments (B operand): query q0 + lq, channels 16*ds + 8*hl .. +7
+  bf16x8 qf[DS];
+  {
+    const uint16_t* qp = p.q + hoff + (size_t)(q0 + lq) * HD + 8 * hl;
 #pragma unroll
-  for (int qs = 0; qs < QS; ++qs) {
-    const uint16_t* qp = p.q + hoff + (size_t)(q0 + qs * 32 + lq) * HD + 8 * hl;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) qf[qs][ds] = *reinterpret_cast<const bf16x8*>(qp + ds * 16);
+    for (int ds = 0; ds < DS; ++ds) qf[ds] = *reinterpret_cast<const bf16x8*>(qp + ds * 16);
   }
   // Land the Q loads now (vmcnt(0) via the builtin, which the compiler's wait
   // bookkeeping understands): otherwise it keeps them "pending" into the key
   // loop and its vmcnt waits there would also wait for the K/V tiles in flight.
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
 
-  // DMA sources: K slots fill 4 rows of 256 B per load (lane -> row l/16,
-  // position l%16 holding chunk (l%16)^kswz(row)); V^T slots fill 8 rows of
-  // 128 B (lane -> row l/8, position l%8 holding chunk (l%8)^vswz(row)).
-  const uint16_t* src[NI];
-  int ldso[NI];
+  // DMA: K loads fill 4 rows of 256 B (lane -> row l/16, position l%16 holding
+  // chunk (l%16)^kswz(row)); V^T loads fill 8 rows of 128 B (lane -> row l/8,
+  // position l%8 holding chunk (l%8)^vswz(row)).  Offsets are relative to the
+  // tile's first K row / first V^T column.
+  const char* kbase0 = reinterpret_cast<const char*>(p.k + hoff);
+  const char* vbase0 = reinterpret_cast<const char*>(p.vt + (size_t)head * HD * p.n_pad);
+  const uint32_t ring0 = att_lds_addr(ring);
+  uint32_t dvo[NI], dm[NI];
 #pragma unroll
   for (int s = 0; s < NI; ++s) {
-    const int j = min(wave + W * s, NK + NV - 1);   // idle slots repeat a valid load
+    const int j = min(wave + W * s, NK + NV - 1);
     if (s < NIK) {
       const int r = 4 * j + lane / 16;
       const int ch = min((lane & 15) ^ att_kswz(r), HD / 8 - 1);
-      src[s] = p.k + hoff + (size_t)r * HD + ch * 8;
-      ldso[s] = j * 1024;
+      dvo[s] = (uint32_t)(r * HD + ch * 8) * 2;
+      dm[s] = __builtin_amdgcn_readfirstlane(ring0 + j * 1024);
     } else {
       const int jv = j - NK;
       const int r = 8 * jv + lane / 8;
       const int ch = (lane & 7) ^ att_vswz(r);
-      src[s] = p.vt + (size_t)head * HD * p.n_pad + (size_t)r * p.n_pad + ch * 8;
-      ldso[s] = KBYTES + jv * 1024;
+      dvo[s] = (uint32_t)r * (uint32_t)p.n_pad * 2 + (uint32_t)ch * 16;
+      dm[s] = __builtin_amdgcn_readfirstlane(ring0 + KBYTES + jv * 1024);
     }
   }
-  auto issue = [&](int kt, char* buf) __attribute__((always_inline)) {
+  const bool has_last = wave + W * (NI - 1) < NK + NV;   // wave-uniform: the last load exists
+  auto issue = [&](int kt, uint32_t slot_off) __attribute__((always_inline)) {
+    const char* kb = kbase0 + (size_t)kt * (ATT_BKV * HD * 2);
+    const char* vb = vbase0 + (size_t)kt * (ATT_BKV * 2);
 #pragma unroll
     for (int s = 0; s < NI; ++s) {
-      if (wave + W * s >= NK + NV) break;   // wave-uniform: this slot has no load
-      const size_t step = s < NIK ? (size_t)ATT_BKV * HD : (size_t)ATT_BKV;
-      att_dma16(src[s] + kt * step, buf + ldso[s]);
+      if (s == NI - 1 && !has_last) break;
+      att_dma16s(dvo[s], s < NIK ? kb : vb, dm[s] + slot_off);
     }
   };
 
-  // fragment read offsets
+  // fragment read bases for two 64 KB windows of the ring
   const int krow = att_sigma(lq);
-  const int koff = krow * KROW;
-  const int kg = att_kswz(krow);
-  int voff[DT];
+  const int kg = att_kswz(krow), vg = att_vswz(lq);
+  uint32_t kbr[2][DS], vbr[2][4];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) voff[t] = KBYTES + (t * 32 + lq) * VROW;
-  int vg[DT];
+  for (int w = 0; w < 2; ++w) {
 #pragma unroll
-  for (int t = 0; t < DT; ++t) vg[t] = att_vswz(t * 32 + lq);
-
-  f32x16 oacc[DT][QS];
-  float m_ref[QS], l_run[QS];
+    for (int ds = 0; ds < DS; ++ds) kbr[w][ds] = ring0 + w * 65536 + krow * KROW + (((2 * ds + hl) ^ kg) * 16);
 #pragma unroll
-  for (int qs = 0; qs < QS; ++qs) {
-#pragma unroll
-    for (int t = 0; t < DT; ++t) oacc[t][qs] = f32x16{};
-    m_ref[qs] = l_run[qs] = 0.f;
+    for (int s = 0; s < 4; ++s) vbr[w][s] = ring0 + w * 65536 + lq * VROW + (((2 * s + hl) ^ vg) * 16);
   }
+  // K fragment ds of half ks, V^T fragment (t, s) of the tile in the slot at
+  // byte offset SO (compile-time, so the offset is an immediate)
+  auto kread = [&](auto SO_, int ks, int ds) __attribute__((always_inline)) {
+    constexpr int SO = decltype(SO_)::value;
+    const int off = SO + ks * 32 * KROW;
+    const int w = off >> 16;
+    return att_read16(kbr[w][ds] + (off - (w << 16)));
+  };
+  auto vread = [&](auto SO_, int t, int s) __attribute__((always_inline)) {
+    constexpr int SO = decltype(SO_)::value;
+    const int off = SO + KBYTES + t * 32 * VROW;
+    const int w = off >> 16;
+    return att_read16(vbr[w][s] + (off - (w << 16)));
+  };
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
+  float m_ref = 0.f, l_run = 0.f;
+  const att_bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   const int KT = (p.n + ATT_BKV - 1) / ATT_BKV;
 
-  // one 32-key half of a tile: scores, softmax bookkeeping, PV accumulation
-  auto half_tile = [&](int kt, int ks, const char* buf) __attribute__((always_inline)) {
-    const bool first = kt == 0 && ks == 0;
-    // ---- S^T = K Q^T - m   (both query sub-tiles share each K fragment)
-    f32x16 sacc[QS];
+  // S^T = K Q^T - m for one half (K fragments from `kr`)
+  auto scores = [&](auto&& kr, int ks) __attribute__((always_inline)) {
+    f32x16 s;
 #pragma unroll
-    for (int qs = 0; qs < QS; ++qs) {
-      const float init = first ? 0.f : -m_ref[qs];
+    for (int v = 0; v < 16; ++v) s[v] = -m_ref;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[qs][v] = init;
-    }
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-          buf + ks * 32 * KROW + koff + (((2 * ds + hl) ^ kg) * 16));
-#pragma unroll
-      for (int qs = 0; qs < QS; ++qs) sacc[qs] = mfma32(a, qf[qs][ds], sacc[qs]);
-    }
-    const int key0 = kt * ATT_BKV + ks * 32;
-    if (key0 + 32 > p.n) {   // only the last keys can be padding: mask keys >= n
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = key0 + 16 * (v / 8) + 8 * hl + (v % 8);
-        if (key >= p.n) {
-#pragma unroll
-          for (int qs = 0; qs < QS; ++qs) sacc[qs][v] = -INFINITY;
-        }
-      }
-    }
-    // ---- softmax bookkeeping per query sub-tile
-    bf16x8 pf[QS][2];
-#pragma unroll
-    for (int qs = 0; qs < QS; ++qs) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(sacc[qs][v], sacc[qs][v + 1]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (first) {
-        m_ref[qs] = mx;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sacc[qs][v] -= mx;
-      } else if (__builtin_amdgcn_ballot_w64(mx > ATT_RESCALE) != 0) {
-        const float sh = fmaxf(mx, 0.f);
-        const float alpha = __builtin_amdgcn_exp2f(-sh);
-        m_ref[qs] += sh;
-        l_run[qs] *= alpha;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sacc[qs][v] -= sh;
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) oacc[t][qs][v] *= alpha;
-      }
-      float rs = 0.f;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float e = __builtin_amdgcn_exp2f(sacc[qs][v]);
-        rs += e;
-        pf[qs][v / 8][v % 8] = (__bf16)e;
-      }
-      l_run[qs] += rs;
-    }
-    // ---- O^T += V^T P^T   (both query sub-tiles share each V fragment)
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int s = 2 * ks + s2;   // 16-key step within the 64-key V^T row
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(buf + voff[t] + (((2 * s + hl) ^ vg[t]) * 16));
-#pragma unroll
-        for (int qs = 0; qs < QS; ++qs) oacc[t][qs] = mfma32(a, pf[qs][s2], oacc[t][qs]);
-      }
-    }
+    for (int ds = 0; ds < DS; ++ds) s = mfma32(kr(ks, ds), qf[ds], s);
+    return s;
   };
-  auto tile = [&](int kt, const char* buf) __attribute__((always_inline)) {
-    half_tile(kt, 0, buf);
-    half_tile(kt, 1, buf);
+  // p = exp2(s) as bf16 pairs and their sum
+  auto probs = [&](const f32x16& s, bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      const att_bf16x2 pr = {(__bf16)__builtin_amdgcn_exp2f(s[v]), (__bf16)__builtin_amdgcn_exp2f(s[v + 1])};
+      pf[v / 8][v % 8] = pr[0];
+      pf[v / 8][v % 8 + 1] = pr[1];
+      if ((v / 2) & 1) {
+        rs1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs1, false);
+      } else {
+        rs0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs0, false);
+      }
+    }
+    return rs0 + rs1;
+  };
+  // softmax of one half: probabilities into pf, running sum updated; the rare
+  // rescale also shifts `other`, the other half's scores already formed with
+  // the old reference point
+  auto softmax = [&](f32x16& s, f32x16& other, bool first, bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+    float rs = probs(s, pf);
+    if (first || __builtin_amdgcn_ballot_w64(!(rs <= ATT_RESCALE_SUM)) != 0) {
+      float mx = s[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float sh = first ? mx : fmaxf(mx, 0.f);
+      const float alpha = __builtin_amdgcn_exp2f(-sh);
+      m_ref += sh;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        s[v] -= sh;
+        other[v] -= sh;
+      }
+      rs = probs(s, pf);
+    }
+    l_run += rs;
+  };
+  // O^T += V^T P^T for half ks (V fragments from `vr`)
+  auto pv = [&](auto&& vr, int ks, const bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) oacc[t] = mfma32(vr(t, 2 * ks + s2), pf[s2], oacc[t]);
+  };
+  auto mask = [&](f32x16& s, int key0) __attribute__((always_inline)) {
+    if (key0 + 32 > p.n) {   // only the last tile can hold keys >= n
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (key0 + 16 * (v / 8) + 8 * hl + (v % 8) >= p.n) s[v] = -INFINITY;
+    }
   };
 
-  // ring: wait for this wave's loads of tile kt (one later tile may stay in
-  // flight), barrier, refill the slot freed by tile kt-1 with tile kt+2, consume kt
-  issue(0, ring);
-  if (KT > 1) issue(1, ring + STAGE);
-  for (int kt = 0; kt < KT; ++kt) {
+  // one tile: both halves' scores, then each half's softmax and PV product
+  auto tile_body = [&](auto&& kr, auto&& vr, int kt, bool masked) __attribute__((always_inline)) {
+    f32x16 s0 = scores(kr, 0);
+    f32x16 s1 = scores(kr, 1);
+    if (masked) {
+      mask(s0, kt * ATT_BKV);
+      mask(s1, kt * ATT_BKV + 32);
+    }
+    bf16x8 pf[2];
+    softmax(s0, s1, kt == 0, pf);
+    pv(vr, 0, pf);
+    softmax(s1, s0, false, pf);
+    pv(vr, 1, pf);
+  };
+
+  // steady tile with compile-time slot U: wait for tile kt, barrier, refill the
+  // slot freed by tile kt-1 with tile kt+2, consume tile kt
+  auto tile_c = [&](auto U_, int kt) __attribute__((always_inline)) {
+    constexpr int U = decltype(U_)::value;
+    constexpr int SO = U * STAGE;
+    att_wait_vmcnt<NI>();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + 2, (uint32_t)(((U + 2) % ATT_SLOTS) * STAGE));
+    tile_body([&](int ks, int ds) __attribute__((always_inline)) { return kread(att_ic<SO>{}, ks, ds); },
+              [&](int t, int s) __attribute__((always_inline)) { return vread(att_ic<SO>{}, t, s); }, kt, false);
+  };
+  // the same with the slot from the runtime phase (the last few tiles)
+  auto tile_r = [&](int kt) __attribute__((always_inline)) {
+    const uint32_t so = (uint32_t)((kt % ATT_SLOTS) * STAGE);
     if (kt + 1 < KT) {
       att_wait_vmcnt<NI>();
     } else {
       att_wait_vmcnt<0>();
     }
     __builtin_amdgcn_s_barrier();
-    if (kt + 2 < KT) issue(kt + 2, ring + ((kt + 2) % 3) * STAGE);
-    tile(kt, ring + (kt % 3) * STAGE);
-  }
+    if (kt + 2 < KT) issue(kt + 2, (uint32_t)(((kt + 2) % ATT_SLOTS) * STAGE));
+    tile_body([&](int ks, int ds) __attribute__((always_inline)) { return att_read16(kbr[0][ds] + so + ks * 32 * KROW); },
+              [&](int t, int s) __attribute__((always_inline)) { return att_read16(vbr[0][s] + so + KBYTES + t * 32 * VROW); },
+              kt, kt + 1 == KT);
+  };
 
+  issue(0, 0);
+  if (KT > 1) issue(1, STAGE);
+  int kt = 0;
+  for (; kt + 5 <= KT; kt += 3) {
+    tile_c(att_ic<0>{}, kt);
+    tile_c(att_ic<1>{}, kt + 1);
+    tile_c(att_ic<2>{}, kt + 2);
+  }
+  for (; kt < KT; ++kt) tile_r(kt);
+
+  const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32, 64));
+  const int qrow = q0 + lq;
+  if (qrow < p.n) {
+    uint16_t* op = p.o + (size_t)qrow * p.heads * HD + head * HD;
 #pragma unroll
-  for (int qs = 0; qs < QS; ++qs) {
-    const float inv = 1.0f / (l_run[qs] + __shfl_xor(l_run[qs], 32, 64));
-    const int qrow = q0 + qs * 32 + lq;
-    if (qrow < p.n) {
-      uint16_t* op = p.o + (size_t)qrow * p.heads * HD + head * HD;
+    for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int dd = t * 32 + 8 * g + 4 * hl;
-          const f32x16& a = oacc[t][qs];
-          const uint2 w = make_uint2(pack2bf(a[4 * g] * inv, a[4 * g + 1] * inv),
-                                     pack2bf(a[4 * g + 2] * inv, a[4 * g + 3] * inv));
-          *reinterpret_cast<uint2*>(op + dd) = w;
-        }
-    }
+      for (int g = 0; g < 4; ++g) {
+        const int dd = t * 32 + 8 * g + 4 * hl;
+        const f32x16& a = oacc[t];
+        const uint2 w = make_uint2(pack2bf(a[4 * g] * inv, a[4 * g + 1] * inv),
+                                   pack2bf(a[4 * g + 2] * inv, a[4 * g + 3] * inv));
+        *reinterpret_cast<uint2*>(op + dd) = w;
+      }
   }
 }
 
