@@ -222,7 +222,8 @@ constexpr int RSTRIDE = 136;   // floats per staged row (128 + 8 of padding)
 
 template <int TM, int TN, int FM, int FN>
 __device__ __forceinline__ void resid_epilogue_lds(const GemmArgs& p, f32x16 (&acc)[FM][FN],
-                                                   int row0, int col0, int lane, float* stage) {
+                                                   int row0, int col0, int lane, float* stage,
+                                                   const int* s_tag) {
   static_assert(TN == 128, "one float4 per lane covers a 128-wide row");
   const int hl = lane >> 5, lc = lane & 31;
   const int gcol = col0 + 4 * lc;
@@ -232,6 +233,9 @@ __device__ __forceinline__ void resid_epilogue_lds(const GemmArgs& p, f32x16 (&a
     const u16x4 bb = *reinterpret_cast<const u16x4*>(p.bias + gcol);
     b4 = make_float4(bf2f(bb[0]), bf2f(bb[1]), bf2f(bb[2]), bf2f(bb[3]));
   }
+  // 32 rows at a time: stage the accumulators, then issue every gate and x load
+  // of the 32 rows before the first store, so the chunk waits for memory once
+  // rather than once per row (the stores could alias the loads otherwise)
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -239,21 +243,31 @@ __device__ __forceinline__ void resid_epilogue_lds(const GemmArgs& p, f32x16 (&a
 #pragma unroll
       for (int v = 0; v < 16; ++v)
         stage[(8 * (v / 4) + 4 * hl + (v % 4)) * RSTRIDE + j * 32 + lc] = acc[i][j][v];
-#pragma unroll 4
+    float4 xv[16];
+    u16x4 gv[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int r = 2 * it + hl;
+      const int row = row0 + i * 32 + r;
+      if (row < p.M && col_ok) {
+        const int t = s_tag[i * 32 + r];
+        gv[it] = *reinterpret_cast<const u16x4*>(p.gate_tab + (size_t)t * p.tag_stride + gcol);
+        xv[it] = *reinterpret_cast<const float4*>(p.x + (size_t)row * p.ldx + gcol);
+      }
+    }
+#pragma unroll
     for (int it = 0; it < 16; ++it) {
       const int r = 2 * it + hl;
       const int row = row0 + i * 32 + r;
       const float4 a = *reinterpret_cast<const float4*>(stage + r * RSTRIDE + 4 * lc);
       if (row < p.M && col_ok) {
-        const int t = p.tag[row];
-        const u16x4 g = *reinterpret_cast<const u16x4*>(p.gate_tab + (size_t)t * p.tag_stride + gcol);
-        float4* xp = reinterpret_cast<float4*>(p.x + (size_t)row * p.ldx + gcol);
-        float4 x = *xp;
+        float4 x = xv[it];
+        const u16x4 g = gv[it];
         x.x += bf2f(g[0]) * (a.x + b4.x);
         x.y += bf2f(g[1]) * (a.y + b4.y);
         x.z += bf2f(g[2]) * (a.z + b4.z);
         x.w += bf2f(g[3]) * (a.w + b4.w);
-        *xp = x;
+        *reinterpret_cast<float4*>(p.x + (size_t)row * p.ldx + gcol) = x;
       }
     }
   }
@@ -600,8 +614,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (; kt < KT; ++kt) step_rt(kt);
   __syncthreads();
   if constexpr (EPI == EPI_RESID) {
+    // the tile's row tags go to LDS past the four staging areas (the ring is free now)
+    int* s_tag = reinterpret_cast<int*>(ring + 4 * 32 * RSTRIDE * sizeof(float));
+    s_tag[tid] = p.tag[min(m0 + tid, p.M - 1)];
+    __syncthreads();
     resid_epilogue_lds<TM, TN, FM, FN>(p, acc, m0 + wm * TM, n0 + wn * TN, lane,
-                                       reinterpret_cast<float*>(ring) + wave * 32 * RSTRIDE);
+                                       reinterpret_cast<float*>(ring) + wave * 32 * RSTRIDE, s_tag + wm * TM);
   } else if constexpr (EPI == EPI_QKV && SEC == 128) {
     const int sec = (n0 + wn * TN) / SEC;
     if (sec < 3 * p.heads)
