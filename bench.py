@@ -165,6 +165,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --only-step: first run a 1 GiB device-to-device copy three times, "
                          "the known-size reference for HBM byte counters")
+    ap.add_argument("--single-block", type=int, default=1,
+                    help="also time one H3 block at N=1192 with bf16 and INT8 weights (0: skip)")
     ap.add_argument("--only-step", default=None,
                     help="time just one step kernel (adaln, qkv_rope, attention, out_proj_resid, "
                          "fc1_swiglu, fc2_resid) on one block's weights, e.g. under a counter run")
@@ -248,6 +250,18 @@ def main():
             "forward_mfma_frac": round(wl2.n_blocks * w2.total_flop / sec2 / 1e12 / PEAK, 4),
             "per_step_kernels": bd2,
         }
+    if args.single_block:
+        # one H3 block at N=1192, bf16 and INT8 W8A16 weights: per-step kernel
+        # times (the block-parity shape; the INT8 variant's MFMA utilization)
+        result["single_block"] = {}
+        for name in ("h3_1blk_n1192", "h3_1blk_n1192_int8"):
+            wl1 = synth.WORKLOADS[name]
+            t1, b1 = synth.make_device_weights(wl1.dims, 1, seed=0)
+            bd1, _ = step_breakdown(lib, wl1.dims, synth.make_device_rows(wl1, seed=1), t1, b1[0],
+                                    args.breakdown_reps, torch)
+            result["single_block"][name] = {"weights": "int8 g32 + bf16 scales" if wl1.dims.wfmt else "bf16",
+                                            "per_step_kernels": bd1}
+            del t1, b1
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(n, wl.n_blocks, dims)
