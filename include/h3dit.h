@@ -38,7 +38,7 @@
  * Supported shapes: hidden % 256 == 0 and hidden <= 8192; head_dim in
  * {96, 128}; ffn % 128 == 0 and (ffn + 256) * hidden * 2 < 2^32; rope_split
  * entries even and summing to head_dim; 1 <= n_tags <= 8;
- * 1 <= n_rows <= 2^24.
+ * 1 <= n_rows <= 2^24; with INT8 weights also heads * head_dim % 128 == 0.
  */
 #ifndef H3DIT_H
 #define H3DIT_H

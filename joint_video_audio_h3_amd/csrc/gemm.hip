@@ -25,10 +25,10 @@
 // reads of the next 16-wide k step are scheduled behind the current step's
 // first MFMA.
 //
-// INT8 weights (gemm_staged_kernel): same MFMA tiling with eight wavefronts;
-// 16-byte chunks of int8 codes go through registers, where they are
-// dequantised to bf16(q * s) (one bf16 scale per 32 K elements) on their way
-// into a double-buffered LDS ring, so the MFMA loop is unchanged.
+// INT8 weights (gemm_w8_kernel): eight wavefronts of 64 x 128 tiles; A streams
+// in by DMA, int8 codes go through registers, where they are dequantised to
+// bf16(q * s) (one bf16 scale per 32 K elements) on their way into a
+// double-buffered LDS stage, interleaved with the MFMAs of the stage before.
 //
 // Block ids are remapped so that each XCD (blocks are dealt round-robin to the
 // 8 XCDs) walks a contiguous run of a grouped tile order in which consecutive
@@ -630,21 +630,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
-// ============================================================ INT8: staged dequant
-constexpr int SBK = 64;
-constexpr int SLDK = SBK + 8;   // padded LDS row (bf16): 144 B
-
+// ============================================================ INT8: dequant into LDS
+// Weights are int8 codes q with one bf16 scale s per 32 K elements; the MFMA
+// operand is W = bf16(q*s) (q*s is exact in fp32, rounded to nearest even).
+// Eight wavefronts, 4 x 2 of 64 x 128 (x 96) tiles, two waves per SIMD, and a
+// two-buffer LDS pipeline with BK = 64 stages.  While stage kt is consumed:
+// A of stage kt+1 streams in by DMA (as in the bf16 kernel), the int8 codes of
+// stage kt+1 (loaded one stage earlier) are dequantised and written to LDS,
+// interleaved with the MFMAs, and then the codes of stage kt+2 are loaded into
+// the same registers.  Each code is turned into bf16(q*s) with one byte-to-float conversion
+// of q + 128 and one exact FMA, (q + 128)*s - 128*s, then rounded.  A full
+// wait the compiler can see ends every stage, so its own wait insertion never
+// counts the DMA loads it cannot see.
 template <int EPI, int SEC, int BN>
-__global__ __launch_bounds__(512) void gemm_staged_kernel(GemmArgs p) {
+__global__ __launch_bounds__(512) void gemm_w8_kernel(GemmArgs p) {
   constexpr int BM = 256, WM = 4, WN = 2, NT = 512;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int A_CH = BM * 8 / NT;           // 16-byte bf16 chunks per thread
-  constexpr int B_CH = (BN * 4 + NT - 1) / NT; // 16-byte int8 chunks per thread (last round partial)
-  static_assert(A_CH * NT == BM * 8, "tile/thread mismatch");
+  constexpr int NA = BM / 8 / 8;                 // 1 KB (8-row) A loads per wave per stage
+  constexpr int NBC = (BN * 4 + NT - 1) / NT;    // 16-code chunks per thread per stage
+  constexpr int ABUF = 32768, BOFF = 65536;      // A of buffer b at b*ABUF, B at BOFF + b*ABUF
   static_assert(EPI != EPI_QKV || TN == SEC, "QKV wave tile must be one head section");
+  static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU needs paired gate/value tiles");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * SLDK];
+  __shared__ __attribute__((aligned(1024))) char sm[4 * ABUF];
   __shared__ int s_tag[EPI == EPI_RESID ? BM : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -655,60 +664,98 @@ __global__ __launch_bounds__(512) void gemm_staged_kernel(GemmArgs p) {
     for (int i = tid; i < BM; i += NT) s_tag[i] = p.tag[min(m0 + i, p.M - 1)];
   }
   const int K = p.K;
-  const uint16_t* a_src[A_CH];
+  const uint32_t rowb = (uint32_t)K * 2;
+  const uint32_t sm0 = lds_addr(sm);
+
+  // A by DMA: load s covers rows 8*(wave + 8s) .. +7; lane l fills row
+  // 8*(wave + 8s) + l/8, position l%8 holding global chunk (l%8) ^ f(row)
+  const char* baseA = reinterpret_cast<const char*>(p.A) + (size_t)m0 * rowb;
+  uint32_t voA[NA];
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + i * NT;
-    a_src[i] = p.A + (size_t)min(m0 + c / 8, p.M - 1) * K + (c % 8) * 8;
+  for (int s = 0; s < NA; ++s) {
+    const int r = 8 * (wave + 8 * s) + lane / 8;
+    voA[s] = (uint32_t)(min(m0 + r, p.M - 1) - m0) * rowb + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
   }
-  const int8_t* b_src[B_CH];
-  const uint16_t* s_src[B_CH];
+  const uint32_t mw = __builtin_amdgcn_readfirstlane(sm0 + wave * 1024);
+  auto dmaA = [&](int ks, uint32_t boff) __attribute__((always_inline)) {
+    const char* sb = baseA + (size_t)ks * (DBK * 2);
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = min(tid + i * NT, BN * 4 - 1);
-    const int brow = weight_row<EPI, BN, TN>(p, tc.tn, c / 4);
-    b_src[i] = reinterpret_cast<const int8_t*>(p.B) + (size_t)brow * K + (c % 4) * 16;
-    s_src[i] = p.Bs + (size_t)brow * (K / 32) + (c % 4) / 2;
-  }
-  uint4 ra[A_CH], rb[B_CH];
-  uint16_t rs[B_CH];
-  auto gload = [&](int kt) {
-    const int k0 = kt * SBK;
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + k0);
-      rs[i] = s_src[i][k0 / 32];
-    }
+    for (int s = 0; s < NA; ++s) dma16s(voA[s], sb, mw + boff + s * 8192);
   };
-  auto sstore = [&](int buf) {
-    uint16_t* As = smem + buf * (BM + BN) * SLDK;
-    uint16_t* Bsm = As + BM * SLDK;
+
+  // B: chunk i of thread t is row r = t/4 + 128*i, codes k = 16*(t%4) .. +15 of
+  // the stage, i.e. bf16 chunks 2c and 2c+1 (c = t%4) of that LDS row
+  // wave-uniform bases of the tile's weight rows and scale rows (SGPRs), per-lane
+  // 32-bit offsets
+  const int b0 = weight_row_base<EPI, BN>(tc.tn);
+  const int8_t* bbase = reinterpret_cast<const int8_t*>(p.B) + (size_t)b0 * K;
+  const uint16_t* sbase = p.Bs + (size_t)b0 * (K / 32);
+  uint32_t boffs[NBC], soffs[NBC], bdst0[NBC], bdst1[NBC];
+  bool bval[NBC];
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int c = tid + i * NT;
-      *reinterpret_cast<uint4*>(As + (c / 8) * SLDK + (c % 8) * 8) = ra[i];
-    }
+  for (int i = 0; i < NBC; ++i) {
+    const int r = tid / 4 + (NT / 4) * i, c = tid & 3;
+    bval[i] = r < BN;
+    const int rr = min(r, BN - 1);
+    const uint32_t brow = (uint32_t)(weight_row<EPI, BN, TN>(p, tc.tn, rr) - b0);
+    boffs[i] = brow * (uint32_t)K + 16 * c;
+    soffs[i] = brow * (uint32_t)(K / 32) + c / 2;
+    bdst0[i] = sm0 + BOFF + rr * DROW + (((2 * c) ^ swz(rr)) * 16);
+    bdst1[i] = sm0 + BOFF + rr * DROW + (((2 * c + 1) ^ swz(rr)) * 16);
+  }
+  // one register set: a stage's codes are dequantised before the next stage's
+  // codes are loaded into the same registers
+  uint4 qv[NBC];
+  uint16_t sv[NBC];
+  auto ldB = [&](int ks) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int c = tid + i * NT;
-      if (c >= BN * 4) break;
-      const float sc = bf2f(rs[i]);
-      const uint32_t w4[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
-      uint32_t o[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t word = w4[e / 2];
-        const int sh = (e % 2) * 16;
-        const float lo = (float)(int8_t)((word >> sh) & 0xff) * sc;
-        const float hi = (float)(int8_t)((word >> (sh + 8)) & 0xff) * sc;
-        o[e] = pack2bf(lo, hi);
+    for (int i = 0; i < NBC; ++i)
+      if (bval[i]) {
+        qv[i] = *reinterpret_cast<const uint4*>(bbase + boffs[i] + (size_t)ks * DBK);
+        sv[i] = sbase[soffs[i] + ks * 2];
       }
-      uint16_t* dst = Bsm + (c / 4) * SLDK + (c % 4) * 16;
-      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<uint4*>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+  };
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) u32x4_t lds_u4_t;
+  auto deqB = [&](uint32_t boff) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NBC; ++i)
+      if (bval[i]) {
+        const float sc = bf2f(sv[i]), msc = -128.0f * sc;
+        const uint32_t w4[4] = {qv[i].x ^ 0x80808080u, qv[i].y ^ 0x80808080u,
+                                qv[i].z ^ 0x80808080u, qv[i].w ^ 0x80808080u};
+        uint32_t o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t word = w4[e / 2];
+          const int sh = (e % 2) * 16;
+          const float lo = __builtin_fmaf((float)((word >> sh) & 0xffu), sc, msc);
+          const float hi = __builtin_fmaf((float)((word >> (sh + 8)) & 0xffu), sc, msc);
+          o[e] = pack2bf(lo, hi);
+        }
+        *(lds_u4_t*)(size_t)(bdst0[i] + boff) = u32x4_t{o[0], o[1], o[2], o[3]};
+        *(lds_u4_t*)(size_t)(bdst1[i] + boff) = u32x4_t{o[4], o[5], o[6], o[7]};
+      }
+  };
+
+  // fragment reads: row lane%32 of each 32-row tile, chunk 2*kk + lane/32;
+  // A of buffer b at b*ABUF, B at BOFF + b*ABUF (one base each, immediates)
+  const int fr = lane & 31, hl = lane >> 5;
+  uint32_t rA[2][4], rB[2][4];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      rA[par][kk] = sm0 + wm * TM * DROW + fr * DROW + (((2 * kk + hl) ^ swz(fr + 32 * par)) * 16);
+      const int pb = ((wn * TN) / 32 + par) & 1;
+      rB[par][kk] = sm0 + BOFF + wn * TN * DROW + fr * DROW + (((2 * kk + hl) ^ swz(fr + 32 * pb)) * 16);
     }
+  auto read_frags = [&](auto B_, int kk, bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) __attribute__((always_inline)) {
+    constexpr int b = decltype(B_)::value;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[i] = lds_read16(rA[i & 1][kk] + b * ABUF + i * 32 * DROW);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[j] = lds_read16(rB[j & 1][kk] + b * ABUF + j * 32 * DROW);
   };
 
   f32x16 acc[FM][FN];
@@ -716,32 +763,51 @@ __global__ __launch_bounds__(512) void gemm_staged_kernel(GemmArgs p) {
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+  auto mfmas = [&](const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+  };
+  // a full wait the compiler's own bookkeeping sees (it also covers the DMA)
+  auto wait_all = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0 << 8)); };
 
-  const int KT = K / SBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  const int lrow = lane & 31, lk = (lane >> 5) * 8;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const uint16_t* As = smem + cur * (BM + BN) * SLDK + (wm * TM + lrow) * SLDK + lk;
-    const uint16_t* Bsm = smem + cur * (BM + BN) * SLDK + BM * SLDK + (wn * TN + lrow) * SLDK + lk;
-#pragma unroll
-    for (int kk = 0; kk < SBK / 16; ++kk) {
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * SLDK + kk * 16);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(Bsm + j * 32 * SLDK + kk * 16);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
-    }
-    if (kt + 1 < KT) sstore(cur ^ 1);
-    __syncthreads();
+  const int KT = K / DBK;
+  bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  // stage kt in buffer b = kt & 1.  The loads of stages kt+1 and kt+2 are
+  // clamped to the last stage: past the end they refill the idle buffer with
+  // valid data that is never read, so every stage has the same shape.
+  auto stage = [&](auto B_, int kt) __attribute__((always_inline)) {
+    constexpr int b = decltype(B_)::value, nb = b ^ 1;
+    dmaA(min(kt + 1, KT - 1), nb * ABUF);
+    read_frags(B_, 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    deqB(nb * ABUF);
+    ldB(min(kt + 2, KT - 1));
+    read_frags(B_, 2, fa0, fb0);
+    mfmas(fa1, fb1);
+    read_frags(B_, 3, fa1, fb1);
+    mfmas(fa0, fb0);
+    wait_all();
+    __builtin_amdgcn_s_barrier();
+    // past the last stage the reads hit the other buffer and go unused
+    read_frags(ic<nb>{}, 0, fa0, fb0);
+    mfmas(fa1, fb1);
+  };
+
+  ldB(0);
+  dmaA(0, 0);
+  wait_all();
+  deqB(0);
+  ldB(min(1, KT - 1));
+  wait_all();
+  __builtin_amdgcn_s_barrier();
+  read_frags(ic<0>{}, 0, fa0, fb0);
+  for (int kt = 0; kt < KT; kt += 2) {   // KT is even (K % 128 == 0, checked at launch)
+    stage(ic<0>{}, kt);
+    stage(ic<1>{}, kt + 1);
   }
+  __syncthreads();
   epilogue<BM, BN, WM, WN, EPI, SEC>(p, acc, m0, n0, tc.tn, wm, wn, lane, s_tag);
 }
 
@@ -760,13 +826,14 @@ static hipError_t run_direct(const GemmArgs& a, hipStream_t s) {
 }
 
 template <int EPI, int SEC, int BN>
-static hipError_t run_staged(const GemmArgs& a, hipStream_t s) {
-  gemm_staged_kernel<EPI, SEC, BN><<<grid_for<256, BN>(EPI, a), 512, 0, s>>>(a);
+static hipError_t run_w8(const GemmArgs& a, hipStream_t s) {
+  gemm_w8_kernel<EPI, SEC, BN><<<grid_for<256, BN>(EPI, a), 512, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
   if (a.K % 64 != 0) return hipErrorInvalidValue;
+  if (wfmt != 0 && a.K % 128 != 0) return hipErrorInvalidValue;   // INT8: an even number of stages
   if (wfmt == 0) {
     switch (epi) {
       case EPI_RESID: return run_direct<EPI_RESID, 0, 256>(a, s);
@@ -778,11 +845,11 @@ hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   }
   switch (epi) {
-    case EPI_RESID: return run_staged<EPI_RESID, 0, 256>(a, s);
-    case EPI_SWIGLU: return run_staged<EPI_SWIGLU, 0, 256>(a, s);
+    case EPI_RESID: return run_w8<EPI_RESID, 0, 256>(a, s);
+    case EPI_SWIGLU: return run_w8<EPI_SWIGLU, 0, 256>(a, s);
     case EPI_QKV:
-      if (a.head_dim == 128) return run_staged<EPI_QKV, 128, 256>(a, s);
-      if (a.head_dim == 96) return run_staged<EPI_QKV, 96, 192>(a, s);
+      if (a.head_dim == 128) return run_w8<EPI_QKV, 128, 256>(a, s);
+      if (a.head_dim == 96) return run_w8<EPI_QKV, 96, 192>(a, s);
   }
   return hipErrorInvalidValue;
 }

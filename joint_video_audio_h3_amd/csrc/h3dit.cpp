@@ -51,6 +51,9 @@ h3_status check_dims(const h3_dims* d) {
     return fail(H3_ERR_UNSUPPORTED, "ffn=%d, hidden=%d: (ffn + 256) * hidden * 2 must be below 2^32",
                 d->ffn, d->hidden);
   if (d->n_tags > 8) return fail(H3_ERR_UNSUPPORTED, "n_tags=%d: at most 8", d->n_tags);
+  if (d->wfmt == H3_W_INT8_G32 && (d->heads * d->head_dim) % 128 != 0)
+    return fail(H3_ERR_UNSUPPORTED, "INT8 weights need heads*head_dim=%d to be a multiple of 128",
+                d->heads * d->head_dim);
   int sum = 0;
   for (int i = 0; i < 3; ++i) {
     if (d->rope_split[i] < 0 || d->rope_split[i] % 2 != 0)

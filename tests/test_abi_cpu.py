@@ -70,6 +70,19 @@ def test_bad_dims_rejected(L, field, value, code):
     assert lib.last_error()
 
 
+def test_int8_needs_inner_multiple_of_128(L):
+    """INT8 GEMMs run an even number of 64-wide K stages: heads*head_dim % 128 == 0."""
+    d = lib.make_dims(synth.TINY_DIMS)
+    d.wfmt = 1
+    assert L.h3_workspace_size(ctypes.byref(d), 100) > 0     # 4 x 96 = 384 = 3 x 128
+    d.heads = 2                                             # 2 x 96 = 192: a multiple of 64 only
+    assert L.h3_workspace_size(ctypes.byref(d), 100) == 0
+    assert L.h3_attention(ctypes.byref(d), FAKE, FAKE, FAKE, 100, FAKE, None) == lib.H3_ERR_UNSUPPORTED
+    assert "128" in lib.last_error()
+    d.wfmt = 0                                              # bf16 weights accept it
+    assert L.h3_workspace_size(ctypes.byref(d), 100) > 0
+
+
 def test_bad_rope_split_rejected(L):
     d = lib.make_dims(synth.H3_DIMS)
     d.rope_split[:] = [32, 48, 46]
