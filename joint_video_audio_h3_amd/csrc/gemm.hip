@@ -637,8 +637,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // two-buffer LDS pipeline with BK = 64 stages.  While stage kt is consumed:
 // A of stage kt+1 streams in by DMA (as in the bf16 kernel), the int8 codes of
 // stage kt+1 (loaded one stage earlier) are dequantised and written to LDS,
-// interleaved with the MFMAs, and then the codes of stage kt+2 are loaded into
-// the same registers.  Each code is turned into bf16(q*s) with one byte-to-float conversion
+// interleaved with the MFMAs, and the codes of stage kt+2 are loaded into the
+// same registers right after, so they have a whole stage to arrive.  Each code is turned into bf16(q*s) with one byte-to-float conversion
 // of q + 128 and one exact FMA, (q + 128)*s - 128*s, then rounded.  A full
 // wait the compiler can see ends every stage, so its own wait insertion never
 // counts the DMA loads it cannot see.
@@ -695,7 +695,7 @@ __global__ __launch_bounds__(512) void gemm_w8_kernel(GemmArgs p) {
 #pragma unroll
   for (int i = 0; i < NBC; ++i) {
     const int r = tid / 4 + (NT / 4) * i, c = tid & 3;
-    bval[i] = r < BN;
+    bval[i] = (NT / 4) * NBC <= BN || r < BN;   // compile-time true when every row exists
     const int rr = min(r, BN - 1);
     const uint32_t brow = (uint32_t)(weight_row<EPI, BN, TN>(p, tc.tn, rr) - b0);
     boffs[i] = brow * (uint32_t)K + 16 * c;
@@ -705,25 +705,30 @@ __global__ __launch_bounds__(512) void gemm_w8_kernel(GemmArgs p) {
   }
   // one register set: a stage's codes are dequantised before the next stage's
   // codes are loaded into the same registers
-  uint4 qv[NBC];
-  uint16_t sv[NBC];
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) u32x4_t lds_u4_t;
+  u32x4_t qv[NBC];
+  uint32_t sv[NBC];
   auto ldB = [&](int ks) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NBC; ++i)
       if (bval[i]) {
-        qv[i] = *reinterpret_cast<const uint4*>(bbase + boffs[i] + (size_t)ks * DBK);
+        qv[i] = *reinterpret_cast<const u32x4_t*>(bbase + boffs[i] + (size_t)ks * DBK);
         sv[i] = sbase[soffs[i] + ks * 2];
       }
   };
-  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) u32x4_t lds_u4_t;
   auto deqB = [&](uint32_t boff) __attribute__((always_inline)) {
+    // the codes count as produced here: nothing computed from them moves above
+    // this point (in particular not into the previous stage, where their loads
+    // are still in flight)
+#pragma unroll
+    for (int i = 0; i < NBC; ++i) asm volatile("" : "+v"(qv[i]), "+v"(sv[i]));
 #pragma unroll
     for (int i = 0; i < NBC; ++i)
       if (bval[i]) {
-        const float sc = bf2f(sv[i]), msc = -128.0f * sc;
-        const uint32_t w4[4] = {qv[i].x ^ 0x80808080u, qv[i].y ^ 0x80808080u,
-                                qv[i].z ^ 0x80808080u, qv[i].w ^ 0x80808080u};
+        const float sc = __uint_as_float(sv[i] << 16), msc = -128.0f * sc;
+        const uint32_t w4[4] = {qv[i][0] ^ 0x80808080u, qv[i][1] ^ 0x80808080u,
+                                qv[i][2] ^ 0x80808080u, qv[i][3] ^ 0x80808080u};
         uint32_t o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -779,11 +784,11 @@ __global__ __launch_bounds__(512) void gemm_w8_kernel(GemmArgs p) {
   // valid data that is never read, so every stage has the same shape.
   auto stage = [&](auto B_, int kt) __attribute__((always_inline)) {
     constexpr int b = decltype(B_)::value, nb = b ^ 1;
+    deqB(nb * ABUF);
+    ldB(min(kt + 2, KT - 1));
     dmaA(min(kt + 1, KT - 1), nb * ABUF);
     read_frags(B_, 1, fa1, fb1);
     mfmas(fa0, fb0);
-    deqB(nb * ABUF);
-    ldB(min(kt + 2, KT - 1));
     read_frags(B_, 2, fa0, fb0);
     mfmas(fa1, fb1);
     read_frags(B_, 3, fa1, fb1);
