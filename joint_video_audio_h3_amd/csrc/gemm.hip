@@ -292,6 +292,14 @@ __device__ __forceinline__ void qkv_epilogue_lds(const GemmArgs& p, f32x16 (&acc
 #pragma unroll
   for (int j = 0; j < FN; ++j) bias_c[j] = p.bias ? bf2f(p.bias[sec * 128 + j * 32 + lc]) : 0.f;
   const uint16_t* gam = kind == 0 ? p.gq : p.gk;
+  // the norm gain of this lane's 64 columns, loaded once (q and k sections)
+  const int c0 = 64 * hl;
+  u16x4 gv[16];
+  if (kind < 2) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      gv[k] = gam ? *reinterpret_cast<const u16x4*>(gam + c0 + 4 * k) : u16x4{0x3f80, 0x3f80, 0x3f80, 0x3f80};
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -301,9 +309,15 @@ __device__ __forceinline__ void qkv_epilogue_lds(const GemmArgs& p, f32x16 (&acc
         stage[(8 * (v / 4) + 4 * hl + (v % 4)) * QSTRIDE + j * 32 + lc] = acc[i][j][v] + bias_c[j];
     const int slab = row0 + i * 32;
     if (kind < 2) {
-      const int r = lc, c0 = 64 * hl;
+      const int r = lc;
       const int row = slab + r;
       const float* src = stage + r * QSTRIDE + c0;
+      // every rotary (cos, sin) load of the row before the first store, so the
+      // row waits for memory once (the stores could alias the loads otherwise)
+      const float4* cs = reinterpret_cast<const float4*>(p.cs + (size_t)row * 128 + c0);
+      float4 tv[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) tv[k] = cs[k];
       float ss = 0.f;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
@@ -313,7 +327,6 @@ __device__ __forceinline__ void qkv_epilogue_lds(const GemmArgs& p, f32x16 (&acc
       ss += __shfl_xor(ss, 32, 64);
       const float rn = 1.0f / sqrtf(ss / 128.0f + p.qk_eps);
       const float sc = kind == 0 ? rn * p.q_scale : rn;
-      const float4* cs = reinterpret_cast<const float4*>(p.cs + (size_t)row * 128 + c0);
       uint16_t* dst = (kind == 0 ? p.q : p.k) + ((size_t)head * p.n_pad + row) * 128 + c0;
       const bool valid = row < p.M;
 #pragma unroll
@@ -323,12 +336,9 @@ __device__ __forceinline__ void qkv_epilogue_lds(const GemmArgs& p, f32x16 (&acc
         for (int kk = 0; kk < 2; ++kk) {
           const int c = 4 * (k + kk);
           const float4 u = *reinterpret_cast<const float4*>(src + c);
-          const float4 t = cs[k + kk];   // (cos, sin) of the two pairs in u
-          float g0 = 1.f, g1 = 1.f, g2 = 1.f, g3 = 1.f;
-          if (gam) {
-            const u16x4 gg = *reinterpret_cast<const u16x4*>(gam + c0 + c);
-            g0 = bf2f(gg[0]); g1 = bf2f(gg[1]); g2 = bf2f(gg[2]); g3 = bf2f(gg[3]);
-          }
+          const float4 t = tv[k + kk];   // (cos, sin) of the two pairs in u
+          const u16x4 gg = gv[k + kk];
+          const float g0 = bf2f(gg[0]), g1 = bf2f(gg[1]), g2 = bf2f(gg[2]), g3 = bf2f(gg[3]);
           const float a0 = u.x * g0, a1 = u.y * g1, b0 = u.z * g2, b1 = u.w * g3;
           const float o0 = (a0 * t.x - a1 * t.y) * sc, o1 = (a0 * t.y + a1 * t.x) * sc;
           const float o2 = (b0 * t.z - b1 * t.w) * sc, o3 = (b0 * t.w + b1 * t.z) * sc;
