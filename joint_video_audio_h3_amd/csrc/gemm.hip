@@ -147,7 +147,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN
           if (row < p.M) {
             const float g = acc[i][j][v] + bg;
             const float u = acc[i][j + FN / 2][v] + bv;
-            const float a = g / (1.0f + __expf(-g)) * u;
+            // silu(g) = g * 1/(1 + e^-g) with the hardware reciprocal (~1 ulp,
+            // far below the bf16 rounding of the result); e^-g = inf gives 0
+            const float a = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
             p.out[(size_t)row * p.ffn + oc] = f2bf(a);
           }
         }
