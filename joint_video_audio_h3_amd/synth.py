@@ -48,6 +48,9 @@ _TID = {
     "x": 0, "w_qkv": 1, "b_qkv": 2, "w_out": 3, "b_out": 4, "w_fc1": 5,
     "b_fc1": 6, "w_fc2": 7, "b_fc2": 8, "q_norm": 9, "k_norm": 10, "table": 11,
     "h": 12, "o": 13, "a": 14, "q": 15, "k": 16, "v": 17, "tags": 18, "pos": 19,
+    "text": 20, "cond": 21, "audio_in": 22, "video_in": 23, "w_text": 24, "b_text": 25,
+    "w_video": 26, "b_video": 27, "w_audio": 28, "b_audio": 29, "w_head_audio": 30,
+    "b_head_audio": 31, "w_head_video": 32, "b_head_video": 33, "final_table": 34,
 }
 TAG_TEXT, TAG_AUDIO, TAG_VIDEO = 0, 1, 2
 WFMT_BF16, WFMT_INT8_G32 = 0, 1
@@ -73,6 +76,18 @@ class Dims:
 
 H3_DIMS = Dims(hidden=5376, heads=56, head_dim=128, ffn=14336)
 TINY_DIMS = Dims(hidden=256, heads=4, head_dim=96, ffn=768, rope_split=(24, 36, 36))
+
+
+@dataclasses.dataclass(frozen=True)
+class IoDims:
+    """Widths of the stream's inputs and outputs around the block stack."""
+    text_dim: int = 5120      # text encoder hidden state
+    video_patch: int = 96     # 24 latent channels x (1 x 2 x 2) patch
+    audio_patch: int = 32     # 32 latent channels
+
+
+H3_IO = IoDims()
+TINY_IO = IoDims(text_dim=128)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -236,6 +251,61 @@ def make_block_weights(dims: Dims, block: int, seed: int = 0,
     else:
         w["q_norm"] = w["k_norm"] = None
     return w
+
+
+def make_io_weights(dims: Dims, io: IoDims, seed: int = 0, biases: bool = True) -> Dict[str, Optional[np.ndarray]]:
+    """Weights of the steps around the block stack (host arrays).
+
+    w_text bf16 bits [D, text_dim]; w_video fp32 [D, video_patch]; w_audio fp32
+    [D, audio_patch]; output heads bf16 bits [patch, D] (drawn in fp32 and
+    rounded once, as the released fp32 heads are converted); biases of the
+    same kinds, all ~ N(0, 1/fan_in).
+    """
+    D = dims.hidden
+    w: Dict[str, Optional[np.ndarray]] = {}
+
+    def f32(name, shape, var):
+        return (_rng(seed, 0, name).standard_normal(shape, dtype=np.float32)
+                * np.float32(np.sqrt(var)))
+
+    w["w_text"] = _normal_bf16(seed, 0, "w_text", (D, io.text_dim), 1.0 / io.text_dim)
+    w["w_video"] = f32("w_video", (D, io.video_patch), 1.0 / io.video_patch)
+    w["w_audio"] = f32("w_audio", (D, io.audio_patch), 1.0 / io.audio_patch)
+    w["w_head_audio"] = _normal_bf16(seed, 0, "w_head_audio", (io.audio_patch, D), 1.0 / D)
+    w["w_head_video"] = _normal_bf16(seed, 0, "w_head_video", (io.video_patch, D), 1.0 / D)
+    if biases:
+        w["b_text"] = _normal_bf16(seed, 0, "b_text", (D,), 1.0 / io.text_dim)
+        w["b_video"] = f32("b_video", (D,), 1.0 / io.video_patch)
+        w["b_audio"] = f32("b_audio", (D,), 1.0 / io.audio_patch)
+        w["b_head_audio"] = _normal_bf16(seed, 0, "b_head_audio", (io.audio_patch,), 1.0 / D)
+        w["b_head_video"] = _normal_bf16(seed, 0, "b_head_video", (io.video_patch,), 1.0 / D)
+    else:
+        for k in ("b_text", "b_video", "b_audio", "b_head_audio", "b_head_video"):
+            w[k] = None
+    return w
+
+
+def make_final_table(dims: Dims, seed: int = 0) -> np.ndarray:
+    """Final AdaLN table bf16 bits [2, 2, D], (audio, video) x (shift, scale), ~ N(0, 0.1)."""
+    return _normal_bf16(seed, 0, "final_table", (2, 2, dims.hidden), 0.1)
+
+
+def make_io_inputs(wl: Workload, io: IoDims, seed: int = 0) -> Dict[str, np.ndarray]:
+    """Per-step inputs of the packed segments: text hidden state bf16 bits
+    [L, text_dim] ~ N(0, 1); condition and video latent patches fp32
+    [C|V, video_patch] and audio patches fp32 [A, audio_patch], all ~ N(0, 1)
+    (the noised latents of rectified flow are unit-variance)."""
+    V = wl.V[0] * wl.V[1] * wl.V[2]
+
+    def f32(name, shape):
+        return _rng(seed, 0, name).standard_normal(shape, dtype=np.float32)
+
+    return {
+        "text": _normal_bf16(seed, 0, "text", (wl.L, io.text_dim), 1.0),
+        "cond": f32("cond", (wl.C, io.video_patch)),
+        "audio": f32("audio_in", (wl.A, io.audio_patch)),
+        "video": f32("video_in", (V, io.video_patch)),
+    }
 
 
 def make_inputs(wl: Workload, seed: int = 0, n_blocks: Optional[int] = None,

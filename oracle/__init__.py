@@ -1,4 +1,4 @@
-"""CPU oracle of the MiniMax-H3 DiT block forward -- test infrastructure.
+"""CPU oracle of the MiniMax-H3 DiT forward -- test infrastructure.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
@@ -10,3 +10,4 @@ from .h3_block import (  # noqa: F401
     merge_heads, modulation_from_table, modulation_live, qkv_split, rms_norm,
     rope_angles, round_to_bf16, silu, swiglu, weight,
 )
+from .h3_io import SEGMENTS, embed_inputs, final_heads, segment_rows, velocity_forward  # noqa: F401
