@@ -132,6 +132,93 @@ H3DIT_API h3_status h3_dit_forward(const h3_dims* dims, float* x_packed, const i
 H3DIT_API const char* h3_last_error(void);
 
 /* ------------------------------------------------------------------------ */
+/* Around the block stack: inputs -> packed stream -> velocity               */
+/* ------------------------------------------------------------------------ */
+/* The packed stream's rows come from four inputs, in the order
+ * [text | conditions | audio | video] (minimax-h3-mlx README, "Architecture"):
+ *   text rows   = text_hidden W_text^T + b_text     (the text encoder's
+ *                 unnormalised hidden state, width 5120, into the DiT's
+ *                 condition projection: minimax-h3-mlx README, "Encoder
+ *                 truncation"); bf16 weights, fp32 accumulation.
+ *   cond rows   = cond_patch W_video^T + b_video     (keyframes are video
+ *                 latents; only two patch projections exist)
+ *   audio rows  = audio_patch W_audio^T + b_audio
+ *   video rows  = video_patch W_video^T + b_video
+ * The patch projections keep fp32 weights, inputs and accumulation (H3-metal
+ * digest, "Specialized projection kernels": 96 -> 5376 video, 32 -> 5376
+ * audio, fp32; minimax-h3-mlx README, "Published quants": these tensors ship
+ * in fp32).  After the blocks, the audio and the video slice each take a final
+ * AdaLN, h = LN(x) * (1 + scale_m) + shift_m, and their output head,
+ * vel = h W_head^T + b_head, with bf16 head weights (converted once from the
+ * released fp32 ones) on bf16 h, fp32 accumulation (H3-metal digest,
+ * "Exact DiT fusions" and "Specialized projection kernels").  Text and
+ * condition rows get no velocity. */
+typedef struct h3_io_dims {
+  int32_t text_dim;    /* text hidden-state width (5120); a multiple of 64       */
+  int32_t video_patch; /* video latent patch width (96 = 24 ch x 1x2x2); 32, 64, 96 or 128 */
+  int32_t audio_patch; /* audio latent patch width (32); 32, 64, 96 or 128       */
+} h3_io_dims;
+
+/* Row counts of the four segments; the stream has text+cond+audio+video rows. */
+typedef struct h3_segments {
+  int64_t text, cond, audio, video;
+} h3_segments;
+
+/* Device pointers.  Weights in PyTorch layout W[out][in]; biases nullable (0).
+ * Pointers of a segment with no rows may be NULL. */
+typedef struct h3_io_weights {
+  const uint16_t* w_text;       /* bf16 [D][text_dim]     condition projection    */
+  const uint16_t* b_text;       /* bf16 [D]                                       */
+  const float* w_video;         /* fp32 [D][video_patch]  video + condition rows  */
+  const float* b_video;         /* fp32 [D]                                       */
+  const float* w_audio;         /* fp32 [D][audio_patch]                          */
+  const float* b_audio;         /* fp32 [D]                                       */
+  const uint16_t* w_head_audio; /* bf16 [audio_patch][D]  audio output head       */
+  const uint16_t* b_head_audio; /* bf16 [audio_patch]                             */
+  const uint16_t* w_head_video; /* bf16 [video_patch][D]  video output head       */
+  const uint16_t* b_head_video; /* bf16 [video_patch]                             */
+} h3_io_weights;
+
+/* Bytes of scratch h3_final_heads needs (max(audio, video) rows of bf16 h).
+ * Pure.  Returns 0 on invalid dims or segments. */
+H3DIT_API size_t h3_heads_workspace_size(const h3_dims* dims, const h3_segments* segments);
+
+/* Writes every row of x_packed fp32 [N][D] from the inputs:
+ *   text bf16 [text][text_dim]; cond fp32 [cond][video_patch];
+ *   audio fp32 [audio][audio_patch]; video fp32 [video][video_patch]. */
+H3DIT_API h3_status h3_embed_inputs(const h3_dims* dims, const h3_io_dims* io_dims,
+                                    const h3_io_weights* io_weights, const h3_segments* segments,
+                                    const uint16_t* text, const float* cond, const float* audio,
+                                    const float* video, float* x_packed, void* stream);
+
+/* Velocities from the stream x_packed fp32 [N][D] (read only):
+ *   final_table bf16 [2][2][D]: (audio, video) x (shift, scale) of the final
+ *               AdaLN for this timestep (precomputed like mod_table)
+ *   vel_audio   fp32 [audio][audio_patch];  vel_video fp32 [video][video_patch]
+ *   workspace   at least h3_heads_workspace_size() bytes */
+H3DIT_API h3_status h3_final_heads(const h3_dims* dims, const h3_io_dims* io_dims,
+                                   const h3_io_weights* io_weights, const h3_segments* segments,
+                                   const float* x_packed, const uint16_t* final_table,
+                                   float* vel_audio, float* vel_video, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* One velocity forward: h3_embed_inputs into x_packed (which the caller
+ * provides and which ends holding the last block's output), n_blocks blocks
+ * as h3_dit_forward (n_blocks may be 0: then tag, positions, mod_table and
+ * weights may be NULL and the workspace needs only h3_heads_workspace_size()
+ * bytes, else h3_workspace_size(dims, N)), then h3_final_heads. */
+H3DIT_API h3_status h3_velocity_forward(const h3_dims* dims, const h3_io_dims* io_dims,
+                                        const h3_io_weights* io_weights,
+                                        const h3_segments* segments, const uint16_t* text,
+                                        const float* cond, const float* audio, const float* video,
+                                        const int32_t* tag, const float* positions,
+                                        const uint16_t* mod_table,
+                                        const h3_block_weights* weights, int32_t n_blocks,
+                                        const uint16_t* final_table, float* x_packed,
+                                        float* vel_audio, float* vel_video, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Step entry points: each runs one step of the block on caller buffers.     */
 /* They are the kernels h3_dit_block_forward launches, exposed for parity   */
 /* tests and per-step timing.                                               */

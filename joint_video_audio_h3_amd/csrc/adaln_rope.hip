@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void adaln_kernel(AdalnArgs a) {
   }
   const float var = wave_sum(q) / (float)a.D;
   const float rstd = 1.0f / sqrtf(var + a.eps);
-  const int t = a.tag[row];
+  const int t = a.tag ? a.tag[row] : 0;   // no tags: one (shift, scale) pair for every row
   const u16x4* sh = reinterpret_cast<const u16x4*>(a.table + ((size_t)t * 6 + a.k_shift) * a.D);
   const u16x4* sc = reinterpret_cast<const u16x4*>(a.table + ((size_t)t * 6 + a.k_scale) * a.D);
   uint2* hr = reinterpret_cast<uint2*>(a.h + (size_t)row * a.D);

@@ -47,6 +47,8 @@
 //             (minimax-h3-mlx README, "Validation": fc2(silu(gate) * value);
 //             H3-metal digest, "Metal 4 and TensorOps paths": paired gate/up
 //             tiles apply SwiGLU before writing).
+//  EPI_STORE  x[r][c] = acc + bias[c], fp32 (the text condition projection
+//             into the stream's text rows, and the narrow output heads).
 //  EPI_QKV    each wave's N range is exactly one head_dim section of the
 //             per-head interleaved [q|k|v] projection; q and k get RMSNorm
 //             over the section (half-wave butterfly), the gain, and the rotary
@@ -219,10 +221,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN
 // Gated residual through LDS: each wavefront stages one 32-row slab of its
 // accumulator tile at a time (fp32, padded rows), then reads it back as
 // float4 along rows, so x is read and written in 16-byte coalesced pieces,
-// the gate in 8-byte pieces, and the bias is loaded once per lane.
+// the gate in 8-byte pieces, and the bias is loaded once per lane.  Without
+// GATED the same path stores acc + bias (EPI_STORE).
 constexpr int RSTRIDE = 136;   // floats per staged row (128 + 8 of padding)
 
-template <int TM, int TN, int FM, int FN>
+template <bool GATED, int TM, int TN, int FM, int FN>
 __device__ __forceinline__ void resid_epilogue_lds(const GemmArgs& p, f32x16 (&acc)[FM][FN],
                                                    int row0, int col0, int lane, float* stage,
                                                    const int* s_tag) {
@@ -252,7 +255,7 @@ __device__ __forceinline__ void resid_epilogue_lds(const GemmArgs& p, f32x16 (&a
     for (int it = 0; it < 16; ++it) {
       const int r = 2 * it + hl;
       const int row = row0 + i * 32 + r;
-      if (row < p.M && col_ok) {
+      if (GATED && row < p.M && col_ok) {
         const int t = s_tag[i * 32 + r];
         gv[it] = *reinterpret_cast<const u16x4*>(p.gate_tab + (size_t)t * p.tag_stride + gcol);
         xv[it] = *reinterpret_cast<const float4*>(p.x + (size_t)row * p.ldx + gcol);
@@ -264,12 +267,17 @@ __device__ __forceinline__ void resid_epilogue_lds(const GemmArgs& p, f32x16 (&a
       const int row = row0 + i * 32 + r;
       const float4 a = *reinterpret_cast<const float4*>(stage + r * RSTRIDE + 4 * lc);
       if (row < p.M && col_ok) {
-        float4 x = xv[it];
-        const u16x4 g = gv[it];
-        x.x += bf2f(g[0]) * (a.x + b4.x);
-        x.y += bf2f(g[1]) * (a.y + b4.y);
-        x.z += bf2f(g[2]) * (a.z + b4.z);
-        x.w += bf2f(g[3]) * (a.w + b4.w);
+        float4 x;
+        if constexpr (GATED) {
+          x = xv[it];
+          const u16x4 g = gv[it];
+          x.x += bf2f(g[0]) * (a.x + b4.x);
+          x.y += bf2f(g[1]) * (a.y + b4.y);
+          x.z += bf2f(g[2]) * (a.z + b4.z);
+          x.w += bf2f(g[3]) * (a.w + b4.w);
+        } else {
+          x = make_float4(a.x + b4.x, a.y + b4.y, a.z + b4.z, a.w + b4.w);
+        }
         *reinterpret_cast<float4*>(p.x + (size_t)row * p.ldx + gcol) = x;
       }
     }
@@ -631,8 +639,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int* s_tag = reinterpret_cast<int*>(ring + 4 * 32 * RSTRIDE * sizeof(float));
     s_tag[tid] = p.tag[min(m0 + tid, p.M - 1)];
     __syncthreads();
-    resid_epilogue_lds<TM, TN, FM, FN>(p, acc, m0 + wm * TM, n0 + wn * TN, lane,
-                                       reinterpret_cast<float*>(ring) + wave * 32 * RSTRIDE, s_tag + wm * TM);
+    resid_epilogue_lds<true, TM, TN, FM, FN>(p, acc, m0 + wm * TM, n0 + wn * TN, lane,
+                                             reinterpret_cast<float*>(ring) + wave * 32 * RSTRIDE, s_tag + wm * TM);
+  } else if constexpr (EPI == EPI_STORE) {
+    resid_epilogue_lds<false, TM, TN, FM, FN>(p, acc, m0 + wm * TM, n0 + wn * TN, lane,
+                                              reinterpret_cast<float*>(ring) + wave * 32 * RSTRIDE, nullptr);
   } else if constexpr (EPI == EPI_QKV && SEC == 128) {
     const int sec = (n0 + wn * TN) / SEC;
     if (sec < 3 * p.heads)
@@ -862,9 +873,10 @@ static int device_cus() {
   return cus[dev];
 }
 
-// Residual GEMMs have the narrowest output (hidden); when 256-wide tiles leave
-// the last wave of tiles mostly empty, 192-wide ones (a quarter fewer MFMAs per
-// tile, ~5% less efficient per MFMA) balance better.  Cost model: waves of
+// Residual and store GEMMs have the narrowest outputs (hidden, or a head's
+// patch width); when 256-wide tiles leave the last wave of tiles mostly empty,
+// or the output is narrower than a tile, 192-wide ones (a quarter fewer MFMAs
+// per tile, ~5% less efficient per MFMA) balance better.  Cost model: waves of
 // tiles x work per tile.
 static bool resid_prefers_192(const GemmArgs& a) {
   const long tiles_m = (a.M + 255) / 256, cus = device_cus();
@@ -881,6 +893,9 @@ hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
       case EPI_RESID:
         if (resid_prefers_192(a)) return run_direct<EPI_RESID, 0, 192>(a, s);
         return run_direct<EPI_RESID, 0, 256>(a, s);
+      case EPI_STORE:
+        if (resid_prefers_192(a)) return run_direct<EPI_STORE, 0, 192>(a, s);
+        return run_direct<EPI_STORE, 0, 256>(a, s);
       case EPI_SWIGLU: return run_direct<EPI_SWIGLU, 0, 256>(a, s);
       case EPI_QKV:
         if (a.head_dim == 128) return run_direct<EPI_QKV, 128, 256>(a, s);
@@ -888,7 +903,7 @@ hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
     }
     return hipErrorInvalidValue;
   }
-  switch (epi) {
+  switch (epi) {   // (EPI_STORE layers have bf16 weights only)
     case EPI_RESID: return run_w8<EPI_RESID, 0, 256>(a, s);
     case EPI_SWIGLU: return run_w8<EPI_SWIGLU, 0, 256>(a, s);
     case EPI_QKV:

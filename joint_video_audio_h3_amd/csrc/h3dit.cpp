@@ -293,6 +293,144 @@ h3_status check_forward_common(const h3_dims* dims, const float* x, const int32_
   return H3_OK;
 }
 
+// ---------------------------------------------------------------- around the block stack
+bool patch_ok(int p) { return p == 32 || p == 64 || p == 96 || p == 128; }
+
+h3_status check_io(const h3_dims* d, const h3_io_dims* io, const h3_segments* sg) {
+  h3_status st;
+  if ((st = check_dims(d)) != H3_OK) return st;
+  if (!io) return fail(H3_ERR_INVALID_ARG, "io_dims is NULL");
+  if (!sg) return fail(H3_ERR_INVALID_ARG, "segments is NULL");
+  if (sg->text < 0 || sg->cond < 0 || sg->audio < 0 || sg->video < 0)
+    return fail(H3_ERR_INVALID_ARG, "segment row counts must be >= 0");
+  if ((st = check_rows(sg->text + sg->cond + sg->audio + sg->video)) != H3_OK) return st;
+  if (io->text_dim <= 0 || io->text_dim % 64 != 0)
+    return fail(H3_ERR_UNSUPPORTED, "text_dim=%d must be a positive multiple of 64", io->text_dim);
+  if (!patch_ok(io->video_patch) || !patch_ok(io->audio_patch))
+    return fail(H3_ERR_UNSUPPORTED, "patch widths video=%d audio=%d: supported 32, 64, 96, 128",
+                io->video_patch, io->audio_patch);
+  return H3_OK;
+}
+
+h3_status check_embed_ptrs(const h3_segments& sg, const h3_io_weights* w, const void* text,
+                           const void* cond, const void* audio, const void* video, const void* x) {
+  if (!w) return fail(H3_ERR_INVALID_ARG, "io_weights is NULL");
+  H3_NEED(x, "x_packed");
+  if (sg.text > 0) {
+    H3_NEED(text, "text");
+    H3_NEED(w->w_text, "w_text");
+    H3_OPT(w->b_text, "b_text");
+  }
+  if (sg.cond > 0) H3_NEED(cond, "cond");
+  if (sg.video > 0) H3_NEED(video, "video");
+  if (sg.cond > 0 || sg.video > 0) {
+    H3_NEED(w->w_video, "w_video");
+    H3_OPT(w->b_video, "b_video");
+  }
+  if (sg.audio > 0) {
+    H3_NEED(audio, "audio");
+    H3_NEED(w->w_audio, "w_audio");
+    H3_OPT(w->b_audio, "b_audio");
+  }
+  return H3_OK;
+}
+
+h3_status check_head_ptrs(const h3_segments& sg, const h3_io_weights* w, const void* x,
+                          const void* final_table, const void* vel_audio, const void* vel_video) {
+  if (!w) return fail(H3_ERR_INVALID_ARG, "io_weights is NULL");
+  H3_NEED(x, "x_packed");
+  H3_NEED(final_table, "final_table");
+  if (sg.audio > 0) {
+    H3_NEED(vel_audio, "vel_audio");
+    H3_NEED(w->w_head_audio, "w_head_audio");
+    H3_OPT(w->b_head_audio, "b_head_audio");
+  }
+  if (sg.video > 0) {
+    H3_NEED(vel_video, "vel_video");
+    H3_NEED(w->w_head_video, "w_head_video");
+    H3_OPT(w->b_head_video, "b_head_video");
+  }
+  return H3_OK;
+}
+
+size_t heads_ws_bytes(const h3_dims& d, const h3_segments& sg) {
+  return up256((size_t)std::max(sg.audio, sg.video) * d.hidden * 2);
+}
+
+hipError_t do_patch(const h3_dims& d, const float* in, const float* W, const float* b, int P,
+                    int64_t rows, float* out, hipStream_t s) {
+  h3::PatchArgs a{};
+  a.in = in;
+  a.W = W;
+  a.bias = b;
+  a.out = out;
+  a.rows = (int)rows;
+  a.P = P;
+  a.D = d.hidden;
+  return h3::launch_patch_embed(a, s);
+}
+
+h3_status run_embed(const h3_dims& d, const h3_io_dims& io, const h3_io_weights& w,
+                    const h3_segments& sg, const uint16_t* text, const float* cond,
+                    const float* audio, const float* video, float* x, hipStream_t s) {
+  const size_t D = d.hidden;
+  h3_status st;
+  if (sg.text > 0) {
+    h3::GemmArgs g = gemm_base(d, text, w.w_text, nullptr, w.b_text, (int)sg.text, io.text_dim, d.hidden);
+    g.x = x;
+    g.ldx = d.hidden;
+    if ((st = hip_ok(h3::launch_gemm(h3::EPI_STORE, H3_W_BF16, g, s), "text projection")) != H3_OK)
+      return st;
+  }
+  float* xc = x + (size_t)sg.text * D;
+  float* xa = xc + (size_t)sg.cond * D;
+  float* xv = xa + (size_t)sg.audio * D;
+  if (sg.cond > 0 &&
+      (st = hip_ok(do_patch(d, cond, w.w_video, w.b_video, io.video_patch, sg.cond, xc, s),
+                   "condition patch projection")) != H3_OK)
+    return st;
+  if (sg.audio > 0 &&
+      (st = hip_ok(do_patch(d, audio, w.w_audio, w.b_audio, io.audio_patch, sg.audio, xa, s),
+                   "audio patch projection")) != H3_OK)
+    return st;
+  if (sg.video > 0 &&
+      (st = hip_ok(do_patch(d, video, w.w_video, w.b_video, io.video_patch, sg.video, xv, s),
+                   "video patch projection")) != H3_OK)
+    return st;
+  return H3_OK;
+}
+
+// Final AdaLN of one modality's slice (one (shift, scale) pair for all its rows)
+// into h, then its output head into vel.
+h3_status run_head(const h3_dims& d, const float* x_rows, int64_t rows, const uint16_t* tab_m,
+                   const uint16_t* w_head, const uint16_t* b_head, int P, uint16_t* h, float* vel,
+                   hipStream_t s, const char* what) {
+  h3_status st;
+  if ((st = hip_ok(do_adaln(d, x_rows, nullptr, tab_m, 0, rows, h, s), what)) != H3_OK) return st;
+  h3::GemmArgs g = gemm_base(d, h, w_head, nullptr, b_head, (int)rows, d.hidden, P);
+  g.x = vel;
+  g.ldx = P;
+  return hip_ok(h3::launch_gemm(h3::EPI_STORE, H3_W_BF16, g, s), what);
+}
+
+h3_status run_heads(const h3_dims& d, const h3_io_dims& io, const h3_io_weights& w,
+                    const h3_segments& sg, const float* x, const uint16_t* final_table,
+                    float* vel_audio, float* vel_video, uint16_t* h, hipStream_t s) {
+  const size_t D = d.hidden;
+  const float* xa = x + (size_t)(sg.text + sg.cond) * D;
+  const float* xv = xa + (size_t)sg.audio * D;
+  h3_status st;
+  if (sg.audio > 0 &&
+      (st = run_head(d, xa, sg.audio, final_table, w.w_head_audio, w.b_head_audio, io.audio_patch,
+                     h, vel_audio, s, "audio head")) != H3_OK)
+    return st;
+  if (sg.video > 0 &&
+      (st = run_head(d, xv, sg.video, final_table + 2 * D, w.w_head_video, w.b_head_video,
+                     io.video_patch, h, vel_video, s, "video head")) != H3_OK)
+    return st;
+  return H3_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -460,6 +598,102 @@ h3_status h3_mlp_fc2_residual(const h3_dims* dims, const uint16_t* a,
   return hip_ok(do_resid(*dims, a, weights->w_fc2, weights->s_fc2, weights->b_fc2, dims->ffn,
                          mod_table, 5, tag, n_rows, x, reinterpret_cast<hipStream_t>(stream)),
                 "fc2+gate");
+}
+
+size_t h3_heads_workspace_size(const h3_dims* dims, const h3_segments* segments) {
+  if (check_dims(dims) != H3_OK) return 0;
+  if (!segments || segments->audio < 0 || segments->video < 0) {
+    fail(H3_ERR_INVALID_ARG, "segments is NULL or negative");
+    return 0;
+  }
+  const size_t b = heads_ws_bytes(*dims, *segments);
+  return b ? b : 256;
+}
+
+h3_status h3_embed_inputs(const h3_dims* dims, const h3_io_dims* io_dims,
+                          const h3_io_weights* io_weights, const h3_segments* segments,
+                          const uint16_t* text, const float* cond, const float* audio,
+                          const float* video, float* x_packed, void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_io(dims, io_dims, segments)) != H3_OK) return st;
+  if ((st = check_embed_ptrs(*segments, io_weights, text, cond, audio, video, x_packed)) != H3_OK)
+    return st;
+  if ((st = check_device()) != H3_OK) return st;
+  return run_embed(*dims, *io_dims, *io_weights, *segments, text, cond, audio, video, x_packed,
+                   reinterpret_cast<hipStream_t>(stream));
+}
+
+h3_status h3_final_heads(const h3_dims* dims, const h3_io_dims* io_dims,
+                         const h3_io_weights* io_weights, const h3_segments* segments,
+                         const float* x_packed, const uint16_t* final_table, float* vel_audio,
+                         float* vel_video, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_io(dims, io_dims, segments)) != H3_OK) return st;
+  if ((st = check_head_ptrs(*segments, io_weights, x_packed, final_table, vel_audio, vel_video)) != H3_OK)
+    return st;
+  H3_NEED(workspace, "workspace");
+  const size_t need = heads_ws_bytes(*dims, *segments);
+  if (workspace_bytes < need)
+    return fail(H3_ERR_WORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, need);
+  if ((st = check_device()) != H3_OK) return st;
+  return run_heads(*dims, *io_dims, *io_weights, *segments, x_packed, final_table, vel_audio,
+                   vel_video, static_cast<uint16_t*>(workspace), reinterpret_cast<hipStream_t>(stream));
+}
+
+h3_status h3_velocity_forward(const h3_dims* dims, const h3_io_dims* io_dims,
+                              const h3_io_weights* io_weights, const h3_segments* segments,
+                              const uint16_t* text, const float* cond, const float* audio,
+                              const float* video, const int32_t* tag, const float* positions,
+                              const uint16_t* mod_table, const h3_block_weights* weights,
+                              int32_t n_blocks, const uint16_t* final_table, float* x_packed,
+                              float* vel_audio, float* vel_video, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_io(dims, io_dims, segments)) != H3_OK) return st;
+  const h3_segments sg = *segments;
+  const int64_t n = sg.text + sg.cond + sg.audio + sg.video;
+  if ((st = check_embed_ptrs(sg, io_weights, text, cond, audio, video, x_packed)) != H3_OK) return st;
+  if ((st = check_head_ptrs(sg, io_weights, x_packed, final_table, vel_audio, vel_video)) != H3_OK)
+    return st;
+  if (n_blocks < 0) return fail(H3_ERR_INVALID_ARG, "n_blocks=%d must be >= 0", n_blocks);
+  if (n_blocks > 0) {
+    if ((st = check_forward_common(dims, x_packed, tag, positions, mod_table, n, workspace,
+                                   workspace_bytes)) != H3_OK)
+      return st;
+    if (!weights) return fail(H3_ERR_INVALID_ARG, "weights is NULL");
+    for (int b = 0; b < n_blocks; ++b) {
+      if ((st = check_weights(dims, &weights[b], true, true, true, true)) != H3_OK) {
+        std::string m = g_err;
+        return fail(st, "block %d: %s", b, m.c_str());
+      }
+    }
+  } else {
+    H3_NEED(workspace, "workspace");
+    const size_t need = heads_ws_bytes(*dims, sg);
+    if (workspace_bytes < need)
+      return fail(H3_ERR_WORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  if ((st = check_device()) != H3_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((st = run_embed(*dims, *io_dims, *io_weights, sg, text, cond, audio, video, x_packed, s)) != H3_OK)
+    return st;
+  uint16_t* h = static_cast<uint16_t*>(workspace);
+  if (n_blocks > 0) {
+    const Arena ar = carve(*dims, n, static_cast<char*>(workspace));
+    if ((st = hip_ok(do_rope(*dims, positions, n, ar.cs, s), "rope table")) != H3_OK) return st;
+    const size_t tstride = (size_t)dims->n_tags * 6 * dims->hidden;
+    for (int b = 0; b < n_blocks; ++b) {
+      if ((st = run_block(*dims, x_packed, tag, mod_table + b * tstride, weights[b], n, ar, s)) != H3_OK) {
+        std::string m = g_err;
+        return fail(st, "block %d: %s", b, m.c_str());
+      }
+    }
+    h = ar.h;   // dead after the last block; holds max(audio, video) rows
+  }
+  return run_heads(*dims, *io_dims, *io_weights, sg, x_packed, final_table, vel_audio, vel_video, h, s);
 }
 
 }  // extern "C"

@@ -17,7 +17,7 @@ hipError_t launch_rope_table(const RopeArgs& a, hipStream_t s);
 
 struct AdalnArgs {
   const float* x;        // [n][D]
-  const int32_t* tag;    // [n]
+  const int32_t* tag;    // [n], or null: every row uses table entry 0
   const uint16_t* table; // [T][6][D]
   uint16_t* h;           // [n][D]
   int n, D, k_shift, k_scale;
@@ -25,7 +25,7 @@ struct AdalnArgs {
 };
 hipError_t launch_adaln(const AdalnArgs& a, hipStream_t s);
 
-enum Epi { EPI_RESID = 0, EPI_SWIGLU = 1, EPI_QKV = 2 };
+enum Epi { EPI_RESID = 0, EPI_SWIGLU = 1, EPI_QKV = 2, EPI_STORE = 3 };
 
 struct GemmArgs {
   const uint16_t* A;      // [M][K] bf16
@@ -35,6 +35,7 @@ struct GemmArgs {
   int M, K;
   int n_out;              // GEMM output columns (= B rows used)
   // EPI_RESID: x[M][ldx] += gate_tab[tag*6*D + col] * (acc + bias)
+  // EPI_STORE: x[M][ldx]  = acc + bias
   float* x; int ldx;
   const uint16_t* gate_tab; const int32_t* tag; int tag_stride;
   // EPI_SWIGLU: out[M][ffn] = silu(gate) * value, gate rows [0,ffn), value rows [ffn, 2ffn)
@@ -51,5 +52,14 @@ struct AttnArgs {
   int n, n_pad, heads, head_dim;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+struct PatchArgs {
+  const float* in;       // [rows][P] fp32 latent patches
+  const float* W;        // [D][P] fp32
+  const float* bias;     // [D] fp32 or null
+  float* out;            // [rows][D] fp32 (rows of the packed stream)
+  int rows, P, D;
+};
+hipError_t launch_patch_embed(const PatchArgs& a, hipStream_t s);
 
 }  // namespace h3

@@ -1,6 +1,6 @@
 """ctypes binding of libh3dit.so (the C ABI declared in include/h3dit.h).
 
-Argument marshalling only: every step of the block runs in the HIP kernels
+Argument marshalling only: every step of the forward runs in the HIP kernels
 behind the C ABI.  torch is used for device memory and streams -- tensors are
 passed by ``data_ptr()`` and the current HIP stream by its handle.  There is no
 CPU path: if the library is missing, :func:`load` raises.
@@ -38,6 +38,25 @@ class H3BlockWeights(ctypes.Structure):
     _fields_ = [(n, c_vp) for n in WEIGHT_FIELDS]
 
 
+class H3IoDims(ctypes.Structure):
+    _fields_ = [("text_dim", c_i32), ("video_patch", c_i32), ("audio_patch", c_i32)]
+
+
+class H3Segments(ctypes.Structure):
+    _fields_ = [("text", c_i64), ("cond", c_i64), ("audio", c_i64), ("video", c_i64)]
+
+
+IO_WEIGHT_FIELDS = ["w_text", "b_text", "w_video", "b_video", "w_audio", "b_audio",
+                    "w_head_audio", "b_head_audio", "w_head_video", "b_head_video"]
+
+
+class H3IoWeights(ctypes.Structure):
+    _fields_ = [(n, c_vp) for n in IO_WEIGHT_FIELDS]
+
+
+_PD, _PIO, _PW, _PSG = (ctypes.POINTER(H3Dims), ctypes.POINTER(H3IoDims), ctypes.POINTER(H3IoWeights),
+                        ctypes.POINTER(H3Segments))
+
 # name -> (restype, argtypes), mirroring include/h3dit.h
 _SIGS = {
     "h3_padded_rows": (c_i64, [c_i64]),
@@ -58,6 +77,12 @@ _SIGS = {
                                   c_i64, c_vp, c_vp]),
     "h3_mlp_fc2_residual": (c_i32, [ctypes.POINTER(H3Dims), c_vp, ctypes.POINTER(H3BlockWeights),
                                     c_vp, c_vp, c_i64, c_vp, c_vp]),
+    "h3_heads_workspace_size": (c_sz, [_PD, _PSG]),
+    "h3_embed_inputs": (c_i32, [_PD, _PIO, _PW, _PSG, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "h3_final_heads": (c_i32, [_PD, _PIO, _PW, _PSG, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "h3_velocity_forward": (c_i32, [_PD, _PIO, _PW, _PSG, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                    ctypes.POINTER(H3BlockWeights), c_i32, c_vp, c_vp, c_vp, c_vp,
+                                    c_vp, c_sz, c_vp]),
 }
 
 _lib = None
@@ -190,6 +215,72 @@ def mlp_fc2_residual(dims, a, block, mod_table, tag, x, stream=None):
     _check(load().h3_mlp_fc2_residual(ctypes.byref(make_dims(dims)), a.data_ptr(), ctypes.byref(w),
                                       mod_table.data_ptr(), tag.data_ptr(), x.shape[0],
                                       x.data_ptr(), _stream(stream)))
+
+
+def make_io_dims(io) -> H3IoDims:
+    s = H3IoDims()
+    s.text_dim, s.video_patch, s.audio_patch = io.text_dim, io.video_patch, io.audio_patch
+    return s
+
+
+def make_segments(text: int, cond: int, audio: int, video: int) -> H3Segments:
+    s = H3Segments()
+    s.text, s.cond, s.audio, s.video = int(text), int(cond), int(audio), int(video)
+    return s
+
+
+def make_io_weights(w: Dict) -> H3IoWeights:
+    out = H3IoWeights()
+    for n in IO_WEIGHT_FIELDS:
+        setattr(out, n, _ptr(w.get(n)))
+    return out
+
+
+def heads_workspace_size(dims, segments: H3Segments) -> int:
+    sz = load().h3_heads_workspace_size(ctypes.byref(make_dims(dims)), ctypes.byref(segments))
+    if sz == 0:
+        raise H3Error(H3_ERR_INVALID_ARG, last_error())
+    return sz
+
+
+def _rows(t) -> int:
+    return 0 if t is None else int(t.shape[0])
+
+
+def segments_of(text, cond, audio, video) -> H3Segments:
+    return make_segments(_rows(text), _rows(cond), _rows(audio), _rows(video))
+
+
+def embed_inputs(dims, io, io_w: Dict, text, cond, audio, video, x, stream=None):
+    """x fp32 [N, D] <- the packed [text | cond | audio | video] rows."""
+    sg = segments_of(text, cond, audio, video)
+    w = make_io_weights(io_w)
+    _check(load().h3_embed_inputs(ctypes.byref(make_dims(dims)), ctypes.byref(make_io_dims(io)),
+                                  ctypes.byref(w), ctypes.byref(sg), _ptr(text), _ptr(cond),
+                                  _ptr(audio), _ptr(video), x.data_ptr(), _stream(stream)))
+
+
+def final_heads(dims, io, io_w: Dict, segments: H3Segments, x, final_table, vel_audio, vel_video,
+                workspace, stream=None):
+    w = make_io_weights(io_w)
+    _check(load().h3_final_heads(ctypes.byref(make_dims(dims)), ctypes.byref(make_io_dims(io)),
+                                 ctypes.byref(w), ctypes.byref(segments), x.data_ptr(),
+                                 final_table.data_ptr(), _ptr(vel_audio), _ptr(vel_video),
+                                 workspace.data_ptr(), workspace.numel(), _stream(stream)))
+
+
+def velocity_forward(dims, io, io_w: Dict, text, cond, audio, video, tag, positions, mod_table,
+                     blocks: Sequence[Dict], final_table, x, vel_audio, vel_video, workspace,
+                     stream=None):
+    """Inputs -> packed stream x -> len(blocks) blocks -> (vel_audio, vel_video)."""
+    sg = segments_of(text, cond, audio, video)
+    w = make_io_weights(io_w)
+    arr = (H3BlockWeights * max(len(blocks), 1))(*[make_weights(b) for b in blocks])
+    _check(load().h3_velocity_forward(
+        ctypes.byref(make_dims(dims)), ctypes.byref(make_io_dims(io)), ctypes.byref(w),
+        ctypes.byref(sg), _ptr(text), _ptr(cond), _ptr(audio), _ptr(video), _ptr(tag),
+        _ptr(positions), _ptr(mod_table), arr, len(blocks), final_table.data_ptr(), x.data_ptr(),
+        _ptr(vel_audio), _ptr(vel_video), workspace.data_ptr(), workspace.numel(), _stream(stream)))
 
 
 def to_device_block(block: Dict, device="cuda") -> Dict:

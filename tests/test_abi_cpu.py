@@ -38,6 +38,9 @@ def test_every_declared_symbol_is_exported(L):
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(lib.H3Dims) == 4 * 12
     assert ctypes.sizeof(lib.H3BlockWeights) == 8 * 14
+    assert ctypes.sizeof(lib.H3IoDims) == 4 * 3
+    assert ctypes.sizeof(lib.H3Segments) == 8 * 4
+    assert ctypes.sizeof(lib.H3IoWeights) == 8 * 10
 
 
 def test_padded_rows_and_workspace(L):
@@ -128,6 +131,55 @@ def test_argument_errors_before_launch(L):
     assert st == lib.H3_ERR_INVALID_ARG and "block 1" in lib.last_error()
     assert L.h3_dit_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, arr, 0, 100, FAKE, ws, None) \
         == lib.H3_ERR_INVALID_ARG
+
+
+def _io_weights():
+    w = lib.H3IoWeights()
+    for f in ("w_text", "w_video", "w_audio", "w_head_audio", "w_head_video"):
+        setattr(w, f, FAKE)
+    return w
+
+
+def _embed_call(L, d, io, w, sg, x=FAKE, text=FAKE):
+    return L.h3_embed_inputs(ctypes.byref(d), ctypes.byref(io), ctypes.byref(w), ctypes.byref(sg),
+                             text, FAKE, FAKE, FAKE, x, None)
+
+
+def test_io_argument_errors_before_launch(L):
+    d = lib.make_dims(synth.H3_DIMS)
+    io = lib.make_io_dims(synth.H3_IO)
+    sg = lib.make_segments(256, 1024, 200, 48360)
+    w = _io_weights()
+    assert lib.heads_workspace_size(synth.H3_DIMS, sg) == 48360 * 5376 * 2
+    assert _embed_call(L, d, io, w, lib.make_segments(0, 0, 0, 0)) == lib.H3_ERR_INVALID_ARG
+    assert _embed_call(L, d, io, w, lib.make_segments(-1, 0, 0, 5)) == lib.H3_ERR_INVALID_ARG
+    assert _embed_call(L, d, io, w, sg, x=None) == lib.H3_ERR_INVALID_ARG
+    assert "x_packed" in lib.last_error()
+    assert _embed_call(L, d, io, w, sg, text=None) == lib.H3_ERR_INVALID_ARG
+    assert "text" in lib.last_error()
+    # a segment with no rows needs no input and no weights
+    w2 = _io_weights()
+    w2.w_audio = None
+    assert _embed_call(L, d, io, w2, sg) == lib.H3_ERR_INVALID_ARG and "w_audio" in lib.last_error()
+    for bad in (lib.H3IoDims(5000, 96, 32), lib.H3IoDims(5120, 48, 32), lib.H3IoDims(5120, 96, 160)):
+        assert _embed_call(L, d, bad, w, sg) == lib.H3_ERR_UNSUPPORTED, lib.last_error()
+    ws = lib.heads_workspace_size(synth.H3_DIMS, sg)
+    st = L.h3_final_heads(ctypes.byref(d), ctypes.byref(io), ctypes.byref(w), ctypes.byref(sg),
+                          FAKE, FAKE, FAKE, FAKE, FAKE, ws - 256, None)
+    assert st == lib.H3_ERR_WORKSPACE
+    st = L.h3_final_heads(ctypes.byref(d), ctypes.byref(io), ctypes.byref(w), ctypes.byref(sg),
+                          FAKE, None, FAKE, FAKE, FAKE, ws, None)
+    assert st == lib.H3_ERR_INVALID_ARG and "final_table" in lib.last_error()
+    # the whole path checks its blocks too
+    arr = (lib.H3BlockWeights * 1)(lib.H3BlockWeights())
+    st = L.h3_velocity_forward(ctypes.byref(d), ctypes.byref(io), ctypes.byref(w), ctypes.byref(sg),
+                               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, arr, 1, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, L.h3_workspace_size(ctypes.byref(d), 49840), None)
+    assert st == lib.H3_ERR_INVALID_ARG and "block 0" in lib.last_error()
+    st = L.h3_velocity_forward(ctypes.byref(d), ctypes.byref(io), ctypes.byref(w), ctypes.byref(sg),
+                               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, arr, -1, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, ws, None)
+    assert st == lib.H3_ERR_INVALID_ARG
 
 
 def test_no_device_reported(L):
