@@ -9,8 +9,9 @@ of synthetic bf16 weights (random init, H3 shapes).
 
 Printed: one JSON line with packed tokens/s per forward, the per-step kernel
 times (HIP events on the launch stream) with their TFLOP/s and fraction of the
-bf16 MFMA peak, the roofline of the dominant kernel, and the CPU oracle timed
-on a bounded sample on the host cores.
+bf16 MFMA peak, the roofline of the dominant kernel, the steps around the block
+stack (input projections, output heads) at the same segment geometry, and the
+CPU oracle timed on a bounded sample on the host cores.
 """
 from __future__ import annotations
 
@@ -102,6 +103,50 @@ def step_breakdown(lib, dims, wl_rows, table, block, reps, torch, only=None):
     out["gemms_total"] = {"ms": round(gemm_ms, 4), "tflops": round(gemm_flop / gemm_ms / 1e9, 1),
                           "mfma_frac": round(gemm_flop / gemm_ms / 1e9 / PEAK, 4)}
     return out, w
+
+
+def io_breakdown(lib, dims, io, wl, reps, torch):
+    """Per-call times of the steps around the block stack at the workload's
+    segment geometry: the whole input projection, the video patch projection
+    alone (its fp32 matrix-core rate and HBM rate), and the two output heads."""
+    V = wl.V[0] * wl.V[1] * wl.V[2]
+    inp = synth.make_io_inputs(wl, io, seed=0)
+    w_host = synth.make_io_weights(dims, io, seed=0)
+    dv = lambda a: (None if a is None or len(a) == 0 else  # noqa: E731
+                    torch.from_numpy(a.view("int16") if a.dtype.name == "uint16" else a).cuda())
+    w = {k: dv(v) for k, v in w_host.items()}
+    d = {k: dv(v) for k, v in inp.items()}
+    ftab = dv(synth.make_final_table(dims, seed=0))
+    x = torch.empty(wl.n_rows, dims.hidden, dtype=torch.float32, device="cuda")
+    xv = torch.empty(V, dims.hidden, dtype=torch.float32, device="cuda")
+    va = torch.empty(wl.A, io.audio_patch, dtype=torch.float32, device="cuda")
+    vv = torch.empty(V, io.video_patch, dtype=torch.float32, device="cuda")
+    sg = lib.segments_of(d["text"], d["cond"], d["audio"], d["video"])
+    sg_v = lib.make_segments(0, 0, 0, V)
+    ws = torch.empty(lib.heads_workspace_size(dims, sg), dtype=torch.uint8, device="cuda")
+    iw = perf_model.io_work(wl.L, wl.C, wl.A, V, dims.hidden, io.text_dim, io.video_patch,
+                            io.audio_patch)
+    calls = {
+        "embed_inputs": (lambda: lib.embed_inputs(dims, io, w, d["text"], d["cond"], d["audio"],
+                                                  d["video"], x),
+                         iw.text_flop + iw.patch_flop, None, PEAK),
+        "video_patch_embed": (lambda: lib.embed_inputs(dims, io, w, None, None, None, d["video"], xv),
+                              iw.video_patch_flop, iw.video_patch_bytes, perf_model.PEAK_FP32_MFMA_TFLOPS),
+        "final_heads": (lambda: lib.final_heads(dims, io, w, sg, x, ftab, va, vv, ws),
+                        iw.head_flop, iw.head_norm_bytes, PEAK),
+        "video_head": (lambda: lib.final_heads(dims, io, w, sg_v, x[-V:], ftab, None, vv, ws),
+                       2.0 * V * dims.hidden * io.video_patch, 6.0 * V * dims.hidden, PEAK),
+    }
+    out = {}
+    for name, (fn, flop, nbytes, peak) in calls.items():
+        ms = _time_launches(fn, reps, torch)
+        r = {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+             "peak_tflops": peak, "mfma_frac": round(flop / (ms * 1e-3) / 1e12 / peak, 4)}
+        if nbytes:
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            r.update(gbs=round(gbs, 1), hbm_frac=round(gbs / HBM, 4))
+        out[name] = r
+    return out
 
 
 def run_forward(lib, dims, rows, table, blocks, ws, steps, warmup, torch):
@@ -239,6 +284,13 @@ def main():
         "per_step_kernels": bd,
         "roofline": roofline,
     }
+    # the steps around the block stack (once per forward), at this workload's segments
+    io = synth.H3_IO
+    result["io_kernels"] = io_breakdown(lib, dims, io, wl, args.breakdown_reps, torch)
+    result["io_kernels"]["share_of_velocity_forward"] = round(
+        (result["io_kernels"]["embed_inputs"]["ms"] + result["io_kernels"]["final_heads"]["ms"])
+        / (sec * 1e3 + result["io_kernels"]["embed_inputs"]["ms"]
+           + result["io_kernels"]["final_heads"]["ms"]), 5)
     if args.secondary != "none":
         wl2 = synth.WORKLOADS[args.secondary]
         sec2, bd2, w2 = measure(wl2, args.secondary_steps, 1)

@@ -9,6 +9,10 @@ not what a particular kernel happens to move:
   attention over all N rows; softmax not counted).
 * AdaLN norm-modulate, per call: read x fp32 [N, D] and write h bf16 [N, D]
   = 6 * N * D bytes (the [T, 6, D] table is negligible and L2-resident).
+* around the block stack (once per forward): the text projection
+  2 * L * text_dim * D FLOP (bf16); each patch projection 2 * rows * P * D
+  FLOP (fp32) moving 4 * rows * (P + D) bytes; each output head a final AdaLN
+  (6 * rows * D bytes) and 2 * rows * D * P FLOP (bf16).
 
 The page "minimax-h3-mlx README", section "Performance", states the linear
 layers are about 42% of the work at 37,966 packed rows and about 20% at
@@ -54,6 +58,30 @@ def forward_flop(n: int, n_blocks: int, hidden: int, inner: int, ffn: int) -> fl
     return n_blocks * block_work(n, hidden, inner, ffn).total_flop
 
 
+@dataclass(frozen=True)
+class IoWork:
+    text_flop: float
+    patch_flop: float          # condition + audio + video projections
+    video_patch_flop: float
+    video_patch_bytes: float
+    head_flop: float           # audio + video heads
+    head_norm_bytes: float     # the two final AdaLN calls
+
+
+def io_work(L: int, C: int, A: int, V: int, hidden: int, text_dim: int, video_patch: int,
+            audio_patch: int) -> IoWork:
+    D = hidden
+    return IoWork(
+        text_flop=2.0 * L * text_dim * D,
+        patch_flop=2.0 * D * ((C + V) * video_patch + A * audio_patch),
+        video_patch_flop=2.0 * V * video_patch * D,
+        video_patch_bytes=4.0 * V * (video_patch + D),
+        head_flop=2.0 * D * (A * audio_patch + V * video_patch),
+        head_norm_bytes=6.0 * (A + V) * D,
+    )
+
+
 # MI355X published peaks (dense; AMD product specification)
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
