@@ -33,7 +33,7 @@ Readings (stated once, used everywhere):
   ~ N(0, 0.1) (variance 0.1) bf16.
 * INT8 weight-only: symmetric, groups of 32 along K, one bf16 scale per group:
   s = bf16(max|w_g| / 127) (s = 0 gives q = 0), q = clamp(round-half-even(w/s),
-  -127, 127).
+  -127, 127).  W8A8 weights: the same with one group per output row.
 """
 from __future__ import annotations
 
@@ -53,7 +53,7 @@ _TID = {
     "b_head_audio": 31, "w_head_video": 32, "b_head_video": 33, "final_table": 34,
 }
 TAG_TEXT, TAG_AUDIO, TAG_VIDEO = 0, 1, 2
-WFMT_BF16, WFMT_INT8_G32 = 0, 1
+WFMT_BF16, WFMT_INT8_G32, WFMT_W8A8 = 0, 1, 2
 
 
 @dataclasses.dataclass(frozen=True)
@@ -115,6 +115,12 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("h3_50blk_n49840", H3_DIMS, 50, 256, 1024, 200, (31, 30, 52)),
         Workload("h3_1blk_n1192_int8",
                  dataclasses.replace(H3_DIMS, wfmt=WFMT_INT8_G32), 1, 128, 0, 40, (1, 32, 32)),
+        Workload("h3_1blk_n1192_w8a8",
+                 dataclasses.replace(H3_DIMS, wfmt=WFMT_W8A8), 1, 128, 0, 40, (1, 32, 32)),
+        Workload("h3_50blk_n6437_w8a8",
+                 dataclasses.replace(H3_DIMS, wfmt=WFMT_W8A8), 50, 256, 0, 37, (6, 32, 32)),
+        Workload("h3_50blk_n49840_w8a8",
+                 dataclasses.replace(H3_DIMS, wfmt=WFMT_W8A8), 50, 256, 1024, 200, (31, 30, 52)),
     ]
 }
 
@@ -132,6 +138,21 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     r += u
     r >>= 16
     return r.astype(np.uint16)
+
+
+def quantize_int8_rows(w_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Symmetric INT8 codes with one bf16 scale per output row (the W8A8 weights).
+
+    ``w_bits`` bf16 [out, in]; returns (q int8 [out, in], s bf16 bits [out]):
+    s = bf16(max|w_row| / 127), q = clamp(round-half-even(w / s), -127, 127).
+    """
+    w = bf16_bits_to_f32(w_bits).astype(np.float64)
+    amax = np.abs(w).max(axis=1)
+    s_bits = f32_to_bf16_bits((amax / 127.0).astype(np.float32))
+    s = bf16_bits_to_f32(s_bits).astype(np.float64)[:, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s > 0, np.rint(w / np.where(s > 0, s, 1.0)), 0.0)
+    return np.clip(q, -127, 127).astype(np.int8), s_bits
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -236,7 +257,11 @@ def make_block_weights(dims: Dims, block: int, seed: int = 0,
     def one(k):
         o, i = shapes[k]
         bits = _normal_bf16(seed, block, "w_" + k, (o, i), 1.0 / i)
-        return quantize_int8_g32(bits) if dims.wfmt == WFMT_INT8_G32 else (bits, None)
+        if dims.wfmt == WFMT_INT8_G32:
+            return quantize_int8_g32(bits)
+        if dims.wfmt == WFMT_W8A8:
+            return quantize_int8_rows(bits)
+        return bits, None
 
     # independent streams per tensor: drawing them concurrently changes no value
     with ThreadPoolExecutor(max_workers=4) as ex:
@@ -364,6 +389,8 @@ def make_device_weights(dims: Dims, n_blocks: int, seed: int = 0, device: str = 
             w = torch.randn(o, i, generator=g, device=device) * float(1.0 / np.sqrt(i))
             if dims.wfmt == WFMT_INT8_G32:
                 wb["w_" + k], wb["s_" + k] = _quantize_int8_g32_torch(w.to(torch.bfloat16))
+            elif dims.wfmt == WFMT_W8A8:
+                wb["w_" + k], wb["s_" + k] = _quantize_int8_rows_torch(w.to(torch.bfloat16))
             else:
                 wb["w_" + k], wb["s_" + k] = w.to(torch.bfloat16), None
             del w
@@ -385,3 +412,14 @@ def _quantize_int8_g32_torch(w_bf16):
     q = torch.where(sf > 0, torch.round(w / torch.where(sf > 0, sf, torch.ones_like(sf))),
                     torch.zeros_like(w))
     return q.clamp_(-127, 127).to(torch.int8).view(o, i).contiguous(), s.contiguous()
+
+
+def _quantize_int8_rows_torch(w_bf16):
+    import torch
+
+    w = w_bf16.float()
+    s = (w.abs().amax(dim=1) / 127.0).to(torch.bfloat16)
+    sf = s.float().unsqueeze(-1)
+    q = torch.where(sf > 0, torch.round(w / torch.where(sf > 0, sf, torch.ones_like(sf))),
+                    torch.zeros_like(w))
+    return q.clamp_(-127, 127).to(torch.int8).contiguous(), s.contiguous()

@@ -6,8 +6,9 @@ its Python binding) never touches it.
 """
 from .h3_block import (  # noqa: F401
     MOD_NAMES, adaln_modulate, apply_rope, attention, bf16_to_f64, bias, block_forward,
-    block_steps, build_mod_table, dequant_int8_g32, dit_forward, layer_norm,
+    WFMT_W8A8, block_steps, build_mod_table, dequant_int8_g32, dit_forward, layer_norm, linear,
     merge_heads, modulation_from_table, modulation_live, qkv_split, rms_norm,
     rope_angles, round_to_bf16, silu, swiglu, weight,
 )
 from .h3_io import SEGMENTS, embed_inputs, final_heads, segment_rows, velocity_forward  # noqa: F401
+from .h3_w8a8 import linear_w8a8, quantize_rows  # noqa: F401

@@ -40,7 +40,8 @@ Readings where the pages are silent: LN and RMSNorm epsilon 1e-6; rotary base
 theta^(-2j/d_axis); softmax scale 1/sqrt(d); all biases optional (absent = 0),
 QK gains optional (absent = 1).  INT8 weight-only layers use
 W = bf16(q * s) with s one bf16 scale per 32 consecutive K elements (the GPU
-feeds the same dequantised bf16 values to its matrix cores).
+feeds the same dequantised bf16 values to its matrix cores).  W8A8 layers
+(int8 weights and activations, one scale per row) follow ``h3_w8a8``.
 """
 from __future__ import annotations
 
@@ -91,6 +92,20 @@ def weight(w: Dict[str, Optional[np.ndarray]], name: str) -> np.ndarray:
 def bias(w, name: str, n_out: int) -> np.ndarray:
     b = w.get("b_" + name)
     return np.zeros(n_out) if b is None else bf16_to_f64(b)
+
+
+WFMT_W8A8 = 2   # int8 weights with one bf16 scale per output row, activations quantized per row
+
+
+def linear(act: np.ndarray, w, name: str, n_out: int, dims) -> np.ndarray:
+    """Trunk linear ``name``: act W^T + b, or its W8A8 form (h3_w8a8) when the
+    weights are W8A8: the activation, rounded to bf16 as the bf16 path stores
+    it, is quantized per row and multiplied in integers."""
+    if getattr(dims, "wfmt", 0) == WFMT_W8A8:
+        from .h3_w8a8 import linear_w8a8, quantize_rows
+        q, s = quantize_rows(round_to_bf16(act))
+        return linear_w8a8(q, s, w["w_" + name], w["s_" + name], bias(w, name, n_out))
+    return act @ weight(w, name).T + bias(w, name, n_out)
 
 
 # ------------------------------------------------------------------ steps
@@ -256,7 +271,7 @@ def block_steps(x, tags, pos, table_b, w, dims, q_rows=None, mods=None) -> Dict[
     out: Dict[str, np.ndarray] = {}
     h = adaln_modulate(x, m["shift1"], m["scale1"], dims.ln_eps)
     out["h"] = h
-    u = h @ weight(w, "qkv").T + bias(w, "qkv", 3 * H * d)
+    u = linear(h, w, "qkv", 3 * H * d, dims)
     q, k, v = qkv_split(u, H, d)
     gq = None if w.get("q_norm") is None else bf16_to_f64(w["q_norm"])
     gk = None if w.get("k_norm") is None else bf16_to_f64(w["k_norm"])
@@ -266,14 +281,14 @@ def block_steps(x, tags, pos, table_b, w, dims, q_rows=None, mods=None) -> Dict[
     out["q"], out["k"], out["v"] = q, k, v
     o = merge_heads(attention(q, k, v, rows))
     out["o"] = o
-    xr = x[rows] + m["gate1"][rows] * (o @ weight(w, "out").T + bias(w, "out", D))
+    xr = x[rows] + m["gate1"][rows] * linear(o, w, "out", D, dims)
     out["x_mid"] = xr
     h2 = adaln_modulate(xr, m["shift2"][rows], m["scale2"][rows], dims.ln_eps)
     out["h2"] = h2
-    z = h2 @ weight(w, "fc1").T + bias(w, "fc1", 2 * F)
+    z = linear(h2, w, "fc1", 2 * F, dims)
     a = swiglu(z, F)
     out["a"] = a
-    out["x_out"] = xr + m["gate2"][rows] * (a @ weight(w, "fc2").T + bias(w, "fc2", D))
+    out["x_out"] = xr + m["gate2"][rows] * linear(a, w, "fc2", D, dims)
     return out
 
 
