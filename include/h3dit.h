@@ -63,8 +63,16 @@ typedef enum h3_status {
 
 typedef enum h3_wfmt {
   H3_W_BF16 = 0,     /* weights bf16 [out][in]                                    */
-  H3_W_INT8_G32 = 1  /* weights int8 [out][in] + bf16 scales [out][in/32]:
+  H3_W_INT8_G32 = 1, /* weights int8 [out][in] + bf16 scales [out][in/32]:
                         W = bf16(q * s), one scale per 32 consecutive K elements  */
+  H3_W_W8A8 = 2      /* W8A8: weights int8 [out][in] + one bf16 scale per output
+                        row [out]; each linear's bf16 input is quantized per row
+                        (amax = max|a|, q = clamp(rint(a * (127 / amax)), +-127),
+                        scale amax / 127, all in float32) and the product is
+                        accumulated in int32 on the int8 matrix cores:
+                        y = s_a[r] * s_w[c] * sum_k q_a q_w + b.  (mlx-h3 README,
+                        "Generate": the 200 trunk linears as group-scaled W8A8;
+                        here the group is the whole K.)                        */
 } h3_wfmt;
 
 typedef struct h3_dims {
@@ -130,6 +138,16 @@ H3DIT_API h3_status h3_dit_forward(const h3_dims* dims, float* x_packed, const i
 
 /* Message of the last error on this thread ("" if none).  Never NULL. */
 H3DIT_API const char* h3_last_error(void);
+
+/* W8A8 activation buffer: int8 codes [n_rows][width], then fp32 row scales
+ * [n_rows] at byte offset roundup(n_rows * width, 256).  Bytes it needs (pure;
+ * 0 for non-positive sizes). */
+H3DIT_API size_t h3_quantized_bytes(int64_t n_rows, int32_t width);
+
+/* Per-row int8 quantization (the H3_W_W8A8 rule) of in bf16 [n_rows][width]
+ * into the activation buffer out.  width % 8 == 0, width <= 16384. */
+H3DIT_API h3_status h3_quantize_rows(const uint16_t* in, int64_t n_rows, int32_t width, void* out,
+                                     void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Around the block stack: inputs -> packed stream -> velocity               */
@@ -221,7 +239,9 @@ H3DIT_API h3_status h3_velocity_forward(const h3_dims* dims, const h3_io_dims* i
 /* ------------------------------------------------------------------------ */
 /* Step entry points: each runs one step of the block on caller buffers.     */
 /* They are the kernels h3_dit_block_forward launches, exposed for parity   */
-/* tests and per-step timing.                                               */
+/* tests and per-step timing.  With dims->wfmt == H3_W_W8A8 the bf16         */
+/* activations below (h, h2, o, a) are W8A8 activation buffers instead       */
+/* (h3_quantized_bytes), written by h3_adaln_modulate / h3_quantize_rows.   */
 /* ------------------------------------------------------------------------ */
 
 /* Rotary table: cs fp32 [n_pad][d/2][2] = (cos, sin) of the angle of every

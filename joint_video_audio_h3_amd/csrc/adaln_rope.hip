@@ -7,7 +7,8 @@
 //   h = LN(x) * (1 + scale[tag]) + shift[tag]      -> bf16
 // (minimax-h3-mlx README, "AdaLN: measure, do not reason": x*(1+scale)+shift
 // for the norms; "AdaLN precompute": the table replaces the projection.)
-// HBM traffic per row: 4*D bytes read + 2*D bytes written.
+// HBM traffic per row: 4*D bytes read + 2*D bytes written (W8A8: the bf16
+// values are quantized per row in registers and D + 4 bytes are written).
 //
 // rope_kernel: cos/sin of pos[r][axis] * theta^(-2j/d_axis) for every channel
 // pair, evaluated in double precision once per forward (3D MM-RoPE,
@@ -17,7 +18,24 @@
 
 namespace h3 {
 
-template <int VPL>  // float4 vectors per lane: ceil(D / 256)
+// Per-row symmetric int8 codes (W8A8 activations), in float32 exactly as
+// specified: amax = max|v|, inv = 127 / amax, q = clamp(rint(v * inv), +-127),
+// scale = amax / 127 (IEEE divisions, rint ties to even; amax = 0 gives 0, 0).
+__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float inv) {
+  auto one = [&](float v) -> uint32_t {
+    const float t = fminf(fmaxf(__builtin_rintf(v * inv), -127.0f), 127.0f);
+    return (uint32_t)((int)t & 0xff);
+  };
+  return one(a) | (one(b) << 8) | (one(c) << 16) | (one(d) << 24);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+template <int VPL, bool Q>  // float4 vectors per lane: ceil(D / 256); Q: int8 output
 __global__ __launch_bounds__(256) void adaln_kernel(AdalnArgs a) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -52,6 +70,7 @@ __global__ __launch_bounds__(256) void adaln_kernel(AdalnArgs a) {
   const u16x4* sh = reinterpret_cast<const u16x4*>(a.table + ((size_t)t * 6 + a.k_shift) * a.D);
   const u16x4* sc = reinterpret_cast<const u16x4*>(a.table + ((size_t)t * 6 + a.k_scale) * a.D);
   uint2* hr = reinterpret_cast<uint2*>(a.h + (size_t)row * a.D);
+  float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int j = lane + 64 * i;
@@ -61,13 +80,70 @@ __global__ __launch_bounds__(256) void adaln_kernel(AdalnArgs a) {
       const float o1 = (v[i].y - mean) * rstd * (1.0f + bf2f(c4[1])) + bf2f(s4[1]);
       const float o2 = (v[i].z - mean) * rstd * (1.0f + bf2f(c4[2])) + bf2f(s4[2]);
       const float o3 = (v[i].w - mean) * rstd * (1.0f + bf2f(c4[3])) + bf2f(s4[3]);
-      hr[j] = make_uint2(pack2bf(o0, o1), pack2bf(o2, o3));
+      const uint32_t p01 = pack2bf(o0, o1), p23 = pack2bf(o2, o3);
+      if constexpr (Q) {
+        // keep the bf16 values (as floats) for the row's int8 codes
+        v[i] = make_float4(__uint_as_float(p01 << 16), __uint_as_float(p01 & 0xffff0000u),
+                           __uint_as_float(p23 << 16), __uint_as_float(p23 & 0xffff0000u));
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+      } else {
+        hr[j] = make_uint2(p01, p23);
+      }
     }
+  }
+  if constexpr (Q) {
+    amax = wave_max(amax);
+    const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+    uint32_t* qr = reinterpret_cast<uint32_t*>(a.hq + (size_t)row * a.D);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int j = lane + 64 * i;
+      if (j < nv) qr[j] = quant4(v[i].x, v[i].y, v[i].z, v[i].w, inv);
+    }
+    if (lane == 0) a.hs[row] = amax > 0.f ? amax / 127.0f : 0.f;
   }
 }
 
-#define H3_ADALN_CASE(V) \
-  case V: adaln_kernel<V><<<grid, 256, 0, s>>>(a); break;
+// One wavefront per row: the bf16 row stays in registers (8 values per 16-byte
+// piece), its absolute maximum is a wavefront reduction, then the codes go out
+// 8 bytes per piece.  HBM traffic per row: 2*K bytes read, K + 4 written.
+template <int VPL>  // 16-byte pieces per lane: ceil(K / 512)
+__global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.n) return;
+  const int nv = a.K >> 3;
+  const uint4* src = reinterpret_cast<const uint4*>(a.in + (size_t)row * a.K);
+  uint4 v[VPL];
+  float amax = 0.f;
+  auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+  auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int j = lane + 64 * i;
+    v[i] = j < nv ? src[j] : make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) amax = fmaxf(amax, fmaxf(fabsf(lo(w[t])), fabsf(hi(w[t]))));
+  }
+  amax = wave_max(amax);
+  const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+  uint2* dst = reinterpret_cast<uint2*>(a.q + (size_t)row * a.K);
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int j = lane + 64 * i;
+    if (j < nv)
+      dst[j] = make_uint2(quant4(lo(v[i].x), hi(v[i].x), lo(v[i].y), hi(v[i].y), inv),
+                          quant4(lo(v[i].z), hi(v[i].z), lo(v[i].w), hi(v[i].w), inv));
+  }
+  if (lane == 0) a.s[row] = amax > 0.f ? amax / 127.0f : 0.f;
+}
+
+#define H3_ADALN_CASE(V)                                                \
+  case V:                                                               \
+    if (a.hq) adaln_kernel<V, true><<<grid, 256, 0, s>>>(a);            \
+    else adaln_kernel<V, false><<<grid, 256, 0, s>>>(a);                \
+    break;
 
 hipError_t launch_adaln(const AdalnArgs& a, hipStream_t s) {
   const int vpl = (a.D / 4 + 63) / 64;
@@ -81,6 +157,27 @@ hipError_t launch_adaln(const AdalnArgs& a, hipStream_t s) {
     H3_ADALN_CASE(21) H3_ADALN_CASE(22) H3_ADALN_CASE(23) H3_ADALN_CASE(24)
     H3_ADALN_CASE(25) H3_ADALN_CASE(26) H3_ADALN_CASE(27) H3_ADALN_CASE(28)
     H3_ADALN_CASE(29) H3_ADALN_CASE(30) H3_ADALN_CASE(31) H3_ADALN_CASE(32)
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+#define H3_QUANT_CASE(V) \
+  case V: quant_rows_kernel<V><<<grid, 256, 0, s>>>(a); break;
+
+hipError_t launch_quant_rows(const QuantArgs& a, hipStream_t s) {
+  if (a.K % 8 != 0) return hipErrorInvalidValue;
+  const int vpl = (a.K / 8 + 63) / 64;
+  const dim3 grid((a.n + 3) / 4);
+  switch (vpl) {
+    H3_QUANT_CASE(1) H3_QUANT_CASE(2) H3_QUANT_CASE(3) H3_QUANT_CASE(4)
+    H3_QUANT_CASE(5) H3_QUANT_CASE(6) H3_QUANT_CASE(7) H3_QUANT_CASE(8)
+    H3_QUANT_CASE(9) H3_QUANT_CASE(10) H3_QUANT_CASE(11) H3_QUANT_CASE(12)
+    H3_QUANT_CASE(13) H3_QUANT_CASE(14) H3_QUANT_CASE(15) H3_QUANT_CASE(16)
+    H3_QUANT_CASE(17) H3_QUANT_CASE(18) H3_QUANT_CASE(19) H3_QUANT_CASE(20)
+    H3_QUANT_CASE(21) H3_QUANT_CASE(22) H3_QUANT_CASE(23) H3_QUANT_CASE(24)
+    H3_QUANT_CASE(25) H3_QUANT_CASE(26) H3_QUANT_CASE(27) H3_QUANT_CASE(28)
+    H3_QUANT_CASE(29) H3_QUANT_CASE(30) H3_QUANT_CASE(31) H3_QUANT_CASE(32)
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

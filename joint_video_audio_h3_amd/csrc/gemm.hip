@@ -410,7 +410,34 @@ __device__ __forceinline__ int weight_row_base(int tn) {
 template <int V>
 using ic = std::integral_constant<int, V>;
 
-template <int EPI, int SEC, int BN>
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+// W8A8 (I8): int32 accumulators from v_mfma_i32_32x32x32_i8 become
+// float(acc) * s_a[row] * s_w[col] before the epilogue; every other step is the
+// bf16 kernel's, since a 16-byte fragment holds 32 int8 values of K where it
+// held 16 bf16 ones (same LDS layout, same loads, twice the K per stage).
+template <int EPI, int BN, int TN, int FM, int FN>
+__device__ __forceinline__ void scale_int_acc(const GemmArgs& p, f32x16 (&acc)[FM][FN], int tn,
+                                              int row0, int wn, int lane) {
+  const int hl = lane >> 5, lc = lane & 31;
+  float sw[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) sw[j] = bf2f(p.Bs[weight_row<EPI, BN, TN>(p, tn, wn * TN + j * 32 + lc)]);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    f32x16 sr;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sr[v] = p.sa[min(row0 + i * 32 + 8 * (v / 4) + 4 * hl + (v % 4), p.M - 1)];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const f32x16 f = __builtin_convertvector(__builtin_bit_cast(i32x16, acc[i][j]), f32x16);
+      acc[i][j] = f * sr * sw[j];
+    }
+  }
+}
+
+template <int EPI, int SEC, int BN, bool I8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_direct_kernel(GemmArgs p) {
   constexpr int BM = 256, WM = 2, WN = 2;
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -430,7 +457,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const TileCoord tc = tile_coord<EPI, BM, BN>(p);
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
   const int K = p.K;
-  const uint32_t rowb = (uint32_t)K * 2;
+  const uint32_t rowb = (uint32_t)K * (I8 ? 1 : 2);
 
   // Loads: wave-uniform tile bases (SGPRs) advanced 128 B per stage, plus
   // per-lane 32-bit offsets fixed for the whole K loop.  Load s of a half
@@ -503,7 +530,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
   auto mfma_range = [&](const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN], int q0, int q1) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = q0; q < q1; ++q) acc[q / FN][q % FN] = mfma32(fa[q / FN], fb[q % FN], acc[q / FN][q % FN]);
+    for (int q = q0; q < q1; ++q) {
+      f32x16& c = acc[q / FN][q % FN];
+      if constexpr (I8) {
+        c = __builtin_bit_cast(f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                __builtin_bit_cast(i32x4, fa[q / FN]), __builtin_bit_cast(i32x4, fb[q % FN]),
+                __builtin_bit_cast(i32x16, c), 0, 0, 0));
+      } else {
+        c = mfma32(fa[q / FN], fb[q % FN], c);
+      }
+    }
   };
   // One k step: the next k step's fragment reads go behind its first MFMA, and
   // the group's loads are spread one part per MFMA quarter (a burst of loads
@@ -554,7 +590,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // the same step with slots from the runtime phase and loads only where the
   // stage exists (the last few stages of the K loop)
-  const int KT = K / DBK;
+  const int KT = K / (I8 ? 2 * DBK : DBK);   // stages of 128 bytes per row
   auto step_rt = [&](int kt) __attribute__((always_inline)) {
     const uint32_t oa = (uint32_t)((2 * kt) % 5) * HSLOT, ob = (uint32_t)((2 * kt + 1) % 5) * HSLOT;
     const uint32_t oa1 = (uint32_t)((2 * kt + 2) % 5) * HSLOT, ob1 = (uint32_t)((2 * kt + 3) % 5) * HSLOT;
@@ -634,6 +670,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   for (; kt < KT; ++kt) step_rt(kt);
   __syncthreads();
+  if constexpr (I8) scale_int_acc<EPI, BN, TN, FM, FN>(p, acc, tc.tn, m0 + wm * TM, wn, lane);
   if constexpr (EPI == EPI_RESID) {
     // the tile's row tags go to LDS past the four staging areas (the ring is free now)
     int* s_tag = reinterpret_cast<int*>(ring + 4 * 32 * RSTRIDE * sizeof(float));
@@ -848,9 +885,9 @@ static dim3 grid_for(int epi, const GemmArgs& a) {
   return dim3(tiles_m * tiles_n);
 }
 
-template <int EPI, int SEC, int BN>
+template <int EPI, int SEC, int BN, bool I8 = false>
 static hipError_t run_direct(const GemmArgs& a, hipStream_t s) {
-  gemm_direct_kernel<EPI, SEC, BN><<<grid_for<256, BN>(EPI, a), 256, 0, s>>>(a);
+  gemm_direct_kernel<EPI, SEC, BN, I8><<<grid_for<256, BN>(EPI, a), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -887,7 +924,19 @@ static bool resid_prefers_192(const GemmArgs& a) {
 
 hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
   if (a.K % 64 != 0) return hipErrorInvalidValue;
-  if (wfmt != 0 && a.K % 128 != 0) return hipErrorInvalidValue;   // INT8: an even number of stages
+  if (wfmt != 0 && a.K % 128 != 0) return hipErrorInvalidValue;   // INT8: 128-element stages
+  if (wfmt == 2) {   // W8A8: int8 activations and weights, per-row scales
+    switch (epi) {
+      case EPI_RESID:
+        if (resid_prefers_192(a)) return run_direct<EPI_RESID, 0, 192, true>(a, s);
+        return run_direct<EPI_RESID, 0, 256, true>(a, s);
+      case EPI_SWIGLU: return run_direct<EPI_SWIGLU, 0, 256, true>(a, s);
+      case EPI_QKV:
+        if (a.head_dim == 128) return run_direct<EPI_QKV, 128, 256, true>(a, s);
+        if (a.head_dim == 96) return run_direct<EPI_QKV, 96, 192, true>(a, s);
+    }
+    return hipErrorInvalidValue;
+  }
   if (wfmt == 0) {
     switch (epi) {
       case EPI_RESID:

@@ -51,7 +51,7 @@ h3_status check_dims(const h3_dims* d) {
     return fail(H3_ERR_UNSUPPORTED, "ffn=%d, hidden=%d: (ffn + 256) * hidden * 2 must be below 2^32",
                 d->ffn, d->hidden);
   if (d->n_tags > 8) return fail(H3_ERR_UNSUPPORTED, "n_tags=%d: at most 8", d->n_tags);
-  if (d->wfmt == H3_W_INT8_G32 && (d->heads * d->head_dim) % 128 != 0)
+  if (d->wfmt != H3_W_BF16 && (d->heads * d->head_dim) % 128 != 0)
     return fail(H3_ERR_UNSUPPORTED, "INT8 weights need heads*head_dim=%d to be a multiple of 128",
                 d->heads * d->head_dim);
   int sum = 0;
@@ -65,7 +65,7 @@ h3_status check_dims(const h3_dims* d) {
   if (!(d->rope_theta > 0.f) || !(d->ln_eps >= 0.f) || !(d->qk_eps >= 0.f) ||
       !std::isfinite(d->rope_theta))
     return fail(H3_ERR_INVALID_ARG, "rope_theta must be > 0 and epsilons >= 0");
-  if (d->wfmt != H3_W_BF16 && d->wfmt != H3_W_INT8_G32)
+  if (d->wfmt != H3_W_BF16 && d->wfmt != H3_W_INT8_G32 && d->wfmt != H3_W_W8A8)
     return fail(H3_ERR_INVALID_ARG, "wfmt=%d unknown", d->wfmt);
   return H3_OK;
 }
@@ -88,7 +88,7 @@ h3_status check_rows(int64_t n) {
 h3_status check_linear(const h3_dims* d, const void* w, const uint16_t* s, const uint16_t* b,
                        const char* wn, const char* sn, const char* bn) {
   H3_NEED(w, wn);
-  if (d->wfmt == H3_W_INT8_G32) H3_NEED(s, sn);
+  if (d->wfmt != H3_W_BF16) H3_NEED(s, sn);
   H3_OPT(b, bn);
   return H3_OK;
 }
@@ -131,6 +131,8 @@ h3_status hip_ok(hipError_t e, const char* what) {
 struct Arena {
   float* cs;
   uint16_t *h, *q, *k, *vt, *o, *a;
+  int8_t* qa;   // W8A8: int8 codes of o, then of a (h's codes live in h)
+  float* qs;    // W8A8: the row scales of the activation being consumed
   size_t bytes;
 };
 
@@ -159,9 +161,19 @@ Arena carve(const h3_dims& d, int64_t n, char* base) {
   a.vt = reinterpret_cast<uint16_t*>(qkv ? qkv + 2 * up256(head_buf) : nullptr);
   a.a = reinterpret_cast<uint16_t*>(qkv);
   a.o = reinterpret_cast<uint16_t*>(take(np * Di * 2));
+  if (d.wfmt == H3_W_W8A8) {
+    // W8A8 activation codes: h's in the h arena; o's and a's (consecutive
+    // lifetimes) here; one scale vector at a time
+    a.qa = reinterpret_cast<int8_t*>(take(np * std::max(Di, F)));
+    a.qs = reinterpret_cast<float*>(take(np * 4));
+  }
   a.bytes = off;
   return a;
 }
+
+// W8A8 activation buffer of the step entry points: codes [n][K], then the fp32
+// row scales at byte offset roundup(n*K, 256).
+size_t qa_scale_offset(int64_t n, int64_t K) { return up256((size_t)n * (size_t)K); }
 
 // ---------------------------------------------------------------- launches
 h3::GemmArgs gemm_base(const h3_dims& d, const uint16_t* A, const void* B, const uint16_t* Bs,
@@ -192,12 +204,15 @@ hipError_t do_rope(const h3_dims& d, const float* pos, int64_t n, float* cs, hip
 }
 
 hipError_t do_adaln(const h3_dims& d, const float* x, const int32_t* tag, const uint16_t* table,
-                    int which, int64_t n, uint16_t* h, hipStream_t s) {
+                    int which, int64_t n, uint16_t* h, hipStream_t s, int8_t* hq = nullptr,
+                    float* hs = nullptr) {
   h3::AdalnArgs a{};
   a.x = x;
   a.tag = tag;
   a.table = table;
   a.h = h;
+  a.hq = hq;
+  a.hs = hs;
   a.n = (int)n;
   a.D = d.hidden;
   a.k_shift = 3 * which;
@@ -206,10 +221,23 @@ hipError_t do_adaln(const h3_dims& d, const float* x, const int32_t* tag, const 
   return h3::launch_adaln(a, s);
 }
 
+hipError_t do_quant(const uint16_t* in, int64_t n, int K, int8_t* q, float* sc, hipStream_t s) {
+  h3::QuantArgs a{};
+  a.in = in;
+  a.q = q;
+  a.s = sc;
+  a.n = (int)n;
+  a.K = K;
+  return h3::launch_quant_rows(a, s);
+}
+
+// sa: the W8A8 row scales of the int8 activation h (ignored otherwise)
 hipError_t do_qkv(const h3_dims& d, const uint16_t* h, const h3_block_weights& w, const float* cs,
-                  int64_t n, uint16_t* q, uint16_t* k, uint16_t* vt, hipStream_t s) {
+                  int64_t n, uint16_t* q, uint16_t* k, uint16_t* vt, hipStream_t s,
+                  const float* sa = nullptr) {
   const int Di = d.heads * d.head_dim;
   h3::GemmArgs g = gemm_base(d, h, w.w_qkv, w.s_qkv, w.b_qkv, (int)n, d.hidden, 3 * Di);
+  g.sa = sa;
   g.q = q;
   g.k = k;
   g.vt = vt;
@@ -240,8 +268,9 @@ hipError_t do_attn(const h3_dims& d, const uint16_t* q, const uint16_t* k, const
 
 hipError_t do_resid(const h3_dims& d, const uint16_t* A, const void* W, const uint16_t* S,
                     const uint16_t* b, int K, const uint16_t* table, int kgate, const int32_t* tag,
-                    int64_t n, float* x, hipStream_t s) {
+                    int64_t n, float* x, hipStream_t s, const float* sa = nullptr) {
   h3::GemmArgs g = gemm_base(d, A, W, S, b, (int)n, K, d.hidden);
+  g.sa = sa;
   g.x = x;
   g.ldx = d.hidden;
   g.gate_tab = table + (size_t)kgate * d.hidden;
@@ -251,15 +280,44 @@ hipError_t do_resid(const h3_dims& d, const uint16_t* A, const void* W, const ui
 }
 
 hipError_t do_fc1(const h3_dims& d, const uint16_t* h2, const h3_block_weights& w, int64_t n,
-                  uint16_t* a, hipStream_t s) {
+                  uint16_t* a, hipStream_t s, const float* sa = nullptr) {
   h3::GemmArgs g = gemm_base(d, h2, w.w_fc1, w.s_fc1, w.b_fc1, (int)n, d.hidden, 2 * d.ffn);
+  g.sa = sa;
   g.out = a;
   g.ffn = d.ffn;
   return h3::launch_gemm(h3::EPI_SWIGLU, d.wfmt, g, s);
 }
 
+// W8A8 block: each linear's input is quantized per row right after it is made
+// (AdaLN writes the codes directly; o and a go through the row quantizer).
+h3_status run_block_w8a8(const h3_dims& d, float* x, const int32_t* tag, const uint16_t* table,
+                         const h3_block_weights& w, int64_t n, const Arena& ar, hipStream_t s) {
+  const int Di = d.heads * d.head_dim;
+  const uint16_t* hq = reinterpret_cast<const uint16_t*>(ar.h);      // int8 codes in the h arena
+  const uint16_t* qa = reinterpret_cast<const uint16_t*>(ar.qa);
+  int8_t* hq_w = reinterpret_cast<int8_t*>(ar.h);
+  h3_status st;
+  if ((st = hip_ok(do_adaln(d, x, tag, table, 0, n, nullptr, s, hq_w, ar.qs), "adaln (attention)")) != H3_OK)
+    return st;
+  if ((st = hip_ok(do_qkv(d, hq, w, ar.cs, n, ar.q, ar.k, ar.vt, s, ar.qs), "qkv+rope")) != H3_OK) return st;
+  if ((st = hip_ok(do_attn(d, ar.q, ar.k, ar.vt, n, ar.o, s), "attention")) != H3_OK) return st;
+  if ((st = hip_ok(do_quant(ar.o, n, Di, ar.qa, ar.qs, s), "quantize o")) != H3_OK) return st;
+  if ((st = hip_ok(do_resid(d, qa, w.w_out, w.s_out, w.b_out, Di, table, 2, tag, n, x, s, ar.qs),
+                   "out-proj+gate")) != H3_OK)
+    return st;
+  if ((st = hip_ok(do_adaln(d, x, tag, table, 1, n, nullptr, s, hq_w, ar.qs), "adaln (mlp)")) != H3_OK)
+    return st;
+  if ((st = hip_ok(do_fc1(d, hq, w, n, ar.a, s, ar.qs), "fc1+swiglu")) != H3_OK) return st;
+  if ((st = hip_ok(do_quant(ar.a, n, d.ffn, ar.qa, ar.qs, s), "quantize a")) != H3_OK) return st;
+  if ((st = hip_ok(do_resid(d, qa, w.w_fc2, w.s_fc2, w.b_fc2, d.ffn, table, 5, tag, n, x, s, ar.qs),
+                   "fc2+gate")) != H3_OK)
+    return st;
+  return H3_OK;
+}
+
 h3_status run_block(const h3_dims& d, float* x, const int32_t* tag, const uint16_t* table,
                     const h3_block_weights& w, int64_t n, const Arena& ar, hipStream_t s) {
+  if (d.wfmt == H3_W_W8A8) return run_block_w8a8(d, x, tag, table, w, n, ar, s);
   const int Di = d.heads * d.head_dim;
   h3_status st;
   if ((st = hip_ok(do_adaln(d, x, tag, table, 0, n, ar.h, s), "adaln (attention)")) != H3_OK) return st;
@@ -431,11 +489,39 @@ h3_status run_heads(const h3_dims& d, const h3_io_dims& io, const h3_io_weights&
   return H3_OK;
 }
 
+// Row scales of a step entry point's activation buffer (W8A8), else null.
+const float* act_scales(const h3_dims& d, const void* act, int64_t n, int64_t K) {
+  if (d.wfmt != H3_W_W8A8) return nullptr;
+  return reinterpret_cast<const float*>(static_cast<const char*>(act) + qa_scale_offset(n, K));
+}
+
 }  // namespace
 
 extern "C" {
 
 int64_t h3_padded_rows(int64_t n_rows) { return n_rows <= 0 ? 0 : pad_rows(n_rows); }
+
+size_t h3_quantized_bytes(int64_t n_rows, int32_t width) {
+  if (n_rows <= 0 || width <= 0) return 0;
+  return qa_scale_offset(n_rows, width) + up256((size_t)n_rows * 4);
+}
+
+h3_status h3_quantize_rows(const uint16_t* in, int64_t n_rows, int32_t width, void* out,
+                           void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_rows(n_rows)) != H3_OK) return st;
+  if (width <= 0 || width % 8 != 0 || width > 16384)
+    return fail(H3_ERR_UNSUPPORTED, "width=%d: need a positive multiple of 8, at most 16384", width);
+  H3_NEED(in, "in");
+  H3_NEED(out, "out");
+  if ((st = check_device()) != H3_OK) return st;
+  char* base = static_cast<char*>(out);
+  return hip_ok(do_quant(in, n_rows, width, reinterpret_cast<int8_t*>(base),
+                         reinterpret_cast<float*>(base + qa_scale_offset(n_rows, width)),
+                         reinterpret_cast<hipStream_t>(stream)),
+                "quantize rows");
+}
 
 size_t h3_workspace_size(const h3_dims* dims, int64_t n_rows) {
   if (check_dims(dims) != H3_OK || check_rows(n_rows) != H3_OK) return 0;
@@ -516,6 +602,13 @@ h3_status h3_adaln_modulate(const h3_dims* dims, const float* x, const int32_t* 
   H3_NEED(h, "h");
   if (which != 0 && which != 1) return fail(H3_ERR_INVALID_ARG, "which=%d must be 0 or 1", which);
   if ((st = check_device()) != H3_OK) return st;
+  if (dims->wfmt == H3_W_W8A8) {   // h is a W8A8 activation buffer
+    char* base = reinterpret_cast<char*>(h);
+    return hip_ok(do_adaln(*dims, x, tag, mod_table, which, n_rows, nullptr,
+                           reinterpret_cast<hipStream_t>(stream), reinterpret_cast<int8_t*>(base),
+                           reinterpret_cast<float*>(base + qa_scale_offset(n_rows, dims->hidden))),
+                  "adaln");
+  }
   return hip_ok(do_adaln(*dims, x, tag, mod_table, which, n_rows, h,
                          reinterpret_cast<hipStream_t>(stream)),
                 "adaln");
@@ -534,7 +627,8 @@ h3_status h3_qkv_rope(const h3_dims* dims, const uint16_t* h, const h3_block_wei
   H3_NEED(k, "k");
   H3_NEED(vt, "vt");
   if ((st = check_device()) != H3_OK) return st;
-  return hip_ok(do_qkv(*dims, h, *weights, cs, n_rows, q, k, vt, reinterpret_cast<hipStream_t>(stream)),
+  return hip_ok(do_qkv(*dims, h, *weights, cs, n_rows, q, k, vt, reinterpret_cast<hipStream_t>(stream),
+                       act_scales(*dims, h, n_rows, dims->hidden)),
                 "qkv+rope");
 }
 
@@ -566,7 +660,8 @@ h3_status h3_out_proj_residual(const h3_dims* dims, const uint16_t* o,
   if ((st = check_device()) != H3_OK) return st;
   return hip_ok(do_resid(*dims, o, weights->w_out, weights->s_out, weights->b_out,
                          dims->heads * dims->head_dim, mod_table, 2, tag, n_rows, x,
-                         reinterpret_cast<hipStream_t>(stream)),
+                         reinterpret_cast<hipStream_t>(stream),
+                         act_scales(*dims, o, n_rows, dims->heads * dims->head_dim)),
                 "out-proj+gate");
 }
 
@@ -579,7 +674,8 @@ h3_status h3_mlp_fc1_swiglu(const h3_dims* dims, const uint16_t* h2, const h3_bl
   H3_NEED(h2, "h2");
   H3_NEED(a, "a");
   if ((st = check_device()) != H3_OK) return st;
-  return hip_ok(do_fc1(*dims, h2, *weights, n_rows, a, reinterpret_cast<hipStream_t>(stream)),
+  return hip_ok(do_fc1(*dims, h2, *weights, n_rows, a, reinterpret_cast<hipStream_t>(stream),
+                       act_scales(*dims, h2, n_rows, dims->hidden)),
                 "fc1+swiglu");
 }
 
@@ -596,7 +692,8 @@ h3_status h3_mlp_fc2_residual(const h3_dims* dims, const uint16_t* a,
   H3_NEED(x, "x");
   if ((st = check_device()) != H3_OK) return st;
   return hip_ok(do_resid(*dims, a, weights->w_fc2, weights->s_fc2, weights->b_fc2, dims->ffn,
-                         mod_table, 5, tag, n_rows, x, reinterpret_cast<hipStream_t>(stream)),
+                         mod_table, 5, tag, n_rows, x, reinterpret_cast<hipStream_t>(stream),
+                         act_scales(*dims, a, n_rows, dims->ffn)),
                 "fc2+gate");
 }
 

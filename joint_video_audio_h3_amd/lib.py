@@ -78,6 +78,8 @@ _SIGS = {
     "h3_mlp_fc2_residual": (c_i32, [ctypes.POINTER(H3Dims), c_vp, ctypes.POINTER(H3BlockWeights),
                                     c_vp, c_vp, c_i64, c_vp, c_vp]),
     "h3_heads_workspace_size": (c_sz, [_PD, _PSG]),
+    "h3_quantized_bytes": (c_sz, [c_i64, c_i32]),
+    "h3_quantize_rows": (c_i32, [c_vp, c_i64, c_i32, c_vp, c_vp]),
     "h3_embed_inputs": (c_i32, [_PD, _PIO, _PW, _PSG, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "h3_final_heads": (c_i32, [_PD, _PIO, _PW, _PSG, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "h3_velocity_forward": (c_i32, [_PD, _PIO, _PW, _PSG, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
@@ -205,9 +207,11 @@ def out_proj_residual(dims, o, block, mod_table, tag, x, stream=None):
 
 
 def mlp_fc1_swiglu(dims, h2, block, a, stream=None):
+    """a [n, F] <- SwiGLU(h2 W_fc1^T + b).  The row count is a's (h2 may be a
+    flat W8A8 activation buffer)."""
     w = make_weights(block)
     _check(load().h3_mlp_fc1_swiglu(ctypes.byref(make_dims(dims)), h2.data_ptr(), ctypes.byref(w),
-                                    h2.shape[0], a.data_ptr(), _stream(stream)))
+                                    a.shape[0], a.data_ptr(), _stream(stream)))
 
 
 def mlp_fc2_residual(dims, a, block, mod_table, tag, x, stream=None):
@@ -215,6 +219,15 @@ def mlp_fc2_residual(dims, a, block, mod_table, tag, x, stream=None):
     _check(load().h3_mlp_fc2_residual(ctypes.byref(make_dims(dims)), a.data_ptr(), ctypes.byref(w),
                                       mod_table.data_ptr(), tag.data_ptr(), x.shape[0],
                                       x.data_ptr(), _stream(stream)))
+
+
+def quantized_bytes(n_rows: int, width: int) -> int:
+    return load().h3_quantized_bytes(n_rows, width)
+
+
+def quantize_rows(x, out, stream=None):
+    """W8A8 activation buffer ``out`` (uint8, quantized_bytes) <- per-row int8 codes of bf16 x."""
+    _check(load().h3_quantize_rows(x.data_ptr(), x.shape[0], x.shape[1], out.data_ptr(), _stream(stream)))
 
 
 def make_io_dims(io) -> H3IoDims:
