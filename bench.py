@@ -105,6 +105,56 @@ def step_breakdown(lib, dims, wl_rows, table, block, reps, torch, only=None):
     return out, w
 
 
+def step_breakdown_w8a8(lib, dims, wl_rows, table, block, reps, torch):
+    """Per-kernel times of one W8A8 block's steps (int8 GEMMs against the int8 peak)."""
+    x, tags, pos = wl_rows
+    n = x.shape[0]
+    D, Di, F, H, d = dims.hidden, dims.inner, dims.ffn, dims.heads, dims.head_dim
+    np_ = lib.padded_rows(n)
+    dev = x.device
+    cs = torch.empty(np_, d // 2, 2, dtype=torch.float32, device=dev)
+    hq = torch.empty(lib.quantized_bytes(n, D), dtype=torch.uint8, device=dev)
+    q = torch.empty(H, np_, d, dtype=torch.int16, device=dev)
+    k = torch.empty_like(q)
+    vt = torch.empty(H, d, np_, dtype=torch.int16, device=dev)
+    o = torch.empty(n, Di, dtype=torch.int16, device=dev)
+    oq = torch.empty(lib.quantized_bytes(n, Di), dtype=torch.uint8, device=dev)
+    a = torch.empty(n, F, dtype=torch.int16, device=dev)
+    aq = torch.empty(lib.quantized_bytes(n, F), dtype=torch.uint8, device=dev)
+    xs = x.clone()
+    t0 = table[0]
+    lib.rope_table(dims, pos, n, cs)
+    w = perf_model.block_work(n, D, Di, F)
+    I8 = perf_model.PEAK_INT8_TOPS
+    steps = {
+        "adaln_quant": (lambda: lib.adaln_modulate(dims, xs, tags, t0, 0, hq), None, 4.0 * n * D + n * D, None),
+        "qkv_rope": (lambda: lib.qkv_rope(dims, hq, block, cs, n, q, k, vt), w.qkv_flop, None, I8),
+        "attention": (lambda: lib.attention(dims, q, k, vt, n, o), w.attn_flop, None, PEAK),
+        "quant_o": (lambda: lib.quantize_rows(o, oq), None, 3.0 * n * Di, None),
+        "out_proj_resid": (lambda: lib.out_proj_residual(dims, oq, block, t0, tags, xs), w.out_flop, None, I8),
+        "fc1_swiglu": (lambda: lib.mlp_fc1_swiglu(dims, hq, block, a), w.fc1_flop, None, I8),
+        "quant_a": (lambda: lib.quantize_rows(a, aq), None, 3.0 * n * F, None),
+        "fc2_resid": (lambda: lib.mlp_fc2_residual(dims, aq, block, t0, tags, xs), w.fc2_flop, None, I8),
+    }
+    out = {}
+    for name, (fn, flop, nbytes, peak) in steps.items():
+        ms = _time_launches(fn, reps, torch)
+        r = {"ms": round(ms, 4)}
+        if flop:
+            tf = flop / (ms * 1e-3) / 1e12
+            r.update(tops=round(tf, 1), peak=peak, mfma_frac=round(tf / peak, 4))
+        if nbytes:
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            r.update(gbs=round(gbs, 1), hbm_frac=round(gbs / HBM, 4))
+        out[name] = r
+    lin = ("qkv_rope", "out_proj_resid", "fc1_swiglu", "fc2_resid")
+    gemm_ms = sum(out[s_]["ms"] for s_ in lin)
+    out["gemms_total"] = {"ms": round(gemm_ms, 4), "tops": round(w.linear_flop / gemm_ms / 1e9, 1),
+                          "peak": I8, "mfma_frac": round(w.linear_flop / gemm_ms / 1e9 / I8, 4),
+                          "bf16_frac_equiv": round(w.linear_flop / gemm_ms / 1e9 / PEAK, 4)}
+    return out, w
+
+
 def io_breakdown(lib, dims, io, wl, reps, torch):
     """Per-call times of the steps around the block stack at the workload's
     segment geometry: the whole input projection, the video patch projection
@@ -212,6 +262,8 @@ def main():
                          "the known-size reference for HBM byte counters")
     ap.add_argument("--single-block", type=int, default=1,
                     help="also time one H3 block at N=1192 with bf16 and INT8 weights (0: skip)")
+    ap.add_argument("--w8a8", type=int, default=1,
+                    help="also run the forwards with the W8A8 trunk (0: skip)")
     ap.add_argument("--only-step", default=None,
                     help="time just one step kernel (adaln, qkv_rope, attention, out_proj_resid, "
                          "fc1_swiglu, fc2_resid) on one block's weights, e.g. under a counter run")
@@ -302,6 +354,35 @@ def main():
             "forward_mfma_frac": round(wl2.n_blocks * w2.total_flop / sec2 / 1e12 / PEAK, 4),
             "per_step_kernels": bd2,
         }
+    if args.w8a8:
+        # the same forwards with the W8A8 trunk (int8 weights and activations,
+        # per-row scales) on the int8 matrix cores
+        del table, blocks
+        torch.cuda.empty_cache()
+        result["w8a8"] = {}
+        names = [args.workload] + ([args.secondary] if args.secondary != "none" else [])
+        dims8 = synth.WORKLOADS[names[0] + "_w8a8"].dims
+        log("generating 50 blocks of W8A8 weights on the device")
+        table8, blocks8 = synth.make_device_weights(dims8, wl.n_blocks, seed=0)
+        for nm in names:
+            wl8 = synth.WORKLOADS[nm + "_w8a8"]
+            rows = synth.make_device_rows(wl8, seed=0)
+            ws = lib.alloc_workspace(dims8, wl8.n_rows)
+            steps8 = args.steps if nm == args.workload else args.secondary_steps
+            sec8 = run_forward(lib, dims8, rows, table8[:wl8.n_blocks], blocks8[:wl8.n_blocks], ws,
+                               steps8, 1, torch)
+            log(f"{wl8.name}: {sec8 * 1e3:.1f} ms per forward")
+            del ws
+            bd8, w8 = step_breakdown_w8a8(lib, dims8, synth.make_device_rows(wl8, seed=1), table8,
+                                          blocks8[0], args.breakdown_reps, torch)
+            result["w8a8"][wl8.name] = {
+                "n_rows": wl8.n_rows, "value": round(wl8.n_rows / sec8, 2), "unit": "packed tokens/s",
+                "ms_per_step": round(sec8 * 1e3, 2), "steps": steps8,
+                "speedup_vs_bf16": round((wl8.n_rows / sec8) / (result["value"] if nm == args.workload
+                                                                 else result["secondary"]["value"]), 3),
+                "per_step_kernels": bd8}
+        del table8, blocks8
+        torch.cuda.empty_cache()
     if args.single_block:
         # one H3 block at N=1192, bf16 and INT8 W8A16 weights: per-step kernel
         # times (the block-parity shape; the INT8 variant's MFMA utilization)

@@ -83,5 +83,6 @@ def io_work(L: int, C: int, A: int, V: int, hidden: int, text_dim: int, video_pa
 
 # MI355X published peaks (dense; AMD product specification)
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_INT8_TOPS = 5000.0
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
