@@ -51,6 +51,7 @@ _TID = {
     "text": 20, "cond": 21, "audio_in": 22, "video_in": 23, "w_text": 24, "b_text": 25,
     "w_video": 26, "b_video": 27, "w_audio": 28, "b_audio": 29, "w_head_audio": 30,
     "b_head_audio": 31, "w_head_video": 32, "b_head_video": 33, "final_table": 34,
+    "tile_mask": 35,
 }
 TAG_TEXT, TAG_AUDIO, TAG_VIDEO = 0, 1, 2
 WFMT_BF16, WFMT_INT8_G32, WFMT_W8A8 = 0, 1, 2
@@ -331,6 +332,38 @@ def make_io_inputs(wl: Workload, io: IoDims, seed: int = 0) -> Dict[str, np.ndar
         "audio": f32("audio_in", (wl.A, io.audio_patch)),
         "video": f32("video_in", (V, io.video_patch)),
     }
+
+
+def make_tile_mask(n: int, heads: int, tile: int, keep: float, dense_rows: int = 0,
+                   seed: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Synthetic key-tile selection of block-sparse attention, CSR (tile_off
+    int32 [heads*nq + 1], tile_idx int32 [nnz]), nq = ceil(n / tile).
+
+    Query tiles that overlap the first ``dense_rows`` rows (the text and
+    condition prefix) select every tile.  Every other query tile selects the
+    prefix's key tiles, its own tile, and further distinct tiles drawn at
+    random until it holds max(ceil(keep * nq), those) tiles; indices sorted.
+    (The trained selection is not available; this keeps its shape: a fixed
+    budget per query tile, dense prefix queries, prefix keys always kept.)
+    """
+    nq = -(-n // tile)
+    budget = max(1, int(np.ceil(keep * nq)))
+    n_prefix = -(-dense_rows // tile) if dense_rows > 0 else 0
+    r = _rng(seed, 0, "tile_mask")
+    off, idx = [0], []
+    for _h in range(heads):
+        for i in range(nq):
+            if i < n_prefix:
+                sel = np.arange(nq)
+            else:
+                base = set(range(n_prefix)) | {i}
+                rest = np.array([j for j in range(nq) if j not in base], np.int64)
+                extra = max(0, budget - len(base))
+                pick = r.choice(rest, size=min(extra, len(rest)), replace=False) if extra else []
+                sel = np.array(sorted(base | set(int(j) for j in pick)))
+            idx.append(sel.astype(np.int32))
+            off.append(off[-1] + len(sel))
+    return np.asarray(off, np.int32), np.concatenate(idx).astype(np.int32)
 
 
 def make_inputs(wl: Workload, seed: int = 0, n_blocks: Optional[int] = None,
