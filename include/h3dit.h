@@ -136,6 +136,16 @@ H3DIT_API h3_status h3_dit_forward(const h3_dims* dims, float* x_packed, const i
                                    int64_t n_rows, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/* h3_dit_forward with block-sparse attention in every block (see
+ * h3_attention_sparse): block b reads its selection from the CSR offsets
+ * tile_off + b * (heads*nq + 1), which index the one array tile_idx. */
+H3DIT_API h3_status h3_dit_forward_sparse(const h3_dims* dims, float* x_packed, const int32_t* tag,
+                                          const float* positions, const uint16_t* mod_table,
+                                          const h3_block_weights* weights, int32_t n_blocks,
+                                          int64_t n_rows, int32_t tile, const int32_t* tile_off,
+                                          const int32_t* tile_idx, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
 /* Message of the last error on this thread ("" if none).  Never NULL. */
 H3DIT_API const char* h3_last_error(void);
 
@@ -273,6 +283,20 @@ H3DIT_API h3_status h3_qkv_rope(const h3_dims* dims, const uint16_t* h,
  * h in columns [h*d, (h+1)*d).  q, k, vt as written by h3_qkv_rope. */
 H3DIT_API h3_status h3_attention(const h3_dims* dims, const uint16_t* q, const uint16_t* k,
                                  const uint16_t* vt, int64_t n_rows, uint16_t* o, void* stream);
+
+/* Block-sparse attention: query tile i (rows [i*tile, (i+1)*tile)) of head h
+ * attends only to the keys of the key tiles j (rows [j*tile, (j+1)*tile), the
+ * last tile ragged) listed in tile_idx[tile_off[h*nq + i] .. tile_off[h*nq + i + 1]),
+ * nq = ceil(n_rows / tile), tile 64 or 128 (FastH3 OmniRef (Ref2VA) on Apple
+ * Silicon MLX, "Opt-in M5 attention backend": selected 64/128 tiles, only
+ * their valid rows visited).  tile_off int32 [heads*nq + 1] and tile_idx int32
+ * are device arrays (4-byte aligned).  Lists need not be sorted and must hold
+ * no duplicates; indices outside [0, nq) are clamped; an empty list gives
+ * zero rows.  q, k, vt, o as for h3_attention. */
+H3DIT_API h3_status h3_attention_sparse(const h3_dims* dims, const uint16_t* q, const uint16_t* k,
+                                        const uint16_t* vt, int64_t n_rows, int32_t tile,
+                                        const int32_t* tile_off, const int32_t* tile_idx,
+                                        uint16_t* o, void* stream);
 
 /* x fp32 [n_rows][D] += gate1[tag] * (o W_out^T + b_out);  o bf16 [n_rows][H*d]. */
 H3DIT_API h3_status h3_out_proj_residual(const h3_dims* dims, const uint16_t* o,

@@ -37,6 +37,15 @@
 // the first tile this is rare.  The first half always sets m to its maximum.
 // Keys at or beyond n are masked in the last tile; padded rows of q/k/v^T are
 // zeros written by the QKV epilogue, so every operand is finite.
+//
+// Block-sparse variant (SPARSE): a block is one query tile of T = 64 or 128
+// rows (T/32 wavefronts) and visits only the key tiles its CSR list selects
+// for this head (FastH3 OmniRef (Ref2VA) on Apple Silicon MLX, "Opt-in M5
+// attention backend": selected 64/128 tiles, only their valid rows).  A
+// selected T-row tile is T/64 of the 64-key LDS tiles.  Blocks take a 2-slot
+// ring (64 KB), so two blocks share a CU and their waves pair up per SIMD; the
+// next selected tile loads while the current one is consumed.  Indices are
+// clamped to the tile range; an empty list writes zeros.
 #include <type_traits>
 
 #include "h3_device.h"
@@ -61,10 +70,9 @@ __device__ __forceinline__ void att_wait_vmcnt() {
 template <int V>
 using att_ic = std::integral_constant<int, V>;
 
-constexpr int ATT_WAVES = 8;            // wavefronts per block, 32 queries each
-constexpr int ATT_BQ = ATT_WAVES * 32;  // queries per block (256)
+constexpr int ATT_WAVES = 8;            // wavefronts per block, 32 queries each (dense)
+constexpr int ATT_BQ = ATT_WAVES * 32;  // queries per block (256, dense)
 constexpr int ATT_BKV = 64;             // keys per tile
-constexpr int ATT_SLOTS = 3;            // LDS ring depth (tiles)
 constexpr float ATT_RESCALE_SUM = 256.0f;   // a lane's 16 probabilities summing above 2^8
 
 __device__ __forceinline__ int att_sigma(int i) {   // MFMA row -> key within 32
@@ -76,8 +84,10 @@ __device__ __forceinline__ int att_sigma(int i) {   // MFMA row -> key within 32
 __device__ __forceinline__ int att_kswz(int r) { return (r ^ (((r >> 3) & 1) << 2)) & 15; }
 __device__ __forceinline__ int att_vswz(int r) { return ((r & 31) ^ ((r & 31) >> 3)) & 7; }
 
-template <int HD>
-__global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs p) {
+template <int HD, int W, bool SPARSE>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnArgs p) {
+  constexpr int ATT_SLOTS = SPARSE ? 2 : 3;   // LDS ring depth (tiles)
+  constexpr int BQ = W * 32;                  // queries per block
   constexpr int DS = HD / 16;             // MFMA k-steps over head_dim
   constexpr int DT = HD / 32;             // 32-row tiles of head_dim in O^T
   constexpr int KROW = 256;               // LDS bytes per K row (16 chunks, HD/8 used)
@@ -86,7 +96,6 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs p) {
   constexpr int VBYTES = HD * VROW;
   constexpr int STAGE = KBYTES + VBYTES;
   constexpr int NK = KBYTES / 1024, NV = VBYTES / 1024;   // 1 KB DMA loads per tile
-  constexpr int W = ATT_WAVES;
   constexpr int NI = (NK + NV + W - 1) / W;               // per wavefront (last may idle)
   constexpr int NIK = NK / W;                             // first NIK loads are K
   static_assert(NK % W == 0, "K loads must split evenly over the waves");
@@ -95,7 +104,7 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.y;
-  const int q0 = blockIdx.x * ATT_BQ + wave * 32;
+  const int q0 = blockIdx.x * BQ + wave * 32;
   const int hl = lane >> 5, lq = lane & 31;
   const size_t hoff = (size_t)head * p.n_pad * HD;
 
@@ -246,7 +255,7 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs p) {
   };
 
   // one tile: both halves' scores, then each half's softmax and PV product
-  auto tile_body = [&](auto&& kr, auto&& vr, int kt, bool masked) __attribute__((always_inline)) {
+  auto tile_body = [&](auto&& kr, auto&& vr, int kt, bool masked, bool first) __attribute__((always_inline)) {
     f32x16 s0 = scores(kr, 0);
     f32x16 s1 = scores(kr, 1);
     if (masked) {
@@ -254,7 +263,7 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs p) {
       mask(s1, kt * ATT_BKV + 32);
     }
     bf16x8 pf[2];
-    softmax(s0, s1, kt == 0, pf);
+    softmax(s0, s1, first, pf);
     pv(vr, 0, pf);
     softmax(s1, s0, false, pf);
     pv(vr, 1, pf);
@@ -269,7 +278,8 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs p) {
     __builtin_amdgcn_s_barrier();
     issue(kt + 2, (uint32_t)(((U + 2) % ATT_SLOTS) * STAGE));
     tile_body([&](int ks, int ds) __attribute__((always_inline)) { return kread(att_ic<SO>{}, ks, ds); },
-              [&](int t, int s) __attribute__((always_inline)) { return vread(att_ic<SO>{}, t, s); }, kt, false);
+              [&](int t, int s) __attribute__((always_inline)) { return vread(att_ic<SO>{}, t, s); }, kt, false,
+              kt == 0);
   };
   // the same with the slot from the runtime phase (the last few tiles)
   auto tile_r = [&](int kt) __attribute__((always_inline)) {
@@ -283,20 +293,50 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs p) {
     if (kt + 2 < KT) issue(kt + 2, (uint32_t)(((kt + 2) % ATT_SLOTS) * STAGE));
     tile_body([&](int ks, int ds) __attribute__((always_inline)) { return att_read16(kbr[0][ds] + so + ks * 32 * KROW); },
               [&](int t, int s) __attribute__((always_inline)) { return att_read16(vbr[0][s] + so + KBYTES + t * 32 * VROW); },
-              kt, kt + 1 == KT);
+              kt, kt + 1 == KT, kt == 0);
   };
 
-  issue(0, 0);
-  if (KT > 1) issue(1, STAGE);
-  int kt = 0;
-  for (; kt + 5 <= KT; kt += 3) {
-    tile_c(att_ic<0>{}, kt);
-    tile_c(att_ic<1>{}, kt + 1);
-    tile_c(att_ic<2>{}, kt + 2);
+  if constexpr (!SPARSE) {
+    issue(0, 0);
+    if (KT > 1) issue(1, STAGE);
+    int kt = 0;
+    for (; kt + 5 <= KT; kt += 3) {
+      tile_c(att_ic<0>{}, kt);
+      tile_c(att_ic<1>{}, kt + 1);
+      tile_c(att_ic<2>{}, kt + 2);
+    }
+    for (; kt < KT; ++kt) tile_r(kt);
+  } else {
+    // the selected key tiles of this (head, query tile), as 64-key LDS tiles
+    constexpr int R = BQ / ATT_BKV;             // 64-key tiles per selected tile (1 or 2)
+    const int nq = (p.n + BQ - 1) / BQ;
+    const int* sel = p.tile_idx + p.tile_off[head * nq + blockIdx.x];
+    const int nkv = (p.tile_off[head * nq + blockIdx.x + 1] - p.tile_off[head * nq + blockIdx.x]) * R;
+    auto kv_of = [&](int i) __attribute__((always_inline)) {
+      const int j = min(max(sel[i / R], 0), nq - 1);
+      return j * R + i % R;
+    };
+    // tile i in slot U (compile-time): wait for it, barrier (every wave's part
+    // landed, tile i-1 consumed), start tile i+1 in the other slot, consume i
+    auto tile_s = [&](auto U_, int i, int kv) __attribute__((always_inline)) {
+      constexpr int U = decltype(U_)::value;
+      constexpr int SO = U * STAGE;
+      att_wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (i + 1 < nkv) issue(kv_of(i + 1), (uint32_t)((1 - U) * STAGE));
+      tile_body([&](int ks, int ds) __attribute__((always_inline)) { return kread(att_ic<SO>{}, ks, ds); },
+                [&](int t, int s) __attribute__((always_inline)) { return vread(att_ic<SO>{}, t, s); }, kv,
+                kv + 1 >= KT, i == 0);
+    };
+    if (nkv > 0) issue(kv_of(0), 0);
+    for (int i = 0; i < nkv; i += 2) {
+      tile_s(att_ic<0>{}, i, kv_of(i));
+      if (i + 1 < nkv) tile_s(att_ic<1>{}, i + 1, kv_of(i + 1));
+    }
   }
-  for (; kt < KT; ++kt) tile_r(kt);
 
-  const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32, 64));
+  const float lsum = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;   // an empty selection writes zeros
   const int qrow = q0 + lq;
   if (qrow < p.n) {
     uint16_t* op = p.o + (size_t)qrow * p.heads * HD + head * HD;
@@ -313,16 +353,24 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs p) {
   }
 }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid((a.n + ATT_BQ - 1) / ATT_BQ, a.heads);
-  if (a.head_dim == 128) {
-    attn_kernel<128><<<grid, ATT_WAVES * 64, 0, s>>>(a);
-  } else if (a.head_dim == 96) {
-    attn_kernel<96><<<grid, ATT_WAVES * 64, 0, s>>>(a);
+template <int HD>
+static hipError_t launch_hd(const AttnArgs& a, hipStream_t s) {
+  if (!a.tile_idx) {
+    attn_kernel<HD, ATT_WAVES, false><<<dim3((a.n + ATT_BQ - 1) / ATT_BQ, a.heads), ATT_WAVES * 64, 0, s>>>(a);
+  } else if (a.tile == 128) {
+    attn_kernel<HD, 4, true><<<dim3((a.n + 127) / 128, a.heads), 256, 0, s>>>(a);
+  } else if (a.tile == 64) {
+    attn_kernel<HD, 2, true><<<dim3((a.n + 63) / 64, a.heads), 128, 0, s>>>(a);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.head_dim == 128) return launch_hd<128>(a, s);
+  if (a.head_dim == 96) return launch_hd<96>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace h3

@@ -252,9 +252,21 @@ hipError_t do_qkv(const h3_dims& d, const uint16_t* h, const h3_block_weights& w
   return h3::launch_gemm(h3::EPI_QKV, d.wfmt, g, s);
 }
 
+// Block-sparse attention selection of one block (null = full attention).
+struct Sparse {
+  int tile;
+  const int32_t* off;   // [heads * ceil(n / tile) + 1]
+  const int32_t* idx;
+};
+
 hipError_t do_attn(const h3_dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* vt,
-                   int64_t n, uint16_t* o, hipStream_t s) {
+                   int64_t n, uint16_t* o, hipStream_t s, const Sparse* sp = nullptr) {
   h3::AttnArgs a{};
+  if (sp) {
+    a.tile = sp->tile;
+    a.tile_off = sp->off;
+    a.tile_idx = sp->idx;
+  }
   a.q = q;
   a.k = k;
   a.vt = vt;
@@ -291,7 +303,8 @@ hipError_t do_fc1(const h3_dims& d, const uint16_t* h2, const h3_block_weights& 
 // W8A8 block: each linear's input is quantized per row right after it is made
 // (AdaLN writes the codes directly; o and a go through the row quantizer).
 h3_status run_block_w8a8(const h3_dims& d, float* x, const int32_t* tag, const uint16_t* table,
-                         const h3_block_weights& w, int64_t n, const Arena& ar, hipStream_t s) {
+                         const h3_block_weights& w, int64_t n, const Arena& ar, hipStream_t s,
+                         const Sparse* sp) {
   const int Di = d.heads * d.head_dim;
   const uint16_t* hq = reinterpret_cast<const uint16_t*>(ar.h);      // int8 codes in the h arena
   const uint16_t* qa = reinterpret_cast<const uint16_t*>(ar.qa);
@@ -300,7 +313,7 @@ h3_status run_block_w8a8(const h3_dims& d, float* x, const int32_t* tag, const u
   if ((st = hip_ok(do_adaln(d, x, tag, table, 0, n, nullptr, s, hq_w, ar.qs), "adaln (attention)")) != H3_OK)
     return st;
   if ((st = hip_ok(do_qkv(d, hq, w, ar.cs, n, ar.q, ar.k, ar.vt, s, ar.qs), "qkv+rope")) != H3_OK) return st;
-  if ((st = hip_ok(do_attn(d, ar.q, ar.k, ar.vt, n, ar.o, s), "attention")) != H3_OK) return st;
+  if ((st = hip_ok(do_attn(d, ar.q, ar.k, ar.vt, n, ar.o, s, sp), "attention")) != H3_OK) return st;
   if ((st = hip_ok(do_quant(ar.o, n, Di, ar.qa, ar.qs, s), "quantize o")) != H3_OK) return st;
   if ((st = hip_ok(do_resid(d, qa, w.w_out, w.s_out, w.b_out, Di, table, 2, tag, n, x, s, ar.qs),
                    "out-proj+gate")) != H3_OK)
@@ -316,13 +329,14 @@ h3_status run_block_w8a8(const h3_dims& d, float* x, const int32_t* tag, const u
 }
 
 h3_status run_block(const h3_dims& d, float* x, const int32_t* tag, const uint16_t* table,
-                    const h3_block_weights& w, int64_t n, const Arena& ar, hipStream_t s) {
-  if (d.wfmt == H3_W_W8A8) return run_block_w8a8(d, x, tag, table, w, n, ar, s);
+                    const h3_block_weights& w, int64_t n, const Arena& ar, hipStream_t s,
+                    const Sparse* sp = nullptr) {
+  if (d.wfmt == H3_W_W8A8) return run_block_w8a8(d, x, tag, table, w, n, ar, s, sp);
   const int Di = d.heads * d.head_dim;
   h3_status st;
   if ((st = hip_ok(do_adaln(d, x, tag, table, 0, n, ar.h, s), "adaln (attention)")) != H3_OK) return st;
   if ((st = hip_ok(do_qkv(d, ar.h, w, ar.cs, n, ar.q, ar.k, ar.vt, s), "qkv+rope")) != H3_OK) return st;
-  if ((st = hip_ok(do_attn(d, ar.q, ar.k, ar.vt, n, ar.o, s), "attention")) != H3_OK) return st;
+  if ((st = hip_ok(do_attn(d, ar.q, ar.k, ar.vt, n, ar.o, s, sp), "attention")) != H3_OK) return st;
   if ((st = hip_ok(do_resid(d, ar.o, w.w_out, w.s_out, w.b_out, Di, table, 2, tag, n, x, s),
                    "out-proj+gate")) != H3_OK)
     return st;
@@ -489,6 +503,14 @@ h3_status run_heads(const h3_dims& d, const h3_io_dims& io, const h3_io_weights&
   return H3_OK;
 }
 
+h3_status check_sparse(int tile, const int32_t* off, const int32_t* idx) {
+  if (tile != 64 && tile != 128) return fail(H3_ERR_UNSUPPORTED, "tile=%d: supported 64 or 128", tile);
+  if (!off || !idx) return fail(H3_ERR_INVALID_ARG, "tile_off / tile_idx is NULL");
+  if ((reinterpret_cast<uintptr_t>(off) | reinterpret_cast<uintptr_t>(idx)) & 3u)
+    return fail(H3_ERR_INVALID_ARG, "tile_off / tile_idx is not 4-byte aligned");
+  return H3_OK;
+}
+
 // Row scales of a step entry point's activation buffer (W8A8), else null.
 const float* act_scales(const h3_dims& d, const void* act, int64_t n, int64_t K) {
   if (d.wfmt != H3_W_W8A8) return nullptr;
@@ -500,6 +522,59 @@ const float* act_scales(const h3_dims& d, const void* act, int64_t n, int64_t K)
 extern "C" {
 
 int64_t h3_padded_rows(int64_t n_rows) { return n_rows <= 0 ? 0 : pad_rows(n_rows); }
+
+h3_status h3_attention_sparse(const h3_dims* dims, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* vt, int64_t n_rows, int32_t tile,
+                              const int32_t* tile_off, const int32_t* tile_idx, uint16_t* o,
+                              void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_dims(dims)) != H3_OK || (st = check_rows(n_rows)) != H3_OK) return st;
+  H3_NEED(q, "q");
+  H3_NEED(k, "k");
+  H3_NEED(vt, "vt");
+  H3_NEED(o, "o");
+  if ((st = check_sparse(tile, tile_off, tile_idx)) != H3_OK) return st;
+  if ((st = check_device()) != H3_OK) return st;
+  const Sparse sp{tile, tile_off, tile_idx};
+  return hip_ok(do_attn(*dims, q, k, vt, n_rows, o, reinterpret_cast<hipStream_t>(stream), &sp),
+                "sparse attention");
+}
+
+h3_status h3_dit_forward_sparse(const h3_dims* dims, float* x, const int32_t* tag,
+                                const float* positions, const uint16_t* mod_table,
+                                const h3_block_weights* weights, int32_t n_blocks, int64_t n_rows,
+                                int32_t tile, const int32_t* tile_off, const int32_t* tile_idx,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_forward_common(dims, x, tag, positions, mod_table, n_rows, workspace,
+                                 workspace_bytes)) != H3_OK)
+    return st;
+  if (n_blocks <= 0) return fail(H3_ERR_INVALID_ARG, "n_blocks=%d must be positive", n_blocks);
+  if (!weights) return fail(H3_ERR_INVALID_ARG, "weights is NULL");
+  for (int b = 0; b < n_blocks; ++b) {
+    if ((st = check_weights(dims, &weights[b], true, true, true, true)) != H3_OK) {
+      std::string m = g_err;
+      return fail(st, "block %d: %s", b, m.c_str());
+    }
+  }
+  if ((st = check_sparse(tile, tile_off, tile_idx)) != H3_OK) return st;
+  if ((st = check_device()) != H3_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const Arena ar = carve(*dims, n_rows, static_cast<char*>(workspace));
+  if ((st = hip_ok(do_rope(*dims, positions, n_rows, ar.cs, s), "rope table")) != H3_OK) return st;
+  const size_t tstride = (size_t)dims->n_tags * 6 * dims->hidden;
+  const int64_t nq = (n_rows + tile - 1) / tile;
+  for (int b = 0; b < n_blocks; ++b) {
+    const Sparse sp{tile, tile_off + (size_t)b * (dims->heads * nq + 1), tile_idx};
+    if ((st = run_block(*dims, x, tag, mod_table + b * tstride, weights[b], n_rows, ar, s, &sp)) != H3_OK) {
+      std::string m = g_err;
+      return fail(st, "block %d: %s", b, m.c_str());
+    }
+  }
+  return H3_OK;
+}
 
 size_t h3_quantized_bytes(int64_t n_rows, int32_t width) {
   if (n_rows <= 0 || width <= 0) return 0;

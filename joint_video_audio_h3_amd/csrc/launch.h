@@ -62,6 +62,11 @@ struct AttnArgs {
   const uint16_t *q, *k, *vt;  // [H][n_pad][d], [H][n_pad][d], [H][d][n_pad]
   uint16_t* o;                 // [n][H*d]
   int n, n_pad, heads, head_dim;
+  // block-sparse: per (head, query tile) CSR lists of selected key tiles of
+  // `tile` rows (64 or 128); tile_idx == null means full attention
+  const int32_t* tile_off;     // [heads * ceil(n / tile) + 1]
+  const int32_t* tile_idx;
+  int tile;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

@@ -79,6 +79,9 @@ _SIGS = {
                                     c_vp, c_vp, c_i64, c_vp, c_vp]),
     "h3_heads_workspace_size": (c_sz, [_PD, _PSG]),
     "h3_quantized_bytes": (c_sz, [c_i64, c_i32]),
+    "h3_attention_sparse": (c_i32, [_PD, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
+    "h3_dit_forward_sparse": (c_i32, [_PD, c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(H3BlockWeights), c_i32,
+                                      c_i64, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "h3_quantize_rows": (c_i32, [c_vp, c_i64, c_i32, c_vp, c_vp]),
     "h3_embed_inputs": (c_i32, [_PD, _PIO, _PW, _PSG, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "h3_final_heads": (c_i32, [_PD, _PIO, _PW, _PSG, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
@@ -219,6 +222,24 @@ def mlp_fc2_residual(dims, a, block, mod_table, tag, x, stream=None):
     _check(load().h3_mlp_fc2_residual(ctypes.byref(make_dims(dims)), a.data_ptr(), ctypes.byref(w),
                                       mod_table.data_ptr(), tag.data_ptr(), x.shape[0],
                                       x.data_ptr(), _stream(stream)))
+
+
+def attention_sparse(dims, q, k, vt, n_rows, tile, tile_off, tile_idx, o, stream=None):
+    """Block-sparse attention: CSR key-tile lists (int32 device tensors) per (head, query tile)."""
+    _check(load().h3_attention_sparse(ctypes.byref(make_dims(dims)), q.data_ptr(), k.data_ptr(),
+                                      vt.data_ptr(), n_rows, tile, tile_off.data_ptr(),
+                                      tile_idx.data_ptr(), o.data_ptr(), _stream(stream)))
+
+
+def dit_forward_sparse(dims, x, tag, positions, mod_table, blocks: Sequence[Dict], tile, tile_off,
+                       tile_idx, workspace, stream=None):
+    """h3_dit_forward with block-sparse attention; tile_off holds one CSR offset array per block."""
+    d = make_dims(dims)
+    arr = (H3BlockWeights * len(blocks))(*[make_weights(b) for b in blocks])
+    _check(load().h3_dit_forward_sparse(ctypes.byref(d), x.data_ptr(), tag.data_ptr(),
+                                        positions.data_ptr(), mod_table.data_ptr(), arr, len(blocks),
+                                        x.shape[0], tile, tile_off.data_ptr(), tile_idx.data_ptr(),
+                                        workspace.data_ptr(), workspace.numel(), _stream(stream)))
 
 
 def quantized_bytes(n_rows: int, width: int) -> int:

@@ -256,12 +256,15 @@ def swiglu(z: np.ndarray, ffn: int) -> np.ndarray:
 
 
 # ------------------------------------------------------------------ block
-def block_steps(x, tags, pos, table_b, w, dims, q_rows=None, mods=None) -> Dict[str, np.ndarray]:
+def block_steps(x, tags, pos, table_b, w, dims, q_rows=None, mods=None,
+                sparse=None) -> Dict[str, np.ndarray]:
     """Run one block and return every intermediate (float64).
 
     ``q_rows`` restricts the row-local steps after attention (and attention's
     query side) to a subset of rows; keys and values always use every row.
     ``mods`` replaces the table gather with given per-row modulation vectors.
+    ``sparse`` = (tile, tile_off, tile_idx) makes step 6 block-sparse
+    (``h3_sparse.attention_sparse``) instead of full.
     """
     D, H, d, F = dims.hidden, dims.heads, dims.head_dim, dims.ffn
     x = np.asarray(x, np.float64)
@@ -279,7 +282,12 @@ def block_steps(x, tags, pos, table_b, w, dims, q_rows=None, mods=None) -> Dict[
     q = apply_rope(rms_norm(q, gq, dims.qk_eps), ang)
     k = apply_rope(rms_norm(k, gk, dims.qk_eps), ang)
     out["q"], out["k"], out["v"] = q, k, v
-    o = merge_heads(attention(q, k, v, rows))
+    if sparse is not None:
+        from .h3_sparse import attention_sparse
+        assert q_rows is None, "block-sparse attention runs over every query row"
+        o = merge_heads(attention_sparse(q, k, v, *sparse))
+    else:
+        o = merge_heads(attention(q, k, v, rows))
     out["o"] = o
     xr = x[rows] + m["gate1"][rows] * linear(o, w, "out", D, dims)
     out["x_mid"] = xr
@@ -292,15 +300,17 @@ def block_steps(x, tags, pos, table_b, w, dims, q_rows=None, mods=None) -> Dict[
     return out
 
 
-def block_forward(x, tags, pos, table_b, w, dims, q_rows=None, mods=None) -> np.ndarray:
+def block_forward(x, tags, pos, table_b, w, dims, q_rows=None, mods=None, sparse=None) -> np.ndarray:
     """One H3 DiT block: x [N, D] -> x_out [N, D] (or [R, D] for ``q_rows``)."""
-    return block_steps(x, tags, pos, table_b, w, dims, q_rows, mods)["x_out"]
+    return block_steps(x, tags, pos, table_b, w, dims, q_rows, mods, sparse)["x_out"]
 
 
 def dit_forward(x, tags, pos, table, weights_for_block: Callable[[int], dict],
-                n_blocks: int, dims) -> np.ndarray:
-    """Blocks 0..n_blocks-1 in order over the packed rows (one denoising forward)."""
+                n_blocks: int, dims, sparse_for_block: Optional[Callable[[int], tuple]] = None) -> np.ndarray:
+    """Blocks 0..n_blocks-1 in order over the packed rows (one denoising forward);
+    ``sparse_for_block(b)`` gives block b's (tile, tile_off, tile_idx) selection."""
     y = np.asarray(x, np.float64)
     for b in range(n_blocks):
-        y = block_forward(y, tags, pos, table[b], weights_for_block(b), dims)
+        sp = None if sparse_for_block is None else sparse_for_block(b)
+        y = block_forward(y, tags, pos, table[b], weights_for_block(b), dims, sparse=sp)
     return y

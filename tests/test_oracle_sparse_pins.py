@@ -104,3 +104,14 @@ def test_generator_mask_shape():
         for i in (10, 200, nq - 1):
             sel = idx[off[h * nq + i]:off[h * nq + i + 1]]
             assert np.all(np.diff(sel) > 0) and set(range(10)) <= set(sel.tolist()) and i in sel
+
+
+def test_block_with_every_tile_selected_equals_dense_block():
+    wl = synth.WORKLOADS["tiny_2blk_n164"]
+    x, tags, pos, table, blocks = synth.make_inputs(wl, seed=7, n_blocks=1)
+    nq = -(-wl.n_rows // 64)
+    off, idx = synth.make_tile_mask(wl.n_rows, wl.dims.heads, 64, 1.0, seed=1)
+    assert len(idx) == wl.dims.heads * nq * nq
+    dense = oracle.block_forward(x, tags, pos, table[0], blocks[0], wl.dims)
+    sparse = oracle.block_forward(x, tags, pos, table[0], blocks[0], wl.dims, sparse=(64, off, idx))
+    np.testing.assert_allclose(sparse, dense, rtol=1e-12, atol=1e-12)
