@@ -199,6 +199,48 @@ def io_breakdown(lib, dims, io, wl, reps, torch):
     return out
 
 
+def visited_flop(n, heads, d, tile, off, idx):
+    """4*d FLOP per (query, selected key) pair of block-sparse attention."""
+    import numpy as np
+
+    nq = -(-n // tile)
+    rows = np.minimum(tile, n - np.arange(nq) * tile)                   # rows per query tile
+    keys_per_tile = np.minimum(tile, n - np.arange(nq) * tile)          # valid rows per key tile
+    counts = np.add.reduceat(keys_per_tile[idx], off[:-1]) * (np.diff(off) > 0)
+    return 4.0 * d * float(np.sum(np.tile(rows, heads) * counts))
+
+
+def sparse_breakdown(lib, dims, n, reps, torch, keep=0.125, dense_rows=1280):
+    """Block-sparse attention at N rows: each tile size at `keep` of the key
+    tiles (dense prefix queries), rated on the FLOPs of the pairs it visits."""
+    H, d = dims.heads, dims.head_dim
+    np_ = lib.padded_rows(n)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    qs = float(1.4426950408889634 / d ** 0.5)
+    q = torch.zeros(H, np_, d, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros_like(q)
+    vt = torch.zeros(H, d, np_, dtype=torch.bfloat16, device="cuda")
+    q[:, :n] = (torch.randn(H, n, d, generator=g, device="cuda") * qs).to(torch.bfloat16)
+    k[:, :n] = torch.randn(H, n, d, generator=g, device="cuda").to(torch.bfloat16)
+    vt[:, :, :n] = torch.randn(H, d, n, generator=g, device="cuda").to(torch.bfloat16)
+    o = torch.empty(n, H * d, dtype=torch.bfloat16, device="cuda")
+    out = {"keep": keep, "dense_prefix_rows": dense_rows}
+    dense_ms = _time_launches(lambda: lib.attention(dims, q, k, vt, n, o), reps, torch)
+    out["dense_ms"] = round(dense_ms, 3)
+    for tile in (128, 64):
+        off, idx = synth.make_tile_mask(n, H, tile, keep, dense_rows=dense_rows, seed=0)
+        offd, idxd = torch.from_numpy(off).cuda(), torch.from_numpy(idx).cuda()
+        ms = _time_launches(lambda: lib.attention_sparse(dims, q, k, vt, n, tile, offd, idxd, o), reps, torch)
+        fl = visited_flop(n, H, d, tile, off, idx)
+        tf = fl / (ms * 1e-3) / 1e12
+        log(f"sparse attention tile {tile}: {ms:.2f} ms")
+        out[f"tile{tile}"] = {"ms": round(ms, 3), "visited_fraction": round(fl / (4.0 * d * H * n * n), 4),
+                              "visited_tflops": round(tf, 1), "mfma_frac": round(tf / PEAK, 4),
+                              "speedup_vs_dense": round(dense_ms / ms, 2)}
+    return out
+
+
 def run_forward(lib, dims, rows, table, blocks, ws, steps, warmup, torch):
     x, tags, pos = rows
     fwd = lambda: lib.dit_forward(dims, x, tags, pos, table, blocks, ws)
@@ -262,6 +304,8 @@ def main():
                          "the known-size reference for HBM byte counters")
     ap.add_argument("--single-block", type=int, default=1,
                     help="also time one H3 block at N=1192 with bf16 and INT8 weights (0: skip)")
+    ap.add_argument("--sparse", type=int, default=1,
+                    help="also time block-sparse attention and the sparse forward (0: skip)")
     ap.add_argument("--w8a8", type=int, default=1,
                     help="also run the forwards with the W8A8 trunk (0: skip)")
     ap.add_argument("--only-step", default=None,
@@ -354,6 +398,38 @@ def main():
             "forward_mfma_frac": round(wl2.n_blocks * w2.total_flop / sec2 / 1e12 / PEAK, 4),
             "per_step_kernels": bd2,
         }
+    if args.sparse:
+        # block-sparse attention (a fixed budget of key tiles per query tile)
+        # at the primary workload: the kernel alone, then the 50-block forward
+        log("block-sparse attention")
+        result["sparse"] = sparse_breakdown(lib, dims, n, args.breakdown_reps, torch)
+        tile, keep = 128, result["sparse"]["keep"]
+        import numpy as np
+        n_masks = 10     # distinct selections, cycled over the blocks
+        masks = [synth.make_tile_mask(n, dims.heads, tile, keep, dense_rows=wl.L + wl.C, seed=b)
+                 for b in range(n_masks)]
+        bases = np.cumsum([0] + [len(m[1]) for m in masks])
+        offd = torch.from_numpy(np.concatenate([(masks[b % n_masks][0] + bases[b % n_masks]).astype(np.int32)
+                                                for b in range(wl.n_blocks)])).cuda()
+        log("sparse forward masks ready")
+        idxd = torch.from_numpy(np.concatenate([m[1] for m in masks])).cuda()
+        x, tags, pos = synth.make_device_rows(wl, seed=0)
+        ws = lib.alloc_workspace(dims, n)
+        fwd = lambda: lib.dit_forward_sparse(dims, x, tags, pos, table, blocks, tile, offd, idxd, ws)  # noqa: E731
+        fwd()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fwd()
+        torch.cuda.synchronize()
+        secs = (time.perf_counter() - t0) / args.steps
+        assert bool(torch.isfinite(x).all()), "non-finite output"
+        result["sparse"]["forward"] = {"tile": tile, "value": round(n / secs, 2), "unit": "packed tokens/s",
+                                       "ms_per_step": round(secs * 1e3, 2), "steps": args.steps,
+                                       "speedup_vs_dense": round((n / secs) / result["value"], 3),
+                                       "masks": "10 generator selections (seeds 0..9) cycled over the blocks"}
+        log(f"sparse forward: {secs * 1e3:.1f} ms")
+        del ws, x, offd, idxd
     if args.w8a8:
         # the same forwards with the W8A8 trunk (int8 weights and activations,
         # per-row scales) on the int8 matrix cores

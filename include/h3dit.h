@@ -290,9 +290,11 @@ H3DIT_API h3_status h3_attention(const h3_dims* dims, const uint16_t* q, const u
  * nq = ceil(n_rows / tile), tile 64 or 128 (FastH3 OmniRef (Ref2VA) on Apple
  * Silicon MLX, "Opt-in M5 attention backend": selected 64/128 tiles, only
  * their valid rows visited).  tile_off int32 [heads*nq + 1] and tile_idx int32
- * are device arrays (4-byte aligned).  Lists need not be sorted and must hold
- * no duplicates; indices outside [0, nq) are clamped; an empty list gives
- * zero rows.  q, k, vt, o as for h3_attention. */
+ * are device arrays (4-byte aligned); tile_off is non-decreasing and its last
+ * entry is the length of tile_idx.  Lists need not be sorted and must hold no
+ * duplicates; indices outside [0, nq) are clamped, lists longer than nq are
+ * cut at nq entries, an empty list gives zero rows.  q, k, vt, o as for
+ * h3_attention. */
 H3DIT_API h3_status h3_attention_sparse(const h3_dims* dims, const uint16_t* q, const uint16_t* k,
                                         const uint16_t* vt, int64_t n_rows, int32_t tile,
                                         const int32_t* tile_off, const int32_t* tile_idx,

@@ -45,7 +45,8 @@
 // selected T-row tile is T/64 of the 64-key LDS tiles.  Blocks take a 2-slot
 // ring (64 KB), so two blocks share a CU and their waves pair up per SIMD; the
 // next selected tile loads while the current one is consumed.  Indices are
-// clamped to the tile range; an empty list writes zeros.
+// clamped to the tile range, a list is cut at nq entries, and an empty list
+// writes zeros.
 #include <type_traits>
 
 #include "h3_device.h"
@@ -311,7 +312,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     constexpr int R = BQ / ATT_BKV;             // 64-key tiles per selected tile (1 or 2)
     const int nq = (p.n + BQ - 1) / BQ;
     const int* sel = p.tile_idx + p.tile_off[head * nq + blockIdx.x];
-    const int nkv = (p.tile_off[head * nq + blockIdx.x + 1] - p.tile_off[head * nq + blockIdx.x]) * R;
+    // a list holds at most nq distinct tiles: a longer (malformed) one is cut there
+    const int cnt = min(max(p.tile_off[head * nq + blockIdx.x + 1] - p.tile_off[head * nq + blockIdx.x], 0), nq);
+    const int nkv = cnt * R;
     auto kv_of = [&](int i) __attribute__((always_inline)) {
       const int j = min(max(sel[i / R], 0), nq - 1);
       return j * R + i % R;

@@ -224,8 +224,16 @@ def mlp_fc2_residual(dims, a, block, mod_table, tag, x, stream=None):
                                       x.data_ptr(), _stream(stream)))
 
 
+def _need_int32(*ts):
+    import torch
+    for t in ts:
+        if t.dtype != torch.int32:
+            raise TypeError(f"tile_off / tile_idx must be int32 device tensors, got {t.dtype}")
+
+
 def attention_sparse(dims, q, k, vt, n_rows, tile, tile_off, tile_idx, o, stream=None):
     """Block-sparse attention: CSR key-tile lists (int32 device tensors) per (head, query tile)."""
+    _need_int32(tile_off, tile_idx)
     _check(load().h3_attention_sparse(ctypes.byref(make_dims(dims)), q.data_ptr(), k.data_ptr(),
                                       vt.data_ptr(), n_rows, tile, tile_off.data_ptr(),
                                       tile_idx.data_ptr(), o.data_ptr(), _stream(stream)))
@@ -234,6 +242,7 @@ def attention_sparse(dims, q, k, vt, n_rows, tile, tile_off, tile_idx, o, stream
 def dit_forward_sparse(dims, x, tag, positions, mod_table, blocks: Sequence[Dict], tile, tile_off,
                        tile_idx, workspace, stream=None):
     """h3_dit_forward with block-sparse attention; tile_off holds one CSR offset array per block."""
+    _need_int32(tile_off, tile_idx)
     d = make_dims(dims)
     arr = (H3BlockWeights * len(blocks))(*[make_weights(b) for b in blocks])
     _check(load().h3_dit_forward_sparse(ctypes.byref(d), x.data_ptr(), tag.data_ptr(),

@@ -341,29 +341,31 @@ def make_tile_mask(n: int, heads: int, tile: int, keep: float, dense_rows: int =
 
     Query tiles that overlap the first ``dense_rows`` rows (the text and
     condition prefix) select every tile.  Every other query tile selects the
-    prefix's key tiles, its own tile, and further distinct tiles drawn at
-    random until it holds max(ceil(keep * nq), those) tiles; indices sorted.
-    (The trained selection is not available; this keeps its shape: a fixed
-    budget per query tile, dense prefix queries, prefix keys always kept.)
+    prefix's key tiles, its own tile, and further distinct tiles at random
+    until it holds max(ceil(keep * nq), those) tiles; indices sorted.  (The
+    trained selection is not available; this keeps its shape: a fixed budget
+    per query tile, dense prefix queries, prefix keys always kept.)
     """
     nq = -(-n // tile)
-    budget = max(1, int(np.ceil(keep * nq)))
-    n_prefix = -(-dense_rows // tile) if dense_rows > 0 else 0
+    budget = min(nq, max(1, int(np.ceil(keep * nq))))
+    n_prefix = min(nq, -(-dense_rows // tile)) if dense_rows > 0 else 0
     r = _rng(seed, 0, "tile_mask")
-    off, idx = [0], []
-    for _h in range(heads):
-        for i in range(nq):
-            if i < n_prefix:
-                sel = np.arange(nq)
-            else:
-                base = set(range(n_prefix)) | {i}
-                rest = np.array([j for j in range(nq) if j not in base], np.int64)
-                extra = max(0, budget - len(base))
-                pick = r.choice(rest, size=min(extra, len(rest)), replace=False) if extra else []
-                sel = np.array(sorted(base | set(int(j) for j in pick)))
-            idx.append(sel.astype(np.int32))
-            off.append(off[-1] + len(sel))
-    return np.asarray(off, np.int32), np.concatenate(idx).astype(np.int32)
+    score = r.random((heads, nq, nq))                 # [head, query tile, key tile]
+    score[:, :, :n_prefix] = 2.0                      # prefix keys always kept
+    ii = np.arange(nq)
+    score[:, ii, ii] = 2.0                            # the own tile always kept
+    score[:, :n_prefix, :] = 2.0                      # prefix queries: every tile
+    # every non-prefix query tile keeps k = max(prefix tiles + own tile, budget)
+    # tiles: those scoring at least its k-th largest score (random scores are
+    # distinct; the forced ones score highest)
+    k = min(nq, max(n_prefix + 1, budget))
+    thr = np.partition(score, nq - k, axis=2)[..., nq - k:nq - k + 1]
+    thr[:, :n_prefix] = -1.0                          # prefix queries keep everything
+    sel = score >= thr
+    counts = sel.sum(axis=2).reshape(-1)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    idx = np.nonzero(sel.reshape(heads * nq, nq))[1].astype(np.int32)   # row-major: sorted per row
+    return off, idx
 
 
 def make_inputs(wl: Workload, seed: int = 0, n_blocks: Optional[int] = None,
