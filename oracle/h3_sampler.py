@@ -1,0 +1,66 @@
+"""Plain CPU oracle of the denoising loop around the velocity forward (float64).
+
+TEST INFRASTRUCTURE ONLY, like ``h3_block``: only the tests, the smoke check of
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` use it.  It shares
+no code with the HIP kernels or their host library.
+
+The sampler is rectified-flow Euler with an exponential sigma shift
+(minimax-h3-mlx README, "Layout": scheduler.py).  Video and audio run their own
+shifted schedules, 12.0 and 3.0, so their timesteps only partly coincide: 77
+distinct ones in a 40-step run (minimax-h3-mlx README, "AdaLN precompute").
+The number of passes is the step count and a terminal zero follows the last
+pass (H3-metal digest, "Sampler and DiT controls").
+
+Reading of those statements, fixed by the 77:
+  base grid    b_i = 1 - i / steps, i = 0 .. steps - 1, then the terminal 0
+  shift        sigma = s b / (1 + (s - 1) b)   (the exponential shift, s = e^mu)
+  Euler pass i for each modality m:
+               z_m <- z_m + (sigma_m[i+1] - sigma_m[i]) * v_m(z, sigma[i])
+With these, the video (12) and audio (3) schedules of 40 passes meet at exactly
+three base points (b = 1; 0.5 with 0.8; 0.2 with 0.5), 80 - 3 = 77.  Text and
+condition rows are not denoised.  Velocity reuse is not modelled (one model
+evaluation per pass).
+"""
+from __future__ import annotations
+
+from typing import Callable, Tuple
+
+import numpy as np
+
+
+def base_grid(steps: int) -> np.ndarray:
+    """b_i = 1 - i/steps for i < steps, then 0: [steps + 1]."""
+    return np.concatenate([1.0 - np.arange(steps, dtype=np.float64) / steps, [0.0]])
+
+
+def shift_sigmas(b: np.ndarray, shift: float) -> np.ndarray:
+    """Exponential shift s b / (1 + (s - 1) b) (identity at s = 1; keeps 0 and 1)."""
+    b = np.asarray(b, np.float64)
+    return shift * b / (1.0 + (shift - 1.0) * b)
+
+
+def schedule(steps: int, shift: float) -> np.ndarray:
+    """The sigmas of one modality, [steps + 1], from 1 down to the terminal 0."""
+    return shift_sigmas(base_grid(steps), shift)
+
+
+def euler(z0, sigmas, velocity: Callable[[int, np.ndarray], np.ndarray]) -> np.ndarray:
+    """Euler over one schedule: z <- z + (s[i+1] - s[i]) * velocity(i, z)."""
+    z = np.asarray(z0, np.float64).copy()
+    for i in range(len(sigmas) - 1):
+        z = z + (sigmas[i + 1] - sigmas[i]) * velocity(i, z)
+    return z
+
+
+def denoise(audio0, video0, sig_audio, sig_video,
+            velocity_pair: Callable[[int, np.ndarray, np.ndarray], Tuple[np.ndarray, np.ndarray]]):
+    """Joint Euler over both modalities: one velocity forward per pass gives
+    (v_audio, v_video) from the current latents, each latent steps on its own
+    schedule."""
+    a = np.asarray(audio0, np.float64).copy()
+    v = np.asarray(video0, np.float64).copy()
+    for i in range(len(sig_video) - 1):
+        va, vv = velocity_pair(i, a, v)
+        a = a + (sig_audio[i + 1] - sig_audio[i]) * va
+        v = v + (sig_video[i + 1] - sig_video[i]) * vv
+    return a, v
