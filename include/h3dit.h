@@ -149,6 +149,7 @@ H3DIT_API h3_status h3_dit_forward_sparse(const h3_dims* dims, float* x_packed, 
 /* Message of the last error on this thread ("" if none).  Never NULL. */
 H3DIT_API const char* h3_last_error(void);
 
+
 /* W8A8 activation buffer: int8 codes [n_rows][width], then fp32 row scales
  * [n_rows] at byte offset roundup(n_rows * width, 256).  Bytes it needs (pure;
  * 0 for non-positive sizes). */
@@ -316,6 +317,40 @@ H3DIT_API h3_status h3_mlp_fc2_residual(const h3_dims* dims, const uint16_t* a,
                                         const h3_block_weights* weights,
                                         const uint16_t* mod_table, const int32_t* tag,
                                         int64_t n_rows, float* x, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Denoising loop: rectified-flow Euler, one velocity forward per pass       */
+/* ------------------------------------------------------------------------ */
+/* Sigmas of one modality's schedule, host double [n_steps + 1]: base grid
+ * b_i = 1 - i/n_steps (i < n_steps), exponentially shifted to
+ * shift*b / (1 + (shift - 1)*b), then the terminal 0 (minimax-h3-mlx README,
+ * "Layout": rectified-flow Euler with exponential sigma shift; "AdaLN
+ * precompute": video shift 12.0, audio 3.0, whose 40-pass schedules meet in 77
+ * distinct timesteps; H3-metal digest, "Sampler and DiT controls": terminal
+ * zero after the last pass).  Pure host function. */
+H3DIT_API h3_status h3_sigma_schedule(int32_t n_steps, double shift, double* sigmas);
+
+/* n_steps Euler passes on the GPU.  Pass i runs the velocity forward
+ * (h3_velocity_forward with the current latents, the blocks' tables
+ * mod_tables + i*n_blocks*T*6*D and the final table final_tables + i*2*2*D)
+ * and then, per modality,  z += (sigma[i+1] - sigma[i]) * v.
+ *   audio fp32 [audio][audio_patch], video fp32 [video][video_patch]: the
+ *         latents, updated in place (text and condition inputs stay fixed)
+ *   mod_tables bf16 [n_steps][n_blocks][T][6][D]; final_tables bf16
+ *         [n_steps][2][2][D] (each step's tables from its own per-modality
+ *         timesteps, precomputed as in "AdaLN precompute")
+ *   sigmas_audio, sigmas_video: host double [n_steps + 1] (h3_sigma_schedule)
+ *   x_packed fp32 [N][D]: scratch for the stream; workspace at least
+ *         h3_workspace_size(dims, N) bytes.  n_blocks >= 1. */
+H3DIT_API h3_status h3_denoise(const h3_dims* dims, const h3_io_dims* io_dims,
+                               const h3_io_weights* io_weights, const h3_segments* segments,
+                               const uint16_t* text, const float* cond, float* audio, float* video,
+                               const int32_t* tag, const float* positions,
+                               const uint16_t* mod_tables, const h3_block_weights* weights,
+                               int32_t n_blocks, const uint16_t* final_tables,
+                               const double* sigmas_audio, const double* sigmas_video,
+                               int32_t n_steps, float* x_packed, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -576,6 +576,82 @@ h3_status h3_dit_forward_sparse(const h3_dims* dims, float* x, const int32_t* ta
   return H3_OK;
 }
 
+h3_status h3_sigma_schedule(int32_t n_steps, double shift, double* sigmas) {
+  g_err.clear();
+  if (n_steps <= 0 || n_steps > 100000) return fail(H3_ERR_INVALID_ARG, "n_steps=%d out of [1, 100000]", n_steps);
+  if (!(shift > 0.0) || !std::isfinite(shift)) return fail(H3_ERR_INVALID_ARG, "shift must be > 0");
+  if (!sigmas) return fail(H3_ERR_INVALID_ARG, "sigmas is NULL");
+  for (int i = 0; i < n_steps; ++i) {
+    const double b = 1.0 - (double)i / (double)n_steps;
+    sigmas[i] = shift * b / (1.0 + (shift - 1.0) * b);
+  }
+  sigmas[n_steps] = 0.0;
+  return H3_OK;
+}
+
+h3_status h3_denoise(const h3_dims* dims, const h3_io_dims* io_dims, const h3_io_weights* io_weights,
+                     const h3_segments* segments, const uint16_t* text, const float* cond,
+                     float* audio, float* video, const int32_t* tag, const float* positions,
+                     const uint16_t* mod_tables, const h3_block_weights* weights, int32_t n_blocks,
+                     const uint16_t* final_tables, const double* sigmas_audio,
+                     const double* sigmas_video, int32_t n_steps, float* x_packed, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_io(dims, io_dims, segments)) != H3_OK) return st;
+  const h3_segments sg = *segments;
+  const int64_t n = sg.text + sg.cond + sg.audio + sg.video;
+  if (n_steps <= 0) return fail(H3_ERR_INVALID_ARG, "n_steps=%d must be positive", n_steps);
+  if (n_blocks <= 0) return fail(H3_ERR_INVALID_ARG, "n_blocks=%d must be positive", n_blocks);
+  if (!sigmas_audio || !sigmas_video) return fail(H3_ERR_INVALID_ARG, "sigmas_audio / sigmas_video is NULL");
+  if ((st = check_embed_ptrs(sg, io_weights, text, cond, audio, video, x_packed)) != H3_OK) return st;
+  if ((st = check_head_ptrs(sg, io_weights, x_packed, final_tables, audio, video)) != H3_OK) return st;
+  if ((st = check_forward_common(dims, x_packed, tag, positions, mod_tables, n, workspace,
+                                 workspace_bytes)) != H3_OK)
+    return st;
+  if (!weights) return fail(H3_ERR_INVALID_ARG, "weights is NULL");
+  for (int b = 0; b < n_blocks; ++b) {
+    if ((st = check_weights(dims, &weights[b], true, true, true, true)) != H3_OK) {
+      std::string m = g_err;
+      return fail(st, "block %d: %s", b, m.c_str());
+    }
+  }
+  // the velocities live in the attention-output arena, dead after the last block
+  const size_t va_bytes = up256((size_t)sg.audio * io_dims->audio_patch * 4);
+  const size_t vv_bytes = up256((size_t)sg.video * io_dims->video_patch * 4);
+  const size_t o_bytes = (size_t)pad_rows(n) * dims->heads * dims->head_dim * 2;
+  if (va_bytes + vv_bytes > o_bytes)
+    return fail(H3_ERR_UNSUPPORTED, "velocities (%zu bytes) exceed the attention-output arena (%zu)",
+                va_bytes + vv_bytes, o_bytes);
+  if ((st = check_device()) != H3_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const Arena ar = carve(*dims, n, static_cast<char*>(workspace));
+  float* vel_a = reinterpret_cast<float*>(ar.o);
+  float* vel_v = reinterpret_cast<float*>(reinterpret_cast<char*>(ar.o) + va_bytes);
+  if ((st = hip_ok(do_rope(*dims, positions, n, ar.cs, s), "rope table")) != H3_OK) return st;
+  const size_t tstride = (size_t)dims->n_tags * 6 * dims->hidden;
+  const size_t fstride = (size_t)4 * dims->hidden;
+  for (int i = 0; i < n_steps; ++i) {
+    if ((st = run_embed(*dims, *io_dims, *io_weights, sg, text, cond, audio, video, x_packed, s)) != H3_OK)
+      return fail(st, "step %d: %s", i, std::string(g_err).c_str());
+    const uint16_t* tab = mod_tables + (size_t)i * n_blocks * tstride;
+    for (int b = 0; b < n_blocks; ++b) {
+      if ((st = run_block(*dims, x_packed, tag, tab + b * tstride, weights[b], n, ar, s)) != H3_OK)
+        return fail(st, "step %d block %d: %s", i, b, std::string(g_err).c_str());
+    }
+    if ((st = run_heads(*dims, *io_dims, *io_weights, sg, x_packed, final_tables + i * fstride, vel_a,
+                        vel_v, ar.h, s)) != H3_OK)
+      return fail(st, "step %d: %s", i, std::string(g_err).c_str());
+    const float dta = (float)(sigmas_audio[i + 1] - sigmas_audio[i]);
+    const float dtv = (float)(sigmas_video[i + 1] - sigmas_video[i]);
+    if ((st = hip_ok(h3::launch_euler(audio, vel_a, dta, sg.audio * io_dims->audio_patch, s), "euler audio")) != H3_OK)
+      return st;
+    if ((st = hip_ok(h3::launch_euler(video, vel_v, dtv, sg.video * io_dims->video_patch, s), "euler video")) != H3_OK)
+      return st;
+  }
+  return H3_OK;
+}
+
 size_t h3_quantized_bytes(int64_t n_rows, int32_t width) {
   if (n_rows <= 0 || width <= 0) return 0;
   return qa_scale_offset(n_rows, width) + up256((size_t)n_rows * 4);

@@ -74,6 +74,30 @@ __global__ __launch_bounds__(256) void patch_embed_kernel(PatchArgs a) {
   }
 }
 
+// One Euler pass of a latent: z += dt * v (rectified flow; minimax-h3-mlx
+// README, "Layout": rectified-flow Euler with exponential sigma shift).
+// float4 pieces; HBM traffic 12 bytes per element.
+__global__ __launch_bounds__(256) void euler_kernel(float* z, const float* v, float dt, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i + 3 < n) {
+    float4 a = *reinterpret_cast<const float4*>(z + i);
+    const float4 b = *reinterpret_cast<const float4*>(v + i);
+    a.x += dt * b.x;
+    a.y += dt * b.y;
+    a.z += dt * b.z;
+    a.w += dt * b.w;
+    *reinterpret_cast<float4*>(z + i) = a;
+  } else {
+    for (int64_t j = i; j < n; ++j) z[j] += dt * v[j];
+  }
+}
+
+hipError_t launch_euler(float* z, const float* v, float dt, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  euler_kernel<<<dim3((unsigned)((n + 1023) / 1024)), 256, 0, s>>>(z, v, dt, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_patch_embed(const PatchArgs& a, hipStream_t s) {
   const dim3 grid((a.rows + 127) / 128, (a.D + 32 * PE_NCT - 1) / (32 * PE_NCT));
   switch (a.P) {

@@ -79,4 +79,7 @@ struct PatchArgs {
 };
 hipError_t launch_patch_embed(const PatchArgs& a, hipStream_t s);
 
+// z[0..n) += dt * v[0..n)  (one Euler pass of a latent)
+hipError_t launch_euler(float* z, const float* v, float dt, int64_t n, hipStream_t s);
+
 }  // namespace h3

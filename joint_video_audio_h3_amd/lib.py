@@ -79,6 +79,11 @@ _SIGS = {
                                     c_vp, c_vp, c_i64, c_vp, c_vp]),
     "h3_heads_workspace_size": (c_sz, [_PD, _PSG]),
     "h3_quantized_bytes": (c_sz, [c_i64, c_i32]),
+    "h3_sigma_schedule": (c_i32, [c_i32, ctypes.c_double, ctypes.POINTER(ctypes.c_double)]),
+    "h3_denoise": (c_i32, [_PD, _PIO, _PW, _PSG, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                           ctypes.POINTER(H3BlockWeights), c_i32, c_vp,
+                           ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), c_i32,
+                           c_vp, c_vp, c_sz, c_vp]),
     "h3_attention_sparse": (c_i32, [_PD, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "h3_dit_forward_sparse": (c_i32, [_PD, c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(H3BlockWeights), c_i32,
                                       c_i64, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
@@ -249,6 +254,32 @@ def dit_forward_sparse(dims, x, tag, positions, mod_table, blocks: Sequence[Dict
                                         positions.data_ptr(), mod_table.data_ptr(), arr, len(blocks),
                                         x.shape[0], tile, tile_off.data_ptr(), tile_idx.data_ptr(),
                                         workspace.data_ptr(), workspace.numel(), _stream(stream)))
+
+
+def sigma_schedule(n_steps: int, shift: float):
+    """Host list of n_steps + 1 sigmas (h3_sigma_schedule)."""
+    buf = (ctypes.c_double * (n_steps + 1))()
+    _check(load().h3_sigma_schedule(n_steps, shift, buf))
+    return list(buf)
+
+
+def denoise(dims, io, io_w: Dict, text, cond, audio, video, tag, positions, mod_tables,
+            blocks: Sequence[Dict], final_tables, sigmas_audio, sigmas_video, x, workspace,
+            stream=None):
+    """len(sigmas) - 1 Euler passes; audio / video latents updated in place."""
+    sg = segments_of(text, cond, audio, video)
+    w = make_io_weights(io_w)
+    arr = (H3BlockWeights * len(blocks))(*[make_weights(b) for b in blocks])
+    n_steps = len(sigmas_video) - 1
+    if len(sigmas_audio) != n_steps + 1:
+        raise ValueError("audio and video schedules must have the same number of passes")
+    sa = (ctypes.c_double * len(sigmas_audio))(*sigmas_audio)
+    sv = (ctypes.c_double * len(sigmas_video))(*sigmas_video)
+    _check(load().h3_denoise(
+        ctypes.byref(make_dims(dims)), ctypes.byref(make_io_dims(io)), ctypes.byref(w), ctypes.byref(sg),
+        _ptr(text), _ptr(cond), _ptr(audio), _ptr(video), tag.data_ptr(), positions.data_ptr(),
+        mod_tables.data_ptr(), arr, len(blocks), final_tables.data_ptr(), sa, sv, n_steps,
+        x.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)))
 
 
 def quantized_bytes(n_rows: int, width: int) -> int:

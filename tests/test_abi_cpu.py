@@ -199,3 +199,34 @@ def test_binding_refuses_missing_library(tmp_path):
             lib.load(str(tmp_path / "nope.so"))
         finally:
             lib._lib = saved
+
+
+def test_sigma_schedule_host_function(L):
+    import numpy as np
+
+    import oracle
+    for steps, shift in ((1, 1.0), (8, 3.0), (40, 12.0), (40, 3.0)):
+        np.testing.assert_array_equal(np.array(lib.sigma_schedule(steps, shift)), oracle.schedule(steps, shift))
+    buf = (ctypes.c_double * 2)()
+    assert L.h3_sigma_schedule(0, 3.0, buf) == lib.H3_ERR_INVALID_ARG
+    assert L.h3_sigma_schedule(4, -1.0, buf) == lib.H3_ERR_INVALID_ARG
+    assert L.h3_sigma_schedule(4, 3.0, None) == lib.H3_ERR_INVALID_ARG
+
+
+def test_denoise_argument_errors_before_launch(L):
+    d = lib.make_dims(synth.TINY_DIMS)
+    io = lib.make_io_dims(synth.TINY_IO)
+    sg = lib.make_segments(16, 0, 20, 128)
+    w = _io_weights()
+    arr = (lib.H3BlockWeights * 1)(_full_weights())
+    sig = (ctypes.c_double * 3)(1.0, 0.5, 0.0)
+    ws = L.h3_workspace_size(ctypes.byref(d), 164)
+
+    def call(n_steps=2, n_blocks=1, sa=sig, ws_bytes=ws):
+        return L.h3_denoise(ctypes.byref(d), ctypes.byref(io), ctypes.byref(w), ctypes.byref(sg),
+                            FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, arr, n_blocks, FAKE, sa, sig,
+                            n_steps, FAKE, FAKE, ws_bytes, None)
+    assert call(n_steps=0) == lib.H3_ERR_INVALID_ARG
+    assert call(n_blocks=0) == lib.H3_ERR_INVALID_ARG
+    assert call(sa=None) == lib.H3_ERR_INVALID_ARG and "sigmas" in lib.last_error()
+    assert call(ws_bytes=ws - 256) == lib.H3_ERR_WORKSPACE
