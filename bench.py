@@ -304,6 +304,8 @@ def main():
                          "the known-size reference for HBM byte counters")
     ap.add_argument("--single-block", type=int, default=1,
                     help="also time one H3 block at N=1192 with bf16 and INT8 weights (0: skip)")
+    ap.add_argument("--denoise-steps", type=int, default=4,
+                    help="Euler passes of the denoising loop timed at the secondary workload (0: skip)")
     ap.add_argument("--sparse", type=int, default=1,
                     help="also time block-sparse attention and the sparse forward (0: skip)")
     ap.add_argument("--w8a8", type=int, default=1,
@@ -398,6 +400,44 @@ def main():
             "forward_mfma_frac": round(wl2.n_blocks * w2.total_flop / sec2 / 1e12 / PEAK, 4),
             "per_step_kernels": bd2,
         }
+    if args.denoise_steps > 0 and args.secondary != "none":
+        # the denoising loop at the secondary workload: inputs -> velocity ->
+        # Euler, video shift 12 and audio shift 3, tables per pass
+        wl2 = synth.WORKLOADS[args.secondary]
+        steps_d = args.denoise_steps
+        log(f"denoising loop: {wl2.name}, {steps_d} passes")
+        io = synth.H3_IO
+        g = torch.Generator(device="cuda")
+        g.manual_seed(11)
+        tabs = (torch.randn(steps_d, wl2.n_blocks, dims.n_tags, 6, dims.hidden, generator=g, device="cuda")
+                * 0.316).to(torch.bfloat16)
+        fins = (torch.randn(steps_d, 2, 2, dims.hidden, generator=g, device="cuda") * 0.316).to(torch.bfloat16)
+        inp = synth.make_io_inputs(wl2, io, seed=0)
+        w_host = synth.make_io_weights(dims, io, seed=0)
+        dv = lambda a: (None if a is None or len(a) == 0 else  # noqa: E731
+                        torch.from_numpy(a.view("int16") if a.dtype.name == "uint16" else a).cuda())
+        iw = {k: dv(v) for k, v in w_host.items()}
+        d = {k: dv(v) for k, v in inp.items()}
+        _, tags2, pos2 = synth.make_device_rows(wl2, seed=0)
+        x2 = torch.empty(wl2.n_rows, dims.hidden, dtype=torch.float32, device="cuda")
+        ws2 = lib.alloc_workspace(dims, wl2.n_rows)
+        sa, sv = lib.sigma_schedule(steps_d, 3.0), lib.sigma_schedule(steps_d, 12.0)
+        run = lambda: lib.denoise(dims, io, iw, d["text"], d["cond"], d["audio"], d["video"], tags2, pos2,  # noqa: E731
+                                  tabs, blocks[:wl2.n_blocks], fins, sa, sv, x2, ws2)
+        run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run()
+        torch.cuda.synchronize()
+        secd = time.perf_counter() - t0
+        assert bool(torch.isfinite(d["video"]).all()), "non-finite latents"
+        result["denoise"] = {"workload": wl2.name, "passes": steps_d, "shifts": {"video": 12.0, "audio": 3.0},
+                             "s_per_loop": round(secd, 4), "ms_per_pass": round(secd / steps_d * 1e3, 2),
+                             "packed_tokens_per_s_per_pass": round(wl2.n_rows * steps_d / secd, 2),
+                             "pass_over_dit_forward": round(secd / steps_d / result["secondary"]["ms_per_step"]
+                                                            * 1e3, 4)}
+        log(f"denoising loop: {secd * 1e3:.1f} ms for {steps_d} passes")
+        del ws2, x2, tabs, fins
     if args.sparse:
         # block-sparse attention (a fixed budget of key tiles per query tile)
         # at the primary workload: the kernel alone, then the 50-block forward
