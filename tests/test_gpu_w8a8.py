@@ -182,3 +182,28 @@ def test_w8a8_forward_matches_oracle(wname, nb, tol):
     e_out, e_delta = rel_l2(got, ref), rel_l2(got - x, ref - x)
     say("w8a8 rel-L2 x_out", e_out, "update", e_delta)
     assert e_out < tol and e_delta < 2 * tol
+
+
+def test_fullsize_w8a8_block_n6437_sampled_rows():
+    """One W8A8 block at N = 6,437 (the 50-block workload's packed layout), in
+    the launch configuration of the forward, compared on sampled output rows;
+    keys and values use every row (quantization is per row, so the oracle's
+    sampled rows see exactly the rows the GPU computed them from)."""
+    wl = synth.WORKLOADS["h3_50blk_n6437_w8a8"]
+    say("fullsize w8a8 block", wl.n_rows)
+    host = synth.make_block_weights(wl.dims, 0, seed=17)
+    tags, pos = synth.packed_layout(wl)
+    x = synth.make_x(wl, wl.dims, seed=17)
+    table = synth.make_table(wl.dims, 1, seed=17)
+    xd = dev(x)
+    ws = lib.alloc_workspace(wl.dims, wl.n_rows)
+    lib.dit_block_forward(wl.dims, xd, dev(tags), dev(pos), dev(table[0]), lib.to_device_block(host), ws)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(5).choice(wl.n_rows, size=21, replace=False)
+    rows = np.unique(np.concatenate([r, [0, wl.n_rows // 2, wl.n_rows - 1]]))
+    got = xd.cpu().numpy().astype(np.float64)[rows]
+    ref = oracle.block_forward(x, tags, pos, table[0], host, wl.dims, q_rows=rows)
+    xr = x[rows].astype(np.float64)
+    say("fullsize w8a8 rel-L2", rel_l2(got, ref), rel_l2(got - xr, ref - xr))
+    assert rel_l2(got, ref) < TOL_BLOCK
+    assert rel_l2(got - xr, ref - xr) < 2 * TOL_BLOCK
