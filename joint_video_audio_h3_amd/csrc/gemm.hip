@@ -714,7 +714,9 @@ __global__ __launch_bounds__(512) void gemm_w8_kernel(GemmArgs p) {
   static_assert(EPI != EPI_QKV || TN == SEC, "QKV wave tile must be one head section");
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU needs paired gate/value tiles");
 
-  __shared__ __attribute__((aligned(1024))) char sm[4 * ABUF];
+  // two LDS buffers during the K loop; the epilogue stages 32 rows per wave here
+  constexpr int EPI_BYTES = 8 * 32 * (RSTRIDE > QSTRIDE ? RSTRIDE : QSTRIDE) * 4;
+  __shared__ __attribute__((aligned(1024))) char sm[4 * ABUF > EPI_BYTES ? 4 * ABUF : EPI_BYTES];
   __shared__ int s_tag[EPI == EPI_RESID ? BM : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -874,7 +876,17 @@ __global__ __launch_bounds__(512) void gemm_w8_kernel(GemmArgs p) {
     stage(ic<1>{}, kt + 1);
   }
   __syncthreads();
-  epilogue<BM, BN, WM, WN, EPI, SEC>(p, acc, m0, n0, tc.tn, wm, wn, lane, s_tag);
+  if constexpr (EPI == EPI_RESID) {
+    resid_epilogue_lds<true, TM, TN, FM, FN>(p, acc, m0 + wm * TM, n0 + wn * TN, lane,
+                                             reinterpret_cast<float*>(sm) + wave * 32 * RSTRIDE, s_tag + wm * TM);
+  } else if constexpr (EPI == EPI_QKV && SEC == 128) {
+    const int sec = (n0 + wn * TN) / SEC;
+    if (sec < 3 * p.heads)
+      qkv_epilogue_lds<TM, FM, FN>(p, acc, m0 + wm * TM, sec, lane,
+                                   reinterpret_cast<float*>(sm) + wave * 32 * QSTRIDE);
+  } else {
+    epilogue<BM, BN, WM, WN, EPI, SEC>(p, acc, m0, n0, tc.tn, wm, wn, lane, s_tag);
+  }
 }
 
 // ============================================================ dispatch
@@ -953,7 +965,9 @@ hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   }
   switch (epi) {   // (EPI_STORE layers have bf16 weights only)
-    case EPI_RESID: return run_w8<EPI_RESID, 0, 256>(a, s);
+    case EPI_RESID:
+      if (resid_prefers_192(a)) return run_w8<EPI_RESID, 0, 192>(a, s);
+      return run_w8<EPI_RESID, 0, 256>(a, s);
     case EPI_SWIGLU: return run_w8<EPI_SWIGLU, 0, 256>(a, s);
     case EPI_QKV:
       if (a.head_dim == 128) return run_w8<EPI_QKV, 128, 256>(a, s);
