@@ -43,7 +43,8 @@
 //             measure, do not reason": x + gate * f(x)).  fp32 in place.
 //  EPI_SWIGLU weights rows are [gate; value]; each wave's N range is half gate
 //             rows and half the matching value rows, so silu(g)*v is formed in
-//             registers and only the F-wide activation is written
+//             registers (staged through LDS for 16-byte row stores) and only
+//             the F-wide activation is written
 //             (minimax-h3-mlx README, "Validation": fc2(silu(gate) * value);
 //             H3-metal digest, "Metal 4 and TensorOps paths": paired gate/up
 //             tiles apply SwiGLU before writing).
@@ -280,6 +281,52 @@ __device__ __forceinline__ void resid_epilogue_lds(const GemmArgs& p, f32x16 (&a
         }
         *reinterpret_cast<float4*>(p.x + (size_t)row * p.ldx + gcol) = x;
       }
+    }
+  }
+}
+
+// SwiGLU through LDS: a wavefront's N range is TN/2 gate columns and the
+// matching TN/2 value columns; a = silu(g) * u is formed in registers, staged
+// 32 rows at a time as fp32, and read back 8 values per lane along rows, so
+// each row's TN/2 bf16 outputs (one 128-byte line for TN = 128) go out as
+// 16-byte stores by 8 lanes.
+constexpr int SSTRIDE = 68;   // floats per staged row (64 + 4 of padding)
+
+template <int TM, int TN, int FM, int FN>
+__device__ __forceinline__ void swiglu_epilogue_lds(const GemmArgs& p, f32x16 (&acc)[FM][FN],
+                                                    int row0, int oc0, int lane, float* stage) {
+  static_assert(TN == 128, "a wavefront writes 64 output columns per row");
+  constexpr int H = FN / 2;
+  const int hl = lane >> 5, lc = lane & 31;
+  float bg[H], bv[H];
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    bg[j] = p.bias ? bf2f(p.bias[oc0 + j * 32 + lc]) : 0.f;
+    bv[j] = p.bias ? bf2f(p.bias[p.ffn + oc0 + j * 32 + lc]) : 0.f;
+  }
+  const int rr = lane >> 3, cc = 8 * (lane & 7);   // read-back: row rr (+8q), columns cc..cc+7
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < H; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float g = acc[i][j][v] + bg[j];
+        const float u = acc[i][j + H][v] + bv[j];
+        // silu(g) = g * 1/(1 + e^-g) with the hardware reciprocal (~1 ulp,
+        // far below the bf16 rounding of the result); e^-g = inf gives 0
+        stage[(8 * (v / 4) + 4 * hl + (v % 4)) * SSTRIDE + j * 32 + lc] =
+            g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+      }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 8 * q + rr;
+      const int row = row0 + i * 32 + r;
+      const float4 a0 = *reinterpret_cast<const float4*>(stage + r * SSTRIDE + cc);
+      const float4 a1 = *reinterpret_cast<const float4*>(stage + r * SSTRIDE + cc + 4);
+      if (row < p.M)
+        *reinterpret_cast<uint4*>(p.out + (size_t)row * p.ffn + oc0 + cc) =
+            make_uint4(pack2bf(a0.x, a0.y), pack2bf(a0.z, a0.w), pack2bf(a1.x, a1.y), pack2bf(a1.z, a1.w));
     }
   }
 }
@@ -686,6 +733,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (sec < 3 * p.heads)
       qkv_epilogue_lds<TM, FM, FN>(p, acc, m0 + wm * TM, sec, lane,
                                    reinterpret_cast<float*>(ring) + wave * 32 * QSTRIDE);
+  } else if constexpr (EPI == EPI_SWIGLU && TN == 128) {
+    swiglu_epilogue_lds<TM, TN, FM, FN>(p, acc, m0 + wm * TM, tc.tn * (BN / 2) + wn * (TN / 2), lane,
+                                        reinterpret_cast<float*>(ring) + wave * 32 * SSTRIDE);
   } else {
     epilogue<BM, BN, WM, WN, EPI, SEC>(p, acc, m0, n0, tc.tn, wm, wn, lane, nullptr);
   }
@@ -884,6 +934,9 @@ __global__ __launch_bounds__(512) void gemm_w8_kernel(GemmArgs p) {
     if (sec < 3 * p.heads)
       qkv_epilogue_lds<TM, FM, FN>(p, acc, m0 + wm * TM, sec, lane,
                                    reinterpret_cast<float*>(sm) + wave * 32 * QSTRIDE);
+  } else if constexpr (EPI == EPI_SWIGLU && TN == 128) {
+    swiglu_epilogue_lds<TM, TN, FM, FN>(p, acc, m0 + wm * TM, tc.tn * (BN / 2) + wn * (TN / 2), lane,
+                                        reinterpret_cast<float*>(sm) + wave * 32 * SSTRIDE);
   } else {
     epilogue<BM, BN, WM, WN, EPI, SEC>(p, acc, m0, n0, tc.tn, wm, wn, lane, s_tag);
   }
