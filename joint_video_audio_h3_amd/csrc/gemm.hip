@@ -108,111 +108,72 @@ __device__ __forceinline__ int weight_row(const GemmArgs& p, int tn, int r) {
   return min(tn * BN + r, p.n_out - 1);
 }
 
+// Per-element QKV epilogue for head sections other than 128 wide (the
+// 96-wide sections of the small model); the wider sections and the other
+// epilogues go through LDS (below).
 template <int BM, int BN, int WM, int WN, int EPI, int SEC, int FM, int FN>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], int m0, int n0,
                                          int tn, int wm, int wn, int lane, const int* s_tag) {
+  static_assert(EPI == EPI_QKV, "only the QKV sections that the LDS path does not take come here");
   constexpr int TM = BM / WM, TN = BN / WN;
   const int hl = lane >> 5;     // half-wave: rows 4..7 of each group of 8
   const int lc = lane & 31;     // column within a 32-wide MFMA tile
   const int row_base = m0 + wm * TM;
-
-  if constexpr (EPI == EPI_RESID) {
+  (void)tn;
+  (void)s_tag;
+  const int sec = (n0 + wn * TN) / SEC;
+  if (sec >= 3 * p.heads) return;
+  const int kind = sec % 3, head = sec / 3;
+  const uint16_t* gam = kind == 0 ? p.gq : p.gk;
+  float bias_c[FN], gain_c[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn * TN + j * 32 + lc;
-      if (col >= p.n_out) continue;
-      const float b = p.bias ? bf2f(p.bias[col]) : 0.f;
+  for (int j = 0; j < FN; ++j) {
+    const int c = j * 32 + lc;
+    bias_c[j] = p.bias ? bf2f(p.bias[sec * SEC + c]) : 0.f;
+    gain_c[j] = (kind < 2 && gam) ? bf2f(gam[c]) : 1.f;
+  }
+  const float2* cs = reinterpret_cast<const float2*>(p.cs);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < FM; ++i) {
+    float u[FN][16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int rl = wm * TM + i * 32 + 8 * (v / 4) + 4 * hl + (v % 4);
-          const int row = m0 + rl;
-          if (row < p.M) {
-            const float g = bf2f(p.gate_tab[(size_t)s_tag[rl] * p.tag_stride + col]);
-            float* xp = p.x + (size_t)row * p.ldx + col;
-            *xp = *xp + g * (acc[i][j][v] + b);
-          }
-        }
-      }
-    }
-  } else if constexpr (EPI == EPI_SWIGLU) {
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-    for (int j = 0; j < FN / 2; ++j) {
-      const int oc = tn * (BN / 2) + wn * (TN / 2) + j * 32 + lc;
-      const float bg = p.bias ? bf2f(p.bias[oc]) : 0.f;
-      const float bv = p.bias ? bf2f(p.bias[p.ffn + oc]) : 0.f;
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = row_base + i * 32 + 8 * (v / 4) + 4 * hl + (v % 4);
-          if (row < p.M) {
-            const float g = acc[i][j][v] + bg;
-            const float u = acc[i][j + FN / 2][v] + bv;
-            // silu(g) = g * 1/(1 + e^-g) with the hardware reciprocal (~1 ulp,
-            // far below the bf16 rounding of the result); e^-g = inf gives 0
-            const float a = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-            p.out[(size_t)row * p.ffn + oc] = f2bf(a);
-          }
-        }
-      }
-    }
-  } else {  // EPI_QKV
-    const int sec = (n0 + wn * TN) / SEC;
-    if (sec >= 3 * p.heads) return;
-    const int kind = sec % 3, head = sec / 3;
-    const uint16_t* gam = kind == 0 ? p.gq : p.gk;
-    float bias_c[FN], gain_c[FN];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int c = j * 32 + lc;
-      bias_c[j] = p.bias ? bf2f(p.bias[sec * SEC + c]) : 0.f;
-      gain_c[j] = (kind < 2 && gam) ? bf2f(gam[c]) : 1.f;
-    }
-    const float2* cs = reinterpret_cast<const float2*>(p.cs);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      float u[FN][16];
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) u[j][v] = acc[i][j][v] + bias_c[j];
-      if (kind < 2) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float ss = 0.f;
-#pragma unroll
-          for (int j = 0; j < FN; ++j) ss += u[j][v] * u[j][v];
-          ss = half_sum(ss);
-          const float r = 1.0f / sqrtf(ss / (float)SEC + p.qk_eps);
-          const int row = row_base + i * 32 + 8 * (v / 4) + 4 * hl + (v % 4);
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const float t = u[j][v] * r * gain_c[j];
-            const float partner = __shfl_xor(t, 1, 64);
-            const int c = j * 32 + lc;
-            const float2 sc = cs[(size_t)row * (SEC / 2) + c / 2];
-            float o = (c & 1) ? partner * sc.y + t * sc.x : t * sc.x - partner * sc.y;
-            if (kind == 0) o *= p.q_scale;
-            u[j][v] = o;
-          }
-        }
-      }
-      uint16_t* dst = kind == 0 ? p.q : p.k;
+      for (int v = 0; v < 16; ++v) u[j][v] = acc[i][j][v] + bias_c[j];
+    if (kind < 2) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) ss += u[j][v] * u[j][v];
+        ss = half_sum(ss);
+        const float r = 1.0f / sqrtf(ss / (float)SEC + p.qk_eps);
         const int row = row_base + i * 32 + 8 * (v / 4) + 4 * hl + (v % 4);
-        const bool valid = row < p.M;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
+          const float t = u[j][v] * r * gain_c[j];
+          const float partner = __shfl_xor(t, 1, 64);
           const int c = j * 32 + lc;
-          const uint16_t val = valid ? f2bf(u[j][v]) : (uint16_t)0;
-          if (kind < 2) {
-            dst[((size_t)head * p.n_pad + row) * SEC + c] = val;
-          } else {
-            p.vt[((size_t)head * SEC + c) * p.n_pad + row] = val;
-          }
+          const float2 sc = cs[(size_t)row * (SEC / 2) + c / 2];
+          float o = (c & 1) ? partner * sc.y + t * sc.x : t * sc.x - partner * sc.y;
+          if (kind == 0) o *= p.q_scale;
+          u[j][v] = o;
+        }
+      }
+    }
+    uint16_t* dst = kind == 0 ? p.q : p.k;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = row_base + i * 32 + 8 * (v / 4) + 4 * hl + (v % 4);
+      const bool valid = row < p.M;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int c = j * 32 + lc;
+        const uint16_t val = valid ? f2bf(u[j][v]) : (uint16_t)0;
+        if (kind < 2) {
+          dst[((size_t)head * p.n_pad + row) * SEC + c] = val;
+        } else {
+          p.vt[((size_t)head * SEC + c) * p.n_pad + row] = val;
         }
       }
     }
@@ -649,12 +610,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int j = 0; j < FN; ++j) fb[j] = lds_read16(rB[0][j & 1][kk] + xb_ + j * 32 * DROW);
     };
-    auto ld = [&](const char* base, const uint32_t (&vo)[NA > NB ? NA : NB], uint32_t slot, int ks, int lo, int hi) __attribute__((always_inline)) {
-      const char* sb = base + (size_t)ks * (DBK * 2);
-#pragma unroll
-      for (int s = lo; s < hi; ++s) dma16s(vo[s], sb, mw + slot + s * 4096);
-    };
-    (void)ld;
     group(fa0, fb0, [&]() __attribute__((always_inline)) { rd(oa, ob, 1, fa1, fb1); },
           [&](int q) __attribute__((always_inline)) {
             if (n1) {
