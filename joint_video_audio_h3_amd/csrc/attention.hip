@@ -10,7 +10,7 @@
 // two 32-key halves.  A wave needs under 256 registers, so two waves share each
 // SIMD and one's softmax runs beside the other's matrix work (VALU from one
 // wave co-issues with the other's MFMAs).  K and V^T tiles stream HBM/L2 ->
-// LDS with global_load_lds_dwordx4 into a 3-slot ring (two tiles in flight
+// LDS with global_load_lds_dwordx4 into a 4-slot ring (three tiles in flight
 // while one is consumed), XOR-swizzled so the 16-byte fragment reads are
 // bank-conflict free.  The key loop is unrolled by the ring period so every
 // slot offset is an immediate: loads take an SGPR tile base plus a fixed
@@ -87,7 +87,7 @@ __device__ __forceinline__ int att_vswz(int r) { return ((r & 31) ^ ((r & 31) >>
 
 template <int HD, int W, bool SPARSE>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnArgs p) {
-  constexpr int ATT_SLOTS = SPARSE ? 2 : 3;   // LDS ring depth (tiles)
+  constexpr int ATT_SLOTS = SPARSE ? 2 : 4;   // LDS ring depth (tiles)
   constexpr int BQ = W * 32;                  // queries per block
   constexpr int DS = HD / 16;             // MFMA k-steps over head_dim
   constexpr int DT = HD / 32;             // 32-row tiles of head_dim in O^T
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   constexpr int NI = (NK + NV + W - 1) / W;               // per wavefront (last may idle)
   constexpr int NIK = NK / W;                             // first NIK loads are K
   static_assert(NK % W == 0, "K loads must split evenly over the waves");
-  static_assert(ATT_SLOTS * STAGE < 2 * 65536, "two 64 KB read windows");
+  static_assert(ATT_SLOTS * STAGE <= 2 * 65536, "two 64 KB read windows");
   __shared__ __attribute__((aligned(1024))) char ring[ATT_SLOTS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -146,6 +146,17 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
   }
   const bool has_last = wave + W * (NI - 1) < NK + NV;   // wave-uniform: the last load exists
+  // wait until at most T tiles of this wave's loads are in flight (a wave
+  // without the last load issues NI - 1 per tile)
+  auto wait_tiles = [&](auto T_) __attribute__((always_inline)) {
+    constexpr int T = decltype(T_)::value;
+    if constexpr ((NK + NV) % W == 0) {
+      att_wait_vmcnt<T * NI>();
+    } else {
+      if (has_last) att_wait_vmcnt<T * NI>();
+      else att_wait_vmcnt<T * (NI - 1)>();
+    }
+  };
   auto issue = [&](int kt, uint32_t slot_off) __attribute__((always_inline)) {
     const char* kb = kbase0 + (size_t)kt * (ATT_BKV * HD * 2);
     const char* vb = vbase0 + (size_t)kt * (ATT_BKV * 2);
@@ -271,13 +282,13 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   };
 
   // steady tile with compile-time slot U: wait for tile kt, barrier, refill the
-  // slot freed by tile kt-1 with tile kt+2, consume tile kt
+  // slot freed by tile kt-1 with tile kt+3, consume tile kt
   auto tile_c = [&](auto U_, int kt) __attribute__((always_inline)) {
     constexpr int U = decltype(U_)::value;
     constexpr int SO = U * STAGE;
-    att_wait_vmcnt<NI>();
+    wait_tiles(att_ic<2>{});
     __builtin_amdgcn_s_barrier();
-    issue(kt + 2, (uint32_t)(((U + 2) % ATT_SLOTS) * STAGE));
+    issue(kt + 3, (uint32_t)(((U + 3) % ATT_SLOTS) * STAGE));
     tile_body([&](int ks, int ds) __attribute__((always_inline)) { return kread(att_ic<SO>{}, ks, ds); },
               [&](int t, int s) __attribute__((always_inline)) { return vread(att_ic<SO>{}, t, s); }, kt, false,
               kt == 0);
@@ -285,13 +296,15 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // the same with the slot from the runtime phase (the last few tiles)
   auto tile_r = [&](int kt) __attribute__((always_inline)) {
     const uint32_t so = (uint32_t)((kt % ATT_SLOTS) * STAGE);
-    if (kt + 1 < KT) {
-      att_wait_vmcnt<NI>();
+    if (kt + 2 < KT) {
+      wait_tiles(att_ic<2>{});
+    } else if (kt + 1 < KT) {
+      wait_tiles(att_ic<1>{});
     } else {
       att_wait_vmcnt<0>();
     }
     __builtin_amdgcn_s_barrier();
-    if (kt + 2 < KT) issue(kt + 2, (uint32_t)(((kt + 2) % ATT_SLOTS) * STAGE));
+    if (kt + 3 < KT) issue(kt + 3, (uint32_t)(((kt + 3) % ATT_SLOTS) * STAGE));
     tile_body([&](int ks, int ds) __attribute__((always_inline)) { return att_read16(kbr[0][ds] + so + ks * 32 * KROW); },
               [&](int t, int s) __attribute__((always_inline)) { return att_read16(vbr[0][s] + so + KBYTES + t * 32 * VROW); },
               kt, kt + 1 == KT, kt == 0);
@@ -300,11 +313,13 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   if constexpr (!SPARSE) {
     issue(0, 0);
     if (KT > 1) issue(1, STAGE);
+    if (KT > 2) issue(2, 2 * STAGE);
     int kt = 0;
-    for (; kt + 5 <= KT; kt += 3) {
+    for (; kt + 7 <= KT; kt += 4) {   // the last of the four issues tile kt + 6
       tile_c(att_ic<0>{}, kt);
       tile_c(att_ic<1>{}, kt + 1);
       tile_c(att_ic<2>{}, kt + 2);
+      tile_c(att_ic<3>{}, kt + 3);
     }
     for (; kt < KT; ++kt) tile_r(kt);
   } else {
