@@ -4,8 +4,9 @@
 A step is one denoising forward: the 50-block DiT over one packed sequence,
 inputs and weights resident in HBM, run through the C ABI (h3_dit_forward).
 Primary workload: N = 49,840 packed rows (L 256 | C 1024 | A 200 | V 31x30x52);
-secondary: N = 6,437 (L 256 | A 37 | V 6x32x32).  Both use the same 50 blocks
-of synthetic bf16 weights (random init, H3 shapes).
+secondary: N = 6,437 (L 256 | A 37 | V 6x32x32); extra: N = 7,461 (the same
+with a 1,024-row reference image, C = 1024).  All use the same 50 blocks of
+synthetic bf16 weights (random init, H3 shapes).
 
 Printed: one JSON line with packed tokens/s per forward, the per-step kernel
 times (HIP events on the launch stream) with their TFLOP/s and fraction of the
@@ -31,7 +32,7 @@ HBM = perf_model.PEAK_HBM_GBS
 # HBM traffic of the dominant kernels from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE,
 # bytes per launch after the copy-kernel calibration (see profiles/); None when
 # the kernel changed after the counters were taken.
-TRAFFIC_BYTES = {("h3_50blk_n49840", "attention"): 21.27e9}
+TRAFFIC_BYTES = {("h3_50blk_n49840", "attention"): 21.22e9}
 
 
 def log(*a):
@@ -297,6 +298,8 @@ def main():
     ap.add_argument("--workload", default="h3_50blk_n49840")
     ap.add_argument("--secondary", default="h3_50blk_n6437", help="'none' to skip")
     ap.add_argument("--secondary-steps", type=int, default=5)
+    ap.add_argument("--extra", default="h3_50blk_n7461",
+                    help="comma-separated further 50-block workloads timed like the secondary ('none' to skip)")
     ap.add_argument("--breakdown-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -399,6 +402,17 @@ def main():
             "forward_tflops": round(wl2.n_blocks * w2.total_flop / sec2 / 1e12, 1),
             "forward_mfma_frac": round(wl2.n_blocks * w2.total_flop / sec2 / 1e12 / PEAK, 4),
             "per_step_kernels": bd2,
+        }
+    for name in [x for x in args.extra.split(",") if x and x != "none"]:
+        wl3 = synth.WORKLOADS[name]
+        sec3, bd3, w3 = measure(wl3, args.secondary_steps, 1)
+        result.setdefault("extra", {})[name] = {
+            "n_rows": wl3.n_rows, "packed": {"L": wl3.L, "C": wl3.C, "A": wl3.A, "V": list(wl3.V)},
+            "value": round(wl3.n_rows / sec3, 2), "unit": "packed tokens/s",
+            "ms_per_step": round(sec3 * 1e3, 2), "steps": args.secondary_steps,
+            "forward_tflops": round(wl3.n_blocks * w3.total_flop / sec3 / 1e12, 1),
+            "forward_mfma_frac": round(wl3.n_blocks * w3.total_flop / sec3 / 1e12 / PEAK, 4),
+            "per_step_kernels": bd3,
         }
     if args.denoise_steps > 0 and args.secondary != "none":
         # the denoising loop at the secondary workload: inputs -> velocity ->
