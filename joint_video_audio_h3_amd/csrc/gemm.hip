@@ -30,9 +30,12 @@
 // bf16(q * s) (one bf16 scale per 32 K elements) on their way into a
 // double-buffered LDS stage, interleaved with the MFMAs of the stage before.
 //
-// Block ids are remapped so that each XCD (blocks are dealt round-robin to the
-// 8 XCDs) walks a contiguous run of a grouped tile order in which consecutive
-// tiles share the same weight tile in that XCD's L2.
+// Block ids are remapped with the XCD in mind (blocks are dealt round-robin to
+// the 8 XCDs): the 32 tiles an XCD runs at once are 8 row tiles x 4 column
+// tiles, so each stage's A and B slices are shared in that XCD's L2; and over
+// whole groups of 64 row tiles the eight XCDs take 8 row tiles each and walk
+// the column tiles in step, so a weight panel comes from HBM once and the
+// other seven XCDs find it in the shared Infinity Cache.
 //
 // MFMA 32x32 accumulator layout: lane l, register v holds
 //   row = 8*(v/4) + 4*(l/32) + (v%4),   col = l%32.
@@ -85,16 +88,29 @@ template <int EPI, int BM, int BN>
 __device__ __forceinline__ TileCoord tile_coord(const GemmArgs& p) {
   const int tiles_m = (EPI == EPI_QKV) ? p.n_pad / BM : (p.M + BM - 1) / BM;
   const int tiles_n = (p.n_out + BN - 1) / BN;
-  const int total = tiles_m * tiles_n;
-  const int raw = blockIdx.x;
-  const int per = total / 8, rem = total % 8;
-  const int xcd = raw % 8, local = raw / 8;
-  const int pid = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
   constexpr int GROUP_M = 8;
+  const int raw = blockIdx.x;
+  const int xcd = raw % 8;
+  // full super-groups of 8 x GROUP_M row tiles: XCD x takes rows [8x, 8x + 8) of
+  // each and all XCDs walk the column tiles in step (shared weight panels)
+  const int sgt = 8 * GROUP_M * tiles_n;
+  const int full = tiles_m / (8 * GROUP_M);
+  if (raw < full * sgt) {
+    const int local = raw / 8;
+    const int sg = local / (GROUP_M * tiles_n), l = local % (GROUP_M * tiles_n);
+    return {sg * 8 * GROUP_M + xcd * GROUP_M + l % GROUP_M, l / GROUP_M};
+  }
+  // the remaining row tiles: contiguous runs per XCD, grouped GROUP_M rows at a time
+  const int rm0 = full * 8 * GROUP_M, rtm = tiles_m - rm0;
+  const int rraw = raw - full * sgt;
+  const int total = rtm * tiles_n;
+  const int per = total / 8, rem = total % 8;
+  const int local = rraw / 8;
+  const int pid = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
   const int in_group = GROUP_M * tiles_n;
   const int first_m = (pid / in_group) * GROUP_M;
-  const int gsz = min(tiles_m - first_m, GROUP_M);
-  return {first_m + (pid % in_group) % gsz, (pid % in_group) / gsz};
+  const int gsz = min(rtm - first_m, GROUP_M);
+  return {rm0 + first_m + (pid % in_group) % gsz, (pid % in_group) / gsz};
 }
 
 // Weight row feeding tile column r of tile tn (SwiGLU pairs gate and value rows per wave).
