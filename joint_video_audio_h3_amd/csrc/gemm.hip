@@ -32,10 +32,11 @@
 //
 // Block ids are remapped with the XCD in mind (blocks are dealt round-robin to
 // the 8 XCDs): the 32 tiles an XCD runs at once are 8 row tiles x 4 column
-// tiles, so each stage's A and B slices are shared in that XCD's L2; and over
-// whole groups of 64 row tiles the eight XCDs take 8 row tiles each and walk
-// the column tiles in step, so a weight panel comes from HBM once and the
-// other seven XCDs find it in the shared Infinity Cache.
+// tiles (4 x 8 when K >= 7168), so each stage's A and B slices are shared in
+// that XCD's L2; and over whole groups of 8 x that many row tiles the eight
+// XCDs take one share each and walk the column tiles in step, so a weight
+// panel comes from HBM once and the other seven XCDs find it in the shared
+// Infinity Cache.
 //
 // MFMA 32x32 accumulator layout: lane l, register v holds
 //   row = 8*(v/4) + 4*(l/32) + (v%4),   col = l%32.
@@ -88,11 +89,13 @@ template <int EPI, int BM, int BN>
 __device__ __forceinline__ TileCoord tile_coord(const GemmArgs& p) {
   const int tiles_m = (EPI == EPI_QKV) ? p.n_pad / BM : (p.M + BM - 1) / BM;
   const int tiles_n = (p.n_out + BN - 1) / BN;
-  constexpr int GROUP_M = 8;
+  // row tiles per XCD group: 8 x 4 tiles run at once, or 4 x 8 for long K, whose
+  // activation panels are too large to stay cached across passes over the columns
+  const int GROUP_M = p.K >= 7168 ? 4 : 8;
   const int raw = blockIdx.x;
   const int xcd = raw % 8;
-  // full super-groups of 8 x GROUP_M row tiles: XCD x takes rows [8x, 8x + 8) of
-  // each and all XCDs walk the column tiles in step (shared weight panels)
+  // full super-groups of 8 x GROUP_M row tiles: XCD x takes GROUP_M of them and
+  // all XCDs walk the column tiles in step (shared weight panels)
   const int sgt = 8 * GROUP_M * tiles_n;
   const int full = tiles_m / (8 * GROUP_M);
   if (raw < full * sgt) {
