@@ -25,7 +25,11 @@
 //   O^T[dd][query] += V^T[dd][key] . P^T[key][query]
 // with V^T written by the QKV epilogue (keys contiguous).  Both halves' score
 // products are issued before the first half's softmax, so a wave's own matrix
-// work runs under its exponentials.
+// work runs under its exponentials.  Every 16-byte fragment read is issued a
+// whole product (8 MFMAs) ahead of its use: a tile starts with the K fragments
+// of its first half, and each MFMA of a product is paired with one read for the
+// next (second half's K, then the V^T of each half).  One fragment per MFMA
+// puts the LDS read port near its limit, so its latency has to be covered.
 //
 // Softmax: q arrives pre-scaled by log2(e)/sqrt(d), so scores are in log2
 // units and p = exp2(s - m).  The reference point m of each query is folded
@@ -201,15 +205,6 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
   const int KT = (p.n + ATT_BKV - 1) / ATT_BKV;
 
-  // S^T = K Q^T - m for one half (K fragments from `kr`)
-  auto scores = [&](auto&& kr, int ks) __attribute__((always_inline)) {
-    f32x16 s;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = -m_ref;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) s = mfma32(kr(ks, ds), qf[ds], s);
-    return s;
-  };
   // p = exp2(s) as bf16 pairs and their sum
   auto probs = [&](const f32x16& s, bf16x8 (&pf)[2]) __attribute__((always_inline)) {
     float rs0 = 0.f, rs1 = 0.f;
@@ -229,7 +224,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // softmax of one half: probabilities into pf, running sum updated; the rare
   // rescale also shifts `other`, the other half's scores already formed with
   // the old reference point
-  auto softmax = [&](f32x16& s, f32x16& other, bool first, bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+  auto softmax = [&](f32x16& s, auto&& shift_other, bool first, bf16x8 (&pf)[2]) __attribute__((always_inline)) {
     float rs = probs(s, pf);
     if (first || __builtin_amdgcn_ballot_w64(!(rs <= ATT_RESCALE_SUM)) != 0) {
       float mx = s[0];
@@ -243,20 +238,11 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
       for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        s[v] -= sh;
-        other[v] -= sh;
-      }
+      for (int v = 0; v < 16; ++v) s[v] -= sh;
+      shift_other(sh);
       rs = probs(s, pf);
     }
     l_run += rs;
-  };
-  // O^T += V^T P^T for half ks (V fragments from `vr`)
-  auto pv = [&](auto&& vr, int ks, const bf16x8 (&pf)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) oacc[t] = mfma32(vr(t, 2 * ks + s2), pf[s2], oacc[t]);
   };
   auto mask = [&](f32x16& s, int key0) __attribute__((always_inline)) {
     if (key0 + 32 > p.n) {   // only the last tile can hold keys >= n
@@ -266,19 +252,58 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
   };
 
-  // one tile: both halves' scores, then each half's softmax and PV product
+  // one tile: S^T = K Q^T - m for both halves, then each half's softmax and
+  // O^T += V^T P^T.  Fragment reads run a whole product ahead: the K fragments
+  // of half 0 first, then each MFMA of a product is paired with one read for the
+  // next product (half 1's K, then half 0's V^T, then half 1's V^T)
   auto tile_body = [&](auto&& kr, auto&& vr, int kt, bool masked, bool first) __attribute__((always_inline)) {
-    f32x16 s0 = scores(kr, 0);
-    f32x16 s1 = scores(kr, 1);
+    bf16x8 ka[DS], kb[DS], va[2 * DT], vb[2 * DT];
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) ka[ds] = kr(0, ds);
+    f32x16 s0, s1;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s0[v] = -m_ref;
+    s1 = s0;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      s0 = mfma32(ka[ds], qf[ds], s0);
+      kb[ds] = kr(1, ds);
+    }
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      s1 = mfma32(kb[ds], qf[ds], s1);
+      va[ds] = vr(ds / 2, ds % 2);
+    }
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (masked) {
       mask(s0, kt * ATT_BKV);
       mask(s1, kt * ATT_BKV + 32);
     }
     bf16x8 pf[2];
-    softmax(s0, s1, first, pf);
-    pv(vr, 0, pf);
-    softmax(s1, s0, false, pf);
-    pv(vr, 1, pf);
+    softmax(s0, [&](float sh) __attribute__((always_inline)) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s1[v] -= sh;
+    }, first, pf);
+#pragma unroll
+    for (int i = 0; i < 2 * DT; ++i) {
+      oacc[i / 2] = mfma32(va[i], pf[i % 2], oacc[i / 2]);
+      vb[i] = vr(i / 2, 2 + i % 2);
+    }
+    softmax(s1, [](float) {}, false, pf);
+#pragma unroll
+    for (int i = 0; i < 2 * DT; ++i) oacc[i / 2] = mfma32(vb[i], pf[i % 2], oacc[i / 2]);
   };
 
   // steady tile with compile-time slot U: wait for tile kt, barrier, refill the
