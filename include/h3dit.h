@@ -138,7 +138,10 @@ H3DIT_API h3_status h3_dit_forward(const h3_dims* dims, float* x_packed, const i
 
 /* h3_dit_forward with block-sparse attention in every block (see
  * h3_attention_sparse): block b reads its selection from the CSR offsets
- * tile_off + b * (heads*nq + 1), which index the one array tile_idx. */
+ * tile_off + b * (heads*nq + 1), which index the one array tile_idx.  Each
+ * block's offsets follow the rules of h3_attention_sparse except that they
+ * start where that block's lists start in tile_idx; every offset must lie in
+ * [0, len(tile_idx)]. */
 H3DIT_API h3_status h3_dit_forward_sparse(const h3_dims* dims, float* x_packed, const int32_t* tag,
                                           const float* positions, const uint16_t* mod_table,
                                           const h3_block_weights* weights, int32_t n_blocks,
@@ -291,11 +294,13 @@ H3DIT_API h3_status h3_attention(const h3_dims* dims, const uint16_t* q, const u
  * nq = ceil(n_rows / tile), tile 64 or 128 (FastH3 OmniRef (Ref2VA) on Apple
  * Silicon MLX, "Opt-in M5 attention backend": selected 64/128 tiles, only
  * their valid rows visited).  tile_off int32 [heads*nq + 1] and tile_idx int32
- * are device arrays (4-byte aligned); tile_off is non-decreasing and its last
- * entry is the length of tile_idx.  Lists need not be sorted and must hold no
- * duplicates; indices outside [0, nq) are clamped, lists longer than nq are
- * cut at nq entries, an empty list gives zero rows.  q, k, vt, o as for
- * h3_attention. */
+ * are device arrays (4-byte aligned); tile_off is non-decreasing, starts at 0
+ * and its last entry is the length of tile_idx.  The library does not read
+ * them on the host: an offset outside [0, len(tile_idx)] makes the kernel read
+ * outside tile_idx.  Lists need not be sorted and must hold no duplicates (a
+ * repeated tile counts its keys twice); indices outside [0, nq) are clamped,
+ * lists longer than nq are cut at nq entries, an empty list gives zero rows.
+ * q, k, vt, o as for h3_attention. */
 H3DIT_API h3_status h3_attention_sparse(const h3_dims* dims, const uint16_t* q, const uint16_t* k,
                                         const uint16_t* vt, int64_t n_rows, int32_t tile,
                                         const int32_t* tile_off, const int32_t* tile_idx,
