@@ -7,7 +7,9 @@
 //
 // Work split: a block of 8 wavefronts takes 256 queries of one head; each
 // wavefront owns 32 queries and walks all keys in tiles of 64, processed as
-// two 32-key halves.  A wave needs under 256 registers, so two waves share each
+// two 32-key halves.  Blocks are dealt round-robin to the 8 XCDs; when the
+// heads split evenly over them, block ids are remapped so that XCD x runs whole
+// heads x, x+8, ..., and its L2 streams one head's K/V at a time.  A wave needs under 256 registers, so two waves share each
 // SIMD and one's softmax runs beside the other's matrix work (VALU from one
 // wave co-issues with the other's MFMAs).  K and V^T tiles stream HBM/L2 ->
 // LDS with global_load_lds_dwordx4 into a 4-slot ring (three tiles in flight
@@ -108,8 +110,17 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   __shared__ __attribute__((aligned(1024))) char ring[ATT_SLOTS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int head = blockIdx.y;
-  const int q0 = blockIdx.x * BQ + wave * 32;
+  // when the heads split evenly over the 8 XCDs (blocks are dealt to them
+  // round-robin), XCD x takes whole heads x, x+8, ..., so its L2 streams one
+  // head's K/V tiles at a time
+  int qb = blockIdx.x, head = blockIdx.y;
+  if (gridDim.y % 8 == 0) {
+    const int id = blockIdx.x + gridDim.x * blockIdx.y;
+    const int local = id / 8;
+    qb = local % gridDim.x;
+    head = id % 8 + 8 * (local / gridDim.x);
+  }
+  const int q0 = qb * BQ + wave * 32;
   const int hl = lane >> 5, lq = lane & 31;
   const size_t hoff = (size_t)head * p.n_pad * HD;
 
@@ -351,9 +362,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     // the selected key tiles of this (head, query tile), as 64-key LDS tiles
     constexpr int R = BQ / ATT_BKV;             // 64-key tiles per selected tile (1 or 2)
     const int nq = (p.n + BQ - 1) / BQ;
-    const int* sel = p.tile_idx + p.tile_off[head * nq + blockIdx.x];
+    const int* sel = p.tile_idx + p.tile_off[head * nq + qb];
     // a list holds at most nq distinct tiles: a longer (malformed) one is cut there
-    const int cnt = min(max(p.tile_off[head * nq + blockIdx.x + 1] - p.tile_off[head * nq + blockIdx.x], 0), nq);
+    const int cnt = min(max(p.tile_off[head * nq + qb + 1] - p.tile_off[head * nq + qb], 0), nq);
     const int nkv = cnt * R;
     auto kv_of = [&](int i) __attribute__((always_inline)) {
       const int j = min(max(sel[i / R], 0), nq - 1);
