@@ -13,4 +13,4 @@ from .h3_block import (  # noqa: F401
 from .h3_io import SEGMENTS, embed_inputs, final_heads, segment_rows, velocity_forward  # noqa: F401
 from .h3_w8a8 import linear_w8a8, quantize_rows  # noqa: F401
 from .h3_sparse import attention_sparse, selected_keys  # noqa: F401
-from .h3_sampler import base_grid, denoise, euler, schedule, shift_sigmas  # noqa: F401
+from .h3_sampler import base_grid, denoise, euler, fresh_passes, schedule, shift_sigmas  # noqa: F401

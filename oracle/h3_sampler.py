@@ -18,8 +18,14 @@ Reading of those statements, fixed by the 77:
                z_m <- z_m + (sigma_m[i+1] - sigma_m[i]) * v_m(z, sigma[i])
 With these, the video (12) and audio (3) schedules of 40 passes meet at exactly
 three base points (b = 1; 0.5 with 0.8; 0.2 with 0.5), 80 - 3 = 77.  Text and
-condition rows are not denoised.  Velocity reuse is not modelled (one model
-evaluation per pass).
+condition rows are not denoised.
+
+Whole-velocity reuse (H3-metal digest, "4. Choose a speed/quality preset"):
+with reuse r, a 20-pass run makes 20, 11 or 8 fresh model evaluations for
+r = 1, 2, 3, and the skipped transitions are extrapolated.  Reading: pass i is
+fresh when i % r == 0 or it is the last pass (the only forward schedule that
+gives those counts and starts fresh); a skipped pass steps each latent with the
+velocity of the last fresh pass.
 """
 from __future__ import annotations
 
@@ -52,15 +58,26 @@ def euler(z0, sigmas, velocity: Callable[[int, np.ndarray], np.ndarray]) -> np.n
     return z
 
 
+def fresh_passes(steps: int, reuse: int = 1) -> np.ndarray:
+    """Which of the passes evaluate the model: i % reuse == 0, and the last."""
+    i = np.arange(steps)
+    return (i % reuse == 0) | (i == steps - 1)
+
+
 def denoise(audio0, video0, sig_audio, sig_video,
-            velocity_pair: Callable[[int, np.ndarray, np.ndarray], Tuple[np.ndarray, np.ndarray]]):
-    """Joint Euler over both modalities: one velocity forward per pass gives
-    (v_audio, v_video) from the current latents, each latent steps on its own
-    schedule."""
+            velocity_pair: Callable[[int, np.ndarray, np.ndarray], Tuple[np.ndarray, np.ndarray]],
+            reuse: int = 1):
+    """Joint Euler over both modalities: a fresh pass runs one velocity forward
+    for (v_audio, v_video) from the current latents, a skipped one (reuse > 1)
+    keeps the last fresh pair; each latent steps on its own schedule."""
     a = np.asarray(audio0, np.float64).copy()
     v = np.asarray(video0, np.float64).copy()
-    for i in range(len(sig_video) - 1):
-        va, vv = velocity_pair(i, a, v)
+    steps = len(sig_video) - 1
+    fresh = fresh_passes(steps, reuse)
+    va = vv = None
+    for i in range(steps):
+        if fresh[i]:
+            va, vv = velocity_pair(i, a, v)
         a = a + (sig_audio[i + 1] - sig_audio[i]) * va
         v = v + (sig_video[i + 1] - sig_video[i]) * vv
     return a, v

@@ -3,7 +3,10 @@
 The pages' figure fixes the schedule: 40 passes with the video shift 12.0 and
 the audio shift 3.0 evaluate 77 distinct timesteps.  The Euler update is tied
 to closed forms: a constant velocity telescopes to z0 - c, and the linear field
-dz/dsigma = lambda z gives the product of (1 + lambda dt) exactly.
+dz/dsigma = lambda z gives the product of (1 + lambda dt) exactly.  Velocity
+reuse is pinned by the pages' counts of fresh evaluations (20, 11, 8 at 20
+passes for reuse 1, 2, 3), by which passes call the model, and by a linear
+field stepped along the held velocity.
 """
 import json
 import os
@@ -69,3 +72,48 @@ def test_joint_denoise_steps_each_modality_on_its_own_schedule():
     # the first pass moves audio by (sa[1]-1) and video by (sv[1]-1): different steps
     a1, v1 = S.denoise(a0, v0, sa[:2], sv[:2], lambda i, a, v: (np.ones(3), np.ones(5)))
     assert not np.isclose(a1[0] - 1.0, v1[0] - 2.0)
+
+
+def test_fresh_evaluation_counts_of_the_pages_reuse_presets():
+    g = json.load(open(GOLDEN))["velocity_reuse_20_steps"]
+    for r, count in g["fresh_evaluations"].items():
+        fresh = S.fresh_passes(g["steps"], int(r))
+        assert int(fresh.sum()) == count
+        assert fresh[0] and fresh[-1]                     # starts fresh, ends on a fresh velocity
+
+
+def test_reuse_calls_the_model_only_on_fresh_passes_and_holds_its_velocity():
+    sa, sv = S.schedule(5, 3.0), S.schedule(5, 12.0)
+    calls = []
+
+    def vel(i, a, v):
+        calls.append(i)
+        return np.full(2, float(i + 1)), np.full(3, -float(i + 1))
+
+    a, v = S.denoise(np.zeros(2), np.zeros(3), sa, sv, vel, reuse=2)
+    assert calls == [0, 2, 4]
+    held = np.array([1, 1, 3, 3, 5], dtype=float)         # velocity used at each pass
+    np.testing.assert_allclose(a, np.full(2, np.dot(np.diff(sa), held)), rtol=1e-13)
+    np.testing.assert_allclose(v, np.full(3, -np.dot(np.diff(sv), held)), rtol=1e-13)
+
+
+def test_reuse_on_a_linear_field_extrapolates_along_the_held_velocity():
+    # dz/dsigma = lam z, reuse 2 over 3 passes: fresh at 0 and 2 (the last)
+    lam, z0 = 0.6, 1.25
+    s = S.schedule(3, 12.0)
+    d = np.diff(s)
+    z1 = z0 + d[0] * lam * z0
+    z2 = z1 + d[1] * lam * z0                              # pass 1 reuses pass 0's velocity
+    z3 = z2 + d[2] * lam * z2
+    a, v = S.denoise(np.array([z0]), np.array([z0]), s, s, lambda i, a, v: (lam * a, lam * v), reuse=2)
+    np.testing.assert_allclose(a, [z3], rtol=1e-13)
+    np.testing.assert_allclose(v, [z3], rtol=1e-13)
+
+
+def test_reuse_one_is_plain_euler():
+    sa, sv = S.schedule(6, 3.0), S.schedule(6, 12.0)
+    f = lambda i, a, v: (0.3 * a - 0.1, -0.2 * v + 0.05)  # noqa: E731
+    a1, v1 = S.denoise(np.ones(4), np.ones(4), sa, sv, f)
+    a2, v2 = S.denoise(np.ones(4), np.ones(4), sa, sv, f, reuse=1)
+    np.testing.assert_array_equal(a1, a2)
+    np.testing.assert_array_equal(v1, v2)
