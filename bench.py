@@ -307,6 +307,8 @@ def main():
                          "the known-size reference for HBM byte counters")
     ap.add_argument("--single-block", type=int, default=1,
                     help="also time one H3 block at N=1192 with bf16 and INT8 weights (0: skip)")
+    ap.add_argument("--denoise-reuse", type=int, default=2,
+                    help="also time the denoising loop with this whole-velocity reuse (1: skip)")
     ap.add_argument("--denoise-steps", type=int, default=4,
                     help="Euler passes of the denoising loop timed at the secondary workload (0: skip)")
     ap.add_argument("--sparse", type=int, default=1,
@@ -436,14 +438,16 @@ def main():
         x2 = torch.empty(wl2.n_rows, dims.hidden, dtype=torch.float32, device="cuda")
         ws2 = lib.alloc_workspace(dims, wl2.n_rows)
         sa, sv = lib.sigma_schedule(steps_d, 3.0), lib.sigma_schedule(steps_d, 12.0)
-        run = lambda: lib.denoise(dims, io, iw, d["text"], d["cond"], d["audio"], d["video"], tags2, pos2,  # noqa: E731
-                                  tabs, blocks[:wl2.n_blocks], fins, sa, sv, x2, ws2)
-        run()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        run()
-        torch.cuda.synchronize()
-        secd = time.perf_counter() - t0
+        def timed_loop(reuse):
+            run = lambda: lib.denoise(dims, io, iw, d["text"], d["cond"], d["audio"], d["video"], tags2,  # noqa: E731
+                                      pos2, tabs, blocks[:wl2.n_blocks], fins, sa, sv, x2, ws2, reuse=reuse)
+            run()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            run()
+            torch.cuda.synchronize()
+            return time.perf_counter() - t0
+        secd = timed_loop(1)
         assert bool(torch.isfinite(d["video"]).all()), "non-finite latents"
         result["denoise"] = {"workload": wl2.name, "passes": steps_d, "shifts": {"video": 12.0, "audio": 3.0},
                              "s_per_loop": round(secd, 4), "ms_per_pass": round(secd / steps_d * 1e3, 2),
@@ -451,6 +455,15 @@ def main():
                              "pass_over_dit_forward": round(secd / steps_d / result["secondary"]["ms_per_step"]
                                                             * 1e3, 4)}
         log(f"denoising loop: {secd * 1e3:.1f} ms for {steps_d} passes")
+        if args.denoise_reuse > 1:
+            # whole-velocity reuse: fresh evaluations at i % r == 0 and the last pass
+            secr = timed_loop(args.denoise_reuse)
+            fresh = sum(1 for i in range(steps_d) if i % args.denoise_reuse == 0 or i == steps_d - 1)
+            result["denoise"]["reuse"] = {"reuse": args.denoise_reuse, "fresh_passes": fresh,
+                                          "s_per_loop": round(secr, 4),
+                                          "ms_per_fresh_pass": round(secr / fresh * 1e3, 2),
+                                          "speedup_vs_reuse_1": round(secd / secr, 3)}
+            log(f"denoising loop, reuse {args.denoise_reuse}: {secr * 1e3:.1f} ms ({fresh} fresh passes)")
         del ws2, x2, tabs, fins
     if args.sparse:
         # block-sparse attention (a fixed budget of key tiles per query tile)

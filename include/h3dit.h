@@ -335,10 +335,15 @@ H3DIT_API h3_status h3_mlp_fc2_residual(const h3_dims* dims, const uint16_t* a,
  * zero after the last pass).  Pure host function. */
 H3DIT_API h3_status h3_sigma_schedule(int32_t n_steps, double shift, double* sigmas);
 
-/* n_steps Euler passes on the GPU.  Pass i runs the velocity forward
+/* n_steps Euler passes on the GPU.  A fresh pass i runs the velocity forward
  * (h3_velocity_forward with the current latents, the blocks' tables
- * mod_tables + i*n_blocks*T*6*D and the final table final_tables + i*2*2*D)
- * and then, per modality,  z += (sigma[i+1] - sigma[i]) * v.
+ * mod_tables + i*n_blocks*T*6*D and the final table final_tables + i*2*2*D);
+ * then every pass steps, per modality,  z += (sigma[i+1] - sigma[i]) * v.
+ * Whole-velocity reuse (H3-metal digest, "4. Choose a speed/quality preset":
+ * at 20 passes, reuse 1, 2, 3 make 20, 11, 8 fresh evaluations and extrapolate
+ * the skipped transitions): pass i is fresh when i % reuse == 0 or it is the
+ * last pass; a skipped pass steps with the last fresh velocities.  reuse >= 1
+ * (1: every pass fresh).
  *   audio fp32 [audio][audio_patch], video fp32 [video][video_patch]: the
  *         latents, updated in place (text and condition inputs stay fixed)
  *   mod_tables bf16 [n_steps][n_blocks][T][6][D]; final_tables bf16
@@ -354,7 +359,7 @@ H3DIT_API h3_status h3_denoise(const h3_dims* dims, const h3_io_dims* io_dims,
                                const uint16_t* mod_tables, const h3_block_weights* weights,
                                int32_t n_blocks, const uint16_t* final_tables,
                                const double* sigmas_audio, const double* sigmas_video,
-                               int32_t n_steps, float* x_packed, void* workspace,
+                               int32_t n_steps, int32_t reuse, float* x_packed, void* workspace,
                                size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus

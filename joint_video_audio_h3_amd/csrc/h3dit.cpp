@@ -594,14 +594,15 @@ h3_status h3_denoise(const h3_dims* dims, const h3_io_dims* io_dims, const h3_io
                      float* audio, float* video, const int32_t* tag, const float* positions,
                      const uint16_t* mod_tables, const h3_block_weights* weights, int32_t n_blocks,
                      const uint16_t* final_tables, const double* sigmas_audio,
-                     const double* sigmas_video, int32_t n_steps, float* x_packed, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+                     const double* sigmas_video, int32_t n_steps, int32_t reuse, float* x_packed,
+                     void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   h3_status st;
   if ((st = check_io(dims, io_dims, segments)) != H3_OK) return st;
   const h3_segments sg = *segments;
   const int64_t n = sg.text + sg.cond + sg.audio + sg.video;
   if (n_steps <= 0) return fail(H3_ERR_INVALID_ARG, "n_steps=%d must be positive", n_steps);
+  if (reuse <= 0) return fail(H3_ERR_INVALID_ARG, "reuse=%d must be positive", reuse);
   if (n_blocks <= 0) return fail(H3_ERR_INVALID_ARG, "n_blocks=%d must be positive", n_blocks);
   if (!sigmas_audio || !sigmas_video) return fail(H3_ERR_INVALID_ARG, "sigmas_audio / sigmas_video is NULL");
   if ((st = check_embed_ptrs(sg, io_weights, text, cond, audio, video, x_packed)) != H3_OK) return st;
@@ -632,16 +633,21 @@ h3_status h3_denoise(const h3_dims* dims, const h3_io_dims* io_dims, const h3_io
   const size_t tstride = (size_t)dims->n_tags * 6 * dims->hidden;
   const size_t fstride = (size_t)4 * dims->hidden;
   for (int i = 0; i < n_steps; ++i) {
-    if ((st = run_embed(*dims, *io_dims, *io_weights, sg, text, cond, audio, video, x_packed, s)) != H3_OK)
-      return fail(st, "step %d: %s", i, std::string(g_err).c_str());
-    const uint16_t* tab = mod_tables + (size_t)i * n_blocks * tstride;
-    for (int b = 0; b < n_blocks; ++b) {
-      if ((st = run_block(*dims, x_packed, tag, tab + b * tstride, weights[b], n, ar, s)) != H3_OK)
-        return fail(st, "step %d block %d: %s", i, b, std::string(g_err).c_str());
+    // a skipped pass keeps the velocities of the last fresh one: nothing else
+    // writes the attention-output arena between passes
+    const bool fresh = i % reuse == 0 || i == n_steps - 1;
+    if (fresh) {
+      if ((st = run_embed(*dims, *io_dims, *io_weights, sg, text, cond, audio, video, x_packed, s)) != H3_OK)
+        return fail(st, "step %d: %s", i, std::string(g_err).c_str());
+      const uint16_t* tab = mod_tables + (size_t)i * n_blocks * tstride;
+      for (int b = 0; b < n_blocks; ++b) {
+        if ((st = run_block(*dims, x_packed, tag, tab + b * tstride, weights[b], n, ar, s)) != H3_OK)
+          return fail(st, "step %d block %d: %s", i, b, std::string(g_err).c_str());
+      }
+      if ((st = run_heads(*dims, *io_dims, *io_weights, sg, x_packed, final_tables + i * fstride, vel_a,
+                          vel_v, ar.h, s)) != H3_OK)
+        return fail(st, "step %d: %s", i, std::string(g_err).c_str());
     }
-    if ((st = run_heads(*dims, *io_dims, *io_weights, sg, x_packed, final_tables + i * fstride, vel_a,
-                        vel_v, ar.h, s)) != H3_OK)
-      return fail(st, "step %d: %s", i, std::string(g_err).c_str());
     const float dta = (float)(sigmas_audio[i + 1] - sigmas_audio[i]);
     const float dtv = (float)(sigmas_video[i + 1] - sigmas_video[i]);
     if ((st = hip_ok(h3::launch_euler(audio, vel_a, dta, sg.audio * io_dims->audio_patch, s), "euler audio")) != H3_OK)

@@ -83,7 +83,7 @@ _SIGS = {
     "h3_denoise": (c_i32, [_PD, _PIO, _PW, _PSG, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                            ctypes.POINTER(H3BlockWeights), c_i32, c_vp,
                            ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), c_i32,
-                           c_vp, c_vp, c_sz, c_vp]),
+                           c_i32, c_vp, c_vp, c_sz, c_vp]),
     "h3_attention_sparse": (c_i32, [_PD, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "h3_dit_forward_sparse": (c_i32, [_PD, c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(H3BlockWeights), c_i32,
                                       c_i64, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
@@ -265,8 +265,9 @@ def sigma_schedule(n_steps: int, shift: float):
 
 def denoise(dims, io, io_w: Dict, text, cond, audio, video, tag, positions, mod_tables,
             blocks: Sequence[Dict], final_tables, sigmas_audio, sigmas_video, x, workspace,
-            stream=None):
-    """len(sigmas) - 1 Euler passes; audio / video latents updated in place."""
+            stream=None, reuse: int = 1):
+    """len(sigmas) - 1 Euler passes; audio / video latents updated in place.
+    reuse r: fresh velocities at passes i % r == 0 and the last, held between."""
     sg = segments_of(text, cond, audio, video)
     w = make_io_weights(io_w)
     arr = (H3BlockWeights * len(blocks))(*[make_weights(b) for b in blocks])
@@ -278,7 +279,7 @@ def denoise(dims, io, io_w: Dict, text, cond, audio, video, tag, positions, mod_
     _check(load().h3_denoise(
         ctypes.byref(make_dims(dims)), ctypes.byref(make_io_dims(io)), ctypes.byref(w), ctypes.byref(sg),
         _ptr(text), _ptr(cond), _ptr(audio), _ptr(video), tag.data_ptr(), positions.data_ptr(),
-        mod_tables.data_ptr(), arr, len(blocks), final_tables.data_ptr(), sa, sv, n_steps,
+        mod_tables.data_ptr(), arr, len(blocks), final_tables.data_ptr(), sa, sv, n_steps, int(reuse),
         x.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)))
 
 

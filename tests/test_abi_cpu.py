@@ -222,11 +222,12 @@ def test_denoise_argument_errors_before_launch(L):
     sig = (ctypes.c_double * 3)(1.0, 0.5, 0.0)
     ws = L.h3_workspace_size(ctypes.byref(d), 164)
 
-    def call(n_steps=2, n_blocks=1, sa=sig, ws_bytes=ws):
+    def call(n_steps=2, n_blocks=1, sa=sig, ws_bytes=ws, reuse=1):
         return L.h3_denoise(ctypes.byref(d), ctypes.byref(io), ctypes.byref(w), ctypes.byref(sg),
                             FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, arr, n_blocks, FAKE, sa, sig,
-                            n_steps, FAKE, FAKE, ws_bytes, None)
+                            n_steps, reuse, FAKE, FAKE, ws_bytes, None)
     assert call(n_steps=0) == lib.H3_ERR_INVALID_ARG
+    assert call(reuse=0) == lib.H3_ERR_INVALID_ARG and "reuse" in lib.last_error()
     assert call(n_blocks=0) == lib.H3_ERR_INVALID_ARG
     assert call(sa=None) == lib.H3_ERR_INVALID_ARG and "sigmas" in lib.last_error()
     assert call(ws_bytes=ws - 256) == lib.H3_ERR_WORKSPACE

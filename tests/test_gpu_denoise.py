@@ -3,7 +3,9 @@
 Each pass of the oracle runs its own velocity forward (inputs, blocks, final
 AdaLN and heads) with that pass's tables; the latents step on the video (12)
 and audio (3) shifted schedules.  One GPU pass also equals one velocity
-forward followed by the Euler update.
+forward followed by the Euler update.  With velocity reuse 2 over 4 passes
+(fresh at 0, 2 and 3) the loop matches the oracle's reuse schedule, and the
+skipped pass moves each latent by its step times the held velocity.
 """
 import numpy as np
 import pytest
@@ -33,14 +35,14 @@ def _case(dims, io, L, C, A, vgrid, nb, steps, seed):
     return wl, tags, pos, tables, finals, blocks, inp, w
 
 
-def _gpu(dims, io, wl, tags, pos, tables, finals, blocks, inp, w, sa, sv):
+def _gpu(dims, io, wl, tags, pos, tables, finals, blocks, inp, w, sa, sv, reuse=1):
     d = {k: (dev(v) if len(v) else None) for k, v in inp.items()}
     x = torch.empty(wl.n_rows, dims.hidden, dtype=torch.float32, device="cuda")
     ws = lib.alloc_workspace(dims, wl.n_rows)
     iw = {k: (None if v is None else dev(v)) for k, v in w.items()}
     lib.denoise(dims, io, iw, d["text"], d["cond"], d["audio"], d["video"], dev(tags), dev(pos),
                 dev(np.ascontiguousarray(tables)), [lib.to_device_block(b) for b in blocks],
-                dev(np.ascontiguousarray(finals)), sa, sv, x, ws)
+                dev(np.ascontiguousarray(finals)), sa, sv, x, ws, reuse=reuse)
     torch.cuda.synchronize()
     return d["audio"].cpu().numpy(), d["video"].cpu().numpy()
 
@@ -88,3 +90,45 @@ def test_one_pass_is_velocity_forward_then_euler():
     ev = inp["video"] + np.float32(sv[1] - sv[0]) * vv.cpu().numpy()
     np.testing.assert_allclose(ga, ea, rtol=1e-6, atol=1e-6)
     np.testing.assert_allclose(gv, ev, rtol=1e-6, atol=1e-6)
+
+
+def test_denoise_with_velocity_reuse_matches_oracle():
+    dims, io = synth.TINY_DIMS, synth.TINY_IO
+    steps, reuse = 4, 2
+    say("denoise reuse", reuse, steps)
+    wl, tags, pos, tables, finals, blocks, inp, w = _case(dims, io, 16, 8, 20, (2, 8, 8), 2, steps, seed=42)
+    sa, sv = lib.sigma_schedule(steps, 3.0), lib.sigma_schedule(steps, 12.0)
+    ga, gv = _gpu(dims, io, wl, tags, pos, tables, finals, blocks, inp, w, sa, sv, reuse=reuse)
+    calls = []
+
+    def vel(i, a, v):
+        calls.append(i)
+        return oracle.velocity_forward(inp["text"], inp["cond"], a.astype(np.float32), v.astype(np.float32),
+                                       w, finals[i], tags, pos, tables[i], lambda b: blocks[b], 2, dims)
+
+    ra, rv = oracle.denoise(inp["audio"], inp["video"], np.array(sa), np.array(sv), vel, reuse=reuse)
+    assert calls == [0, 2, 3]
+    ea, ev = rel_l2(ga, ra), rel_l2(gv, rv)
+    say("denoise reuse rel-L2 audio", ea, "video", ev)
+    assert ea < TOL_DEPTH and ev < TOL_DEPTH
+    # reuse changes the result (passes 1 and 2 differ from the fresh loop)
+    fa, fv = _gpu(dims, io, wl, tags, pos, tables, finals, blocks, inp, w, sa, sv, reuse=1)
+    assert rel_l2(fa, ga) > 10 * ea
+
+
+def test_reuse_beyond_steps_runs_first_and_last_pass_only():
+    dims, io = synth.TINY_DIMS, synth.TINY_IO
+    say("denoise reuse 5 over 3")
+    wl, tags, pos, tables, finals, blocks, inp, w = _case(dims, io, 16, 8, 20, (2, 8, 8), 2, 3, seed=43)
+    sa, sv = lib.sigma_schedule(3, 3.0), lib.sigma_schedule(3, 12.0)
+    ga, gv = _gpu(dims, io, wl, tags, pos, tables, finals, blocks, inp, w, sa, sv, reuse=5)
+    calls = []
+
+    def vel(i, a, v):
+        calls.append(i)
+        return oracle.velocity_forward(inp["text"], inp["cond"], a.astype(np.float32), v.astype(np.float32),
+                                       w, finals[i], tags, pos, tables[i], lambda b: blocks[b], 2, dims)
+
+    ra, rv = oracle.denoise(inp["audio"], inp["video"], np.array(sa), np.array(sv), vel, reuse=5)
+    assert calls == [0, 2]
+    assert rel_l2(ga, ra) < TOL_DEPTH and rel_l2(gv, rv) < TOL_DEPTH
