@@ -32,7 +32,7 @@ HBM = perf_model.PEAK_HBM_GBS
 # HBM traffic of the dominant kernels from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE,
 # bytes per launch after the copy-kernel calibration (see profiles/); None when
 # the kernel changed after the counters were taken.
-TRAFFIC_BYTES = {("h3_50blk_n49840", "attention"): 21.22e9}
+TRAFFIC_BYTES = {("h3_50blk_n49840", "attention"): 11.46e9}
 
 
 def log(*a):
