@@ -414,6 +414,8 @@ static hipError_t launch_hd(const AttnArgs& a, hipStream_t s) {
   } else if (a.tile == 128) {
     attn_kernel<HD, 4, true><<<dim3((a.n + 127) / 128, a.heads), 256, 0, s>>>(a);
   } else if (a.tile == 64) {
+    // two waves per block and two 64 KB blocks per CU: one wave per SIMD whatever
+    // the register count (the build notes that two per SIMD is not reached)
     attn_kernel<HD, 2, true><<<dim3((a.n + 63) / 64, a.heads), 128, 0, s>>>(a);
   } else {
     return hipErrorInvalidValue;
