@@ -49,7 +49,8 @@ def _ref(dims, q, k, v, tile, off, idx):
 
 
 CASES = [("tiny", synth.TINY_DIMS, 300, 64, 0.3), ("tiny", synth.TINY_DIMS, 333, 128, 0.4),
-         ("tiny", synth.TINY_DIMS, 64, 64, 0.5), ("h3", synth.H3_DIMS, 777, 128, 0.25),
+         ("tiny", synth.TINY_DIMS, 64, 64, 0.5), ("tiny", synth.TINY_DIMS, 40, 64, 1.0),
+         ("h3", synth.H3_DIMS, 1, 128, 1.0), ("h3", synth.H3_DIMS, 777, 128, 0.25),
          ("h3", synth.H3_DIMS, 700, 64, 0.2)]
 
 

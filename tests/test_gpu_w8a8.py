@@ -23,7 +23,8 @@ pytestmark = pytest.mark.gpu
 
 W8_TINY = dataclasses.replace(synth.TINY_DIMS, wfmt=synth.WFMT_W8A8)
 W8_H3 = dataclasses.replace(synth.H3_DIMS, wfmt=synth.WFMT_W8A8)
-CASES = [("tiny", W8_TINY, 164), ("tiny", W8_TINY, 300), ("h3", W8_H3, 257), ("h3", W8_H3, 1192)]
+CASES = [("tiny", W8_TINY, 1), ("tiny", W8_TINY, 164), ("tiny", W8_TINY, 300), ("h3", W8_H3, 1),
+         ("h3", W8_H3, 257), ("h3", W8_H3, 1192)]
 IDS = [f"{n}-N{r}" for n, _, r in CASES]
 
 
