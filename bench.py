@@ -242,7 +242,11 @@ def sparse_breakdown(lib, dims, n, reps, torch, keep=0.125, dense_rows=1280):
     return out
 
 
-def run_forward(lib, dims, rows, table, blocks, ws, steps, warmup, torch):
+def run_forward(lib, dims, rows, table, blocks, ws, steps, warmup, torch, per_step=None):
+    """Seconds per forward over `steps` back-to-back forwards (wall clock around
+    all of them).  HIP events on the launch stream between forwards give each
+    forward's own time without a host wait; with `per_step` (a dict) their mean
+    and sample standard deviation in ms are stored there."""
     x, tags, pos = rows
     fwd = lambda: lib.dit_forward(dims, x, tags, pos, table, blocks, ws)
     for i in range(warmup):
@@ -250,12 +254,20 @@ def run_forward(lib, dims, rows, table, blocks, ws, steps, warmup, torch):
         torch.cuda.synchronize()
         log(f"warmup forward {i + 1}/{warmup} done")
     torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
+    ev[0].record()
     for i in range(steps):
         fwd()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     assert bool(torch.isfinite(x).all()), "non-finite output"
+    if per_step is not None:
+        ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        mean = sum(ms) / len(ms)
+        sd = (sum((m - mean) ** 2 for m in ms) / (len(ms) - 1)) ** 0.5 if len(ms) > 1 else 0.0
+        per_step.update({"mean_ms": round(mean, 2), "sd_ms": round(sd, 2), "n": len(ms)})
     return dt / steps
 
 
@@ -349,11 +361,15 @@ def main():
     table, blocks = synth.make_device_weights(dims, wl.n_blocks, seed=0)
     torch.cuda.synchronize()
 
+    measured_steps = {}
+
     def measure(wlx, steps, warmup):
         rows = synth.make_device_rows(wlx, seed=0)
         ws = lib.alloc_workspace(dims, wlx.n_rows)
+        ps = {}
         sec = run_forward(lib, dims, rows, table[:wlx.n_blocks], blocks[:wlx.n_blocks], ws,
-                          steps, warmup, torch)
+                          steps, warmup, torch, per_step=ps)
+        measured_steps[wlx.name] = ps
         log(f"{wlx.name}: {sec * 1e3:.1f} ms per forward")
         bd, w = step_breakdown(lib, dims, synth.make_device_rows(wlx, seed=1), table, blocks[0],
                                args.breakdown_reps, torch)
@@ -382,6 +398,7 @@ def main():
         "config": {"workload": wl.name, "n_rows": n, "blocks": wl.n_blocks, "hidden": dims.hidden,
                    "heads": dims.heads, "head_dim": dims.head_dim, "ffn": dims.ffn,
                    "packed": {"L": wl.L, "C": wl.C, "A": wl.A, "V": list(wl.V)}},
+        "step_events": measured_steps[wl.name],
         "forward_tflops": round(flop_fwd / sec / 1e12, 1),
         "forward_mfma_frac": round(flop_fwd / sec / 1e12 / PEAK, 4),
         "per_step_kernels": bd,
@@ -400,7 +417,7 @@ def main():
         result["secondary"] = {
             "workload": wl2.name, "n_rows": wl2.n_rows, "value": round(wl2.n_rows / sec2, 2),
             "unit": "packed tokens/s", "ms_per_step": round(sec2 * 1e3, 2),
-            "steps": args.secondary_steps,
+            "steps": args.secondary_steps, "step_events": measured_steps[wl2.name],
             "forward_tflops": round(wl2.n_blocks * w2.total_flop / sec2 / 1e12, 1),
             "forward_mfma_frac": round(wl2.n_blocks * w2.total_flop / sec2 / 1e12 / PEAK, 4),
             "per_step_kernels": bd2,
@@ -412,6 +429,7 @@ def main():
             "n_rows": wl3.n_rows, "packed": {"L": wl3.L, "C": wl3.C, "A": wl3.A, "V": list(wl3.V)},
             "value": round(wl3.n_rows / sec3, 2), "unit": "packed tokens/s",
             "ms_per_step": round(sec3 * 1e3, 2), "steps": args.secondary_steps,
+            "step_events": measured_steps[wl3.name],
             "forward_tflops": round(wl3.n_blocks * w3.total_flop / sec3 / 1e12, 1),
             "forward_mfma_frac": round(wl3.n_blocks * w3.total_flop / sec3 / 1e12 / PEAK, 4),
             "per_step_kernels": bd3,
