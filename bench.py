@@ -271,6 +271,14 @@ def run_forward(lib, dims, rows, table, blocks, ws, steps, warmup, torch, per_st
     return dt / steps
 
 
+def env_receipt(torch):
+    """What the numbers were measured on: device, software versions."""
+    p = torch.cuda.get_device_properties(0)
+    return {"device": p.name, "gcn_arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
+            "hbm_gib": round(p.total_memory / 2**30, 1), "torch": torch.__version__,
+            "hip": getattr(torch.version, "hip", None)}
+
+
 def cpu_baseline(n_target, n_blocks, dims_h3):
     """The oracle as it stands, on a bounded sample: one full block of the same
     model width at N=1192 rows, its attention step timed on its own; both parts
@@ -295,7 +303,20 @@ def cpu_baseline(n_target, n_blocks, dims_h3):
     t_attn = time.perf_counter() - t0
     t_rest = max(t_block - t_attn, 1e-9)
     t_fwd = n_blocks * (t_rest * n_target / n + t_attn * (n_target / n) ** 2)
+    cpu_model, blas = "unknown", "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu_model)
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()
+                                 if i.get("user_api") == "blas"})) or blas
+    except Exception:
+        pass
     return {"value": round(n_target / t_fwd, 4), "unit": "packed tokens/s", "cores": cores,
+            "host": {"cpu_model": cpu_model, "nproc": os.cpu_count(), "blas": blas},
             "kind": "oracle",
             "sample": (f"one float64 oracle block at N={n} (H3 width) took {t_block:.1f} s, its "
                        f"attention {t_attn:.1f} s; scaled to the {n_blocks}-block N={n_target} "
@@ -399,6 +420,7 @@ def main():
                    "heads": dims.heads, "head_dim": dims.head_dim, "ffn": dims.ffn,
                    "packed": {"L": wl.L, "C": wl.C, "A": wl.A, "V": list(wl.V)}},
         "step_events": measured_steps[wl.name],
+        "env": env_receipt(torch),
         "forward_tflops": round(flop_fwd / sec / 1e12, 1),
         "forward_mfma_frac": round(flop_fwd / sec / 1e12 / PEAK, 4),
         "per_step_kernels": bd,
