@@ -1,0 +1,60 @@
+"""Full-depth parity of the 50-block forward at N = 6,437 (the secondary
+workload) against the float64 oracle (GPU, long job).
+
+The oracle's 50 blocks are about 307 TFLOP of float64 work on the host (about
+ten minutes on 16 cores), and the host holds all 50 blocks' weights (38.5 GB),
+so the test runs only when H3_LONG_TESTS=1 is set.  The GPU side is one
+h3_dit_forward call over the 50 device blocks; the oracle runs block by block,
+printing its progress.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from joint_video_audio_h3_amd import lib, synth
+from tests.gpu_util import TOL_DEPTH, dev, rel_l2, say
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(os.environ.get("H3_LONG_TESTS") != "1",
+                                 reason="long job (about 12 minutes, 40 GB of host memory): set H3_LONG_TESTS=1")]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    lib.load()
+
+
+def test_fifty_block_forward_n6437_matches_oracle():
+    wl = synth.WORKLOADS["h3_50blk_n6437"]
+    dims = wl.dims
+    say("long depth: generating", wl.n_blocks, "blocks at N =", wl.n_rows)
+    tags, pos = synth.packed_layout(wl)
+    x = synth.make_x(wl, dims, seed=50)
+    table = synth.make_table(dims, wl.n_blocks, seed=50)
+    hosts, devs = [], []
+    for b in range(wl.n_blocks):
+        hosts.append(synth.make_block_weights(dims, b, seed=50))
+        devs.append(lib.to_device_block(hosts[-1]))
+        if b % 10 == 9:
+            say("long depth: weights of", b + 1, "blocks ready")
+    xd = dev(x)
+    ws = lib.alloc_workspace(dims, wl.n_rows)
+    lib.dit_forward(dims, xd, dev(tags), dev(pos), dev(table), devs, ws)
+    torch.cuda.synchronize()
+    got = xd.cpu().numpy().astype(np.float64)
+    del devs, ws, xd
+    torch.cuda.empty_cache()
+    ref = x.astype(np.float64)
+    for b in range(wl.n_blocks):
+        ref = oracle.block_forward(ref, tags, pos, table[b], hosts[b], dims)
+        say("long depth: oracle block", b + 1, "of", wl.n_blocks)
+    x64 = x.astype(np.float64)
+    e, du = rel_l2(got, ref), rel_l2(got - x64, ref - x64)
+    say("long depth: rel-L2 x_out", e, "update", du)
+    assert np.isfinite(got).all()
+    assert e < TOL_DEPTH
+    assert du < 2 * TOL_DEPTH
