@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -348,6 +349,29 @@ h3_status run_block(const h3_dims& d, float* x, const int32_t* tag, const uint16
   return H3_OK;
 }
 
+// With H3_CHECK=1 in the environment, the modality tags are checked on the
+// device before anything else is enqueued: one small kernel, then a wait for
+// the stream (so not for use under stream capture).  Any tag outside
+// [0, n_tags) fails the call with nothing else enqueued.
+h3_status check_tags(const h3_dims& d, const int32_t* tag, int64_t n, hipStream_t s) {
+  const char* e = std::getenv("H3_CHECK");
+  if (!e || std::strcmp(e, "1") != 0) return H3_OK;
+  unsigned int* bad = nullptr;
+  unsigned int host = 0;
+  h3_status st;
+  if ((st = hip_ok(hipMalloc(&bad, sizeof(unsigned int)), "H3_CHECK buffer")) != H3_OK) return st;
+  hipError_t r = hipMemsetAsync(bad, 0, sizeof(unsigned int), s);
+  if (r == hipSuccess) r = h3::launch_count_bad_tags(tag, n, d.n_tags, bad, s);
+  if (r == hipSuccess) r = hipMemcpyAsync(&host, bad, sizeof(unsigned int), hipMemcpyDeviceToHost, s);
+  if (r == hipSuccess) r = hipStreamSynchronize(s);
+  const hipError_t rf = hipFree(bad);
+  if ((st = hip_ok(r, "H3_CHECK tag scan")) != H3_OK) return st;
+  if ((st = hip_ok(rf, "H3_CHECK buffer")) != H3_OK) return st;
+  if (host != 0)
+    return fail(H3_ERR_INVALID_ARG, "%u modality tags outside [0, %d) (H3_CHECK)", host, d.n_tags);
+  return H3_OK;
+}
+
 h3_status check_forward_common(const h3_dims* dims, const float* x, const int32_t* tag,
                                const float* pos, const uint16_t* table, int64_t n, void* ws,
                                size_t ws_bytes) {
@@ -562,6 +586,7 @@ h3_status h3_dit_forward_sparse(const h3_dims* dims, float* x, const int32_t* ta
   if ((st = check_sparse(tile, tile_off, tile_idx)) != H3_OK) return st;
   if ((st = check_device()) != H3_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((st = check_tags(*dims, tag, n_rows, s)) != H3_OK) return st;
   const Arena ar = carve(*dims, n_rows, static_cast<char*>(workspace));
   if ((st = hip_ok(do_rope(*dims, positions, n_rows, ar.cs, s), "rope table")) != H3_OK) return st;
   const size_t tstride = (size_t)dims->n_tags * 6 * dims->hidden;
@@ -626,6 +651,7 @@ h3_status h3_denoise(const h3_dims* dims, const h3_io_dims* io_dims, const h3_io
                 va_bytes + vv_bytes, o_bytes);
   if ((st = check_device()) != H3_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((st = check_tags(*dims, tag, n, s)) != H3_OK) return st;
   const Arena ar = carve(*dims, n, static_cast<char*>(workspace));
   float* vel_a = reinterpret_cast<float*>(ar.o);
   float* vel_v = reinterpret_cast<float*>(reinterpret_cast<char*>(ar.o) + va_bytes);
@@ -699,6 +725,7 @@ h3_status h3_dit_block_forward(const h3_dims* dims, float* x, const int32_t* tag
   if ((st = check_weights(dims, weights, true, true, true, true)) != H3_OK) return st;
   if ((st = check_device()) != H3_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((st = check_tags(*dims, tag, n_rows, s)) != H3_OK) return st;
   const Arena ar = carve(*dims, n_rows, static_cast<char*>(workspace));
   if ((st = hip_ok(do_rope(*dims, positions, n_rows, ar.cs, s), "rope table")) != H3_OK) return st;
   return run_block(*dims, x, tag, mod_table, *weights, n_rows, ar, s);
@@ -723,6 +750,7 @@ h3_status h3_dit_forward(const h3_dims* dims, float* x, const int32_t* tag, cons
   }
   if ((st = check_device()) != H3_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((st = check_tags(*dims, tag, n_rows, s)) != H3_OK) return st;
   const Arena ar = carve(*dims, n_rows, static_cast<char*>(workspace));
   if ((st = hip_ok(do_rope(*dims, positions, n_rows, ar.cs, s), "rope table")) != H3_OK) return st;
   const size_t tstride = (size_t)dims->n_tags * 6 * dims->hidden;
@@ -759,6 +787,7 @@ h3_status h3_adaln_modulate(const h3_dims* dims, const float* x, const int32_t* 
   H3_NEED(h, "h");
   if (which != 0 && which != 1) return fail(H3_ERR_INVALID_ARG, "which=%d must be 0 or 1", which);
   if ((st = check_device()) != H3_OK) return st;
+  if ((st = check_tags(*dims, tag, n_rows, reinterpret_cast<hipStream_t>(stream))) != H3_OK) return st;
   if (dims->wfmt == H3_W_W8A8) {   // h is a W8A8 activation buffer
     char* base = reinterpret_cast<char*>(h);
     return hip_ok(do_adaln(*dims, x, tag, mod_table, which, n_rows, nullptr,
@@ -815,6 +844,7 @@ h3_status h3_out_proj_residual(const h3_dims* dims, const uint16_t* o,
   H3_NEED(tag, "modality_tag");
   H3_NEED(x, "x");
   if ((st = check_device()) != H3_OK) return st;
+  if ((st = check_tags(*dims, tag, n_rows, reinterpret_cast<hipStream_t>(stream))) != H3_OK) return st;
   return hip_ok(do_resid(*dims, o, weights->w_out, weights->s_out, weights->b_out,
                          dims->heads * dims->head_dim, mod_table, 2, tag, n_rows, x,
                          reinterpret_cast<hipStream_t>(stream),
@@ -848,6 +878,7 @@ h3_status h3_mlp_fc2_residual(const h3_dims* dims, const uint16_t* a,
   H3_NEED(tag, "modality_tag");
   H3_NEED(x, "x");
   if ((st = check_device()) != H3_OK) return st;
+  if ((st = check_tags(*dims, tag, n_rows, reinterpret_cast<hipStream_t>(stream))) != H3_OK) return st;
   return hip_ok(do_resid(*dims, a, weights->w_fc2, weights->s_fc2, weights->b_fc2, dims->ffn,
                          mod_table, 5, tag, n_rows, x, reinterpret_cast<hipStream_t>(stream),
                          act_scales(*dims, a, n_rows, dims->ffn)),
@@ -932,6 +963,7 @@ h3_status h3_velocity_forward(const h3_dims* dims, const h3_io_dims* io_dims,
   }
   if ((st = check_device()) != H3_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((st = check_tags(*dims, tag, n, s)) != H3_OK) return st;
   if ((st = run_embed(*dims, *io_dims, *io_weights, sg, text, cond, audio, video, x_packed, s)) != H3_OK)
     return st;
   uint16_t* h = static_cast<uint16_t*>(workspace);

@@ -98,6 +98,22 @@ hipError_t launch_euler(float* z, const float* v, float dt, int64_t n, hipStream
   return hipGetLastError();
 }
 
+// Count the modality tags outside [0, n_tags) (the optional argument check).
+__global__ __launch_bounds__(256) void count_bad_tags_kernel(const int32_t* tag, int64_t n, int n_tags,
+                                                             unsigned int* bad) {
+  unsigned int c = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    c += (tag[i] < 0 || tag[i] >= n_tags) ? 1u : 0u;
+  if (c) atomicAdd(bad, c);
+}
+
+hipError_t launch_count_bad_tags(const int32_t* tag, int64_t n, int n_tags, unsigned int* bad, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  count_bad_tags_kernel<<<dim3((unsigned)(blocks < 1024 ? blocks : 1024)), 256, 0, s>>>(tag, n, n_tags, bad);
+  return hipGetLastError();
+}
+
 hipError_t launch_patch_embed(const PatchArgs& a, hipStream_t s) {
   const dim3 grid((a.rows + 127) / 128, (a.D + 32 * PE_NCT - 1) / (32 * PE_NCT));
   switch (a.P) {
