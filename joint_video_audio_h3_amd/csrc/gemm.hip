@@ -210,7 +210,7 @@ template <bool GATED, int TM, int TN, int FM, int FN>
 __device__ __forceinline__ void resid_epilogue_lds(const GemmArgs& p, f32x16 (&acc)[FM][FN],
                                                    int row0, int col0, int lane, float* stage,
                                                    const int* s_tag) {
-  static_assert(TN == 128 || TN == 96, "a half-wave's float4s cover one staged row");
+  static_assert(TN == 128 || TN == 96 || TN == 64, "a half-wave's float4s cover one staged row");
   const int hl = lane >> 5, lc = lane & 31;
   const int gcol = col0 + 4 * lc;
   // n_out % 4 == 0, so a float4 is all in or all out; lanes past TN/4 idle
@@ -950,16 +950,21 @@ static int device_cus() {
 }
 
 // Residual and store GEMMs have the narrowest outputs (hidden, or a head's
-// patch width); when 256-wide tiles leave the last wave of tiles mostly empty,
-// or the output is narrower than a tile, 192-wide ones (a quarter fewer MFMAs
-// per tile, ~5% less efficient per MFMA) balance better.  Cost model: waves of
-// tiles x work per tile.
-static bool resid_prefers_192(const GemmArgs& a) {
+// patch width): when 256-wide tiles leave the last wave of tiles mostly empty,
+// or the output is narrower than a tile, 192- or 128-wide tiles balance better
+// at a cost per MFMA (a quarter or a half fewer MFMAs per fragment read and per
+// byte staged; measured ~5 % and ~25 % on the H3 residual GEMMs).  Cost
+// model: waves of tiles x work per tile x that factor; returns the tile width.
+// 128-wide tiles win only when a single wave of them covers the output (at
+// H3 width up to 1,536 rows: 1.5x at 1,192 rows).
+static int resid_tile_width(const GemmArgs& a, bool allow128) {
   const long tiles_m = (a.M + 255) / 256, cus = device_cus();
-  const long w256 = (tiles_m * ((a.n_out + 255) / 256) + cus - 1) / cus;
-  const long w192 = (tiles_m * ((a.n_out + 191) / 192) + cus - 1) / cus;
-  return w192 * 192 * 105 < w256 * 256 * 100;
+  auto waves = [&](long bn) { return (tiles_m * ((a.n_out + bn - 1) / bn) + cus - 1) / cus; };
+  const long c256 = waves(256) * 256 * 100, c192 = waves(192) * 192 * 105, c128 = waves(128) * 128 * 125;
+  if (allow128 && c128 < c192 && c128 < c256) return 128;
+  return c192 < c256 ? 192 : 256;
 }
+static bool resid_prefers_192(const GemmArgs& a) { return resid_tile_width(a, false) == 192; }
 
 hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
   if (a.K % 64 != 0) return hipErrorInvalidValue;
@@ -979,8 +984,11 @@ hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
   if (wfmt == 0) {
     switch (epi) {
       case EPI_RESID:
-        if (resid_prefers_192(a)) return run_direct<EPI_RESID, 0, 192>(a, s);
-        return run_direct<EPI_RESID, 0, 256>(a, s);
+        switch (resid_tile_width(a, true)) {
+          case 128: return run_direct<EPI_RESID, 0, 128>(a, s);
+          case 192: return run_direct<EPI_RESID, 0, 192>(a, s);
+          default: return run_direct<EPI_RESID, 0, 256>(a, s);
+        }
       case EPI_STORE:
         if (resid_prefers_192(a)) return run_direct<EPI_STORE, 0, 192>(a, s);
         return run_direct<EPI_STORE, 0, 256>(a, s);

@@ -5,7 +5,8 @@ whose column tiles the eight XCDs walk in step, and the rows past the last
 whole group (8 x 8 row tiles when K < 7168, 8 x 4 when K >= 7168).  At these
 row counts both regions are present for both group sizes, or only the
 remainder: 49,840 (195 row tiles), 16,640 (65) and 8,449 (34, the last holding
-one row).  Outputs start as NaN (bf16 and q/k/v^T) and every element must
+one row); at 1,192 (5 row tiles) the gated-residual GEMMs take 128-wide
+column tiles.  Outputs start as NaN (bf16 and q/k/v^T) and every element must
 have been written, or zero (the fp32 residual stream) and every 32 x 32 tile
 must hold updates; the values themselves are checked against the oracle on
 sampled rows elsewhere.
@@ -18,7 +19,7 @@ from tests.gpu_util import say
 
 pytestmark = pytest.mark.gpu
 H3 = synth.H3_DIMS
-SIZES = [8449, 16640, 49840]
+SIZES = [1192, 8449, 16640, 49840]
 BF16_NAN = 0x7FC0
 
 
