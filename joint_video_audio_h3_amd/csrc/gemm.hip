@@ -1001,8 +1001,11 @@ hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
   }
   switch (epi) {   // (EPI_STORE layers have bf16 weights only)
     case EPI_RESID:
-      if (resid_prefers_192(a)) return run_w8<EPI_RESID, 0, 192>(a, s);
-      return run_w8<EPI_RESID, 0, 256>(a, s);
+      switch (resid_tile_width(a, true)) {
+        case 128: return run_w8<EPI_RESID, 0, 128>(a, s);
+        case 192: return run_w8<EPI_RESID, 0, 192>(a, s);
+        default: return run_w8<EPI_RESID, 0, 256>(a, s);
+      }
     case EPI_SWIGLU: return run_w8<EPI_SWIGLU, 0, 256>(a, s);
     case EPI_QKV:
       if (a.head_dim == 128) return run_w8<EPI_QKV, 128, 256>(a, s);
