@@ -972,8 +972,11 @@ hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
   if (wfmt == 2) {   // W8A8: int8 activations and weights, per-row scales
     switch (epi) {
       case EPI_RESID:
-        if (resid_prefers_192(a)) return run_direct<EPI_RESID, 0, 192, true>(a, s);
-        return run_direct<EPI_RESID, 0, 256, true>(a, s);
+        switch (resid_tile_width(a, true)) {
+          case 128: return run_direct<EPI_RESID, 0, 128, true>(a, s);
+          case 192: return run_direct<EPI_RESID, 0, 192, true>(a, s);
+          default: return run_direct<EPI_RESID, 0, 256, true>(a, s);
+        }
       case EPI_SWIGLU: return run_direct<EPI_SWIGLU, 0, 256, true>(a, s);
       case EPI_QKV:
         if (a.head_dim == 128) return run_direct<EPI_QKV, 128, 256, true>(a, s);
