@@ -6,7 +6,8 @@ whole group (8 x 8 row tiles when K < 7168, 8 x 4 when K >= 7168).  At these
 row counts both regions are present for both group sizes, or only the
 remainder: 49,840 (195 row tiles), 16,640 (65) and 8,449 (34, the last holding
 one row); at 1,192 (5 row tiles) the gated-residual GEMMs take 128-wide
-column tiles.  Outputs start as NaN (bf16 and q/k/v^T) and every element must
+column tiles.  Both weight formats run: bf16 (the direct-to-LDS kernel) and
+INT8 group-32 (the dequantising kernel, with its own wave layout).  Outputs start as NaN (bf16 and q/k/v^T) and every element must
 have been written, or zero (the fp32 residual stream) and every 32 x 32 tile
 must hold updates; the values themselves are checked against the oracle on
 sampled rows elsewhere.
@@ -19,7 +20,9 @@ from tests.gpu_util import say
 
 pytestmark = pytest.mark.gpu
 H3 = synth.H3_DIMS
+INT8_H3 = synth.WORKLOADS["h3_1blk_n1192_int8"].dims   # INT8 group-32 weights, own kernel
 SIZES = [1192, 8449, 16640, 49840]
+FORMATS = {"bf16": H3, "int8": INT8_H3}
 BF16_NAN = 0x7FC0
 
 
@@ -29,9 +32,15 @@ def _lib():
     lib.load()
 
 
-@pytest.fixture(scope="module")
-def devw():
-    return lib.to_device_block(synth.make_block_weights(H3, 0, seed=31))
+_WEIGHTS = {}
+
+
+@pytest.fixture(scope="module", params=list(FORMATS))
+def fmt(request):
+    # one block of each weight format, made once
+    if request.param not in _WEIGHTS:
+        _WEIGHTS[request.param] = lib.to_device_block(synth.make_block_weights(FORMATS[request.param], 0, seed=31))
+    return FORMATS[request.param], _WEIGHTS[request.param]
 
 
 def _no_nan_bf16(t):
@@ -39,8 +48,9 @@ def _no_nan_bf16(t):
 
 
 @pytest.mark.parametrize("n", SIZES)
-def test_fc1_writes_every_element(n, devw):
-    say("tile coverage fc1", n)
+def test_fc1_writes_every_element(n, fmt):
+    H3, devw = fmt
+    say("tile coverage fc1", n, H3.wfmt)
     h2 = synth.make_device_activation(n, H3.hidden, seed=32)
     a = torch.full((n, H3.ffn), BF16_NAN, dtype=torch.int16, device="cuda")
     lib.mlp_fc1_swiglu(H3, h2.view(torch.int16), devw, a)
@@ -49,8 +59,9 @@ def test_fc1_writes_every_element(n, devw):
 
 
 @pytest.mark.parametrize("n", SIZES)
-def test_qkv_writes_every_element(n, devw):
-    say("tile coverage qkv", n)
+def test_qkv_writes_every_element(n, fmt):
+    H3, devw = fmt
+    say("tile coverage qkv", n, H3.wfmt)
     h = synth.make_device_activation(n, H3.hidden, seed=33)
     pos = torch.from_numpy(synth.make_positions(n, seed=33)).cuda()
     np_ = lib.padded_rows(n)
@@ -66,8 +77,9 @@ def test_qkv_writes_every_element(n, devw):
 
 @pytest.mark.parametrize("n", SIZES)
 @pytest.mark.parametrize("which", ["out", "fc2"])
-def test_residual_updates_every_element(n, which, devw):
-    say("tile coverage residual", which, n)
+def test_residual_updates_every_element(n, which, fmt):
+    H3, devw = fmt
+    say("tile coverage residual", which, n, H3.wfmt)
     K = H3.inner if which == "out" else H3.ffn
     a = synth.make_device_activation(n, K, seed=34, std=0.3)
     x = torch.zeros(n, H3.hidden, dtype=torch.float32, device="cuda")
