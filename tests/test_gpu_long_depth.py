@@ -1,5 +1,6 @@
 """Full-depth parity of the 50-block forward at N = 6,437 (the secondary
-workload) against the float64 oracle (GPU, long job).
+workload), with bf16 weights and with the W8A8 trunk, against the float64
+oracle (GPU, long job).
 
 The oracle's 50 blocks are about 307 TFLOP of float64 work on the host (about
 ten minutes on 16 cores), and the host holds all 50 blocks' weights (38.5 GB),
@@ -15,7 +16,7 @@ import torch
 
 import oracle
 from joint_video_audio_h3_amd import lib, synth
-from tests.gpu_util import TOL_DEPTH, dev, rel_l2, say
+from tests.gpu_util import TOL_BLOCK, TOL_DEPTH, dev, rel_l2, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(os.environ.get("H3_LONG_TESTS") != "1",
@@ -28,8 +29,9 @@ def _lib():
     lib.load()
 
 
-def test_fifty_block_forward_n6437_matches_oracle():
-    wl = synth.WORKLOADS["h3_50blk_n6437"]
+@pytest.mark.parametrize("wname", ["h3_50blk_n6437", "h3_50blk_n6437_w8a8"])
+def test_fifty_block_forward_n6437_matches_oracle(wname):
+    wl = synth.WORKLOADS[wname]
     dims = wl.dims
     say("long depth: generating", wl.n_blocks, "blocks at N =", wl.n_rows)
     tags, pos = synth.packed_layout(wl)
@@ -55,6 +57,11 @@ def test_fifty_block_forward_n6437_matches_oracle():
     x64 = x.astype(np.float64)
     e, du = rel_l2(got, ref), rel_l2(got - x64, ref - x64)
     say("long depth: rel-L2 x_out", e, "update", du)
+    # bf16 weights: the stated full-depth bar.  W8A8: each side quantizes its own
+    # activations per row, so a code near a rounding boundary can differ between
+    # the two, and every block adds an independent error of up to the block bar;
+    # over B blocks that grows as sqrt(B): TOL_BLOCK * sqrt(50) = 7.1e-2
+    tol = TOL_DEPTH if wl.dims.wfmt != synth.WFMT_W8A8 else TOL_BLOCK * np.sqrt(wl.n_blocks)
     assert np.isfinite(got).all()
-    assert e < TOL_DEPTH
-    assert du < 2 * TOL_DEPTH
+    assert e < tol
+    assert du < 2 * tol
