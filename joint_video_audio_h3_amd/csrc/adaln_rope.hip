@@ -42,8 +42,11 @@ __global__ __launch_bounds__(256) void adaln_kernel(AdalnArgs a) {
   if (row >= a.n) return;
   const int nv = a.D >> 2;
   const float4* xr = reinterpret_cast<const float4*>(a.x + (size_t)row * a.D);
+  const int t = a.tag ? a.tag[row] : 0;   // no tags: one (shift, scale) pair for every row
+  const u16x4* sh = reinterpret_cast<const u16x4*>(a.table + ((size_t)t * 6 + a.k_shift) * a.D);
+  const u16x4* sc = reinterpret_cast<const u16x4*>(a.table + ((size_t)t * 6 + a.k_scale) * a.D);
   float4 v[VPL];
-  float s = 0.f;
+  u16x4 s4v[VPL], c4v[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int j = lane + 64 * i;
@@ -52,8 +55,20 @@ __global__ __launch_bounds__(256) void adaln_kernel(AdalnArgs a) {
     } else {
       v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
   }
+  // the row's (shift, scale) entries (L2 hits: n_tags rows) are in flight
+  // while the row is reduced, rather than fetched after the reductions
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int j = lane + 64 * i;
+    if (j < nv) {
+      s4v[i] = sh[j];
+      c4v[i] = sc[j];
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
   const float mean = wave_sum(s) / (float)a.D;
   float q = 0.f;
 #pragma unroll
@@ -66,16 +81,13 @@ __global__ __launch_bounds__(256) void adaln_kernel(AdalnArgs a) {
   }
   const float var = wave_sum(q) / (float)a.D;
   const float rstd = 1.0f / sqrtf(var + a.eps);
-  const int t = a.tag ? a.tag[row] : 0;   // no tags: one (shift, scale) pair for every row
-  const u16x4* sh = reinterpret_cast<const u16x4*>(a.table + ((size_t)t * 6 + a.k_shift) * a.D);
-  const u16x4* sc = reinterpret_cast<const u16x4*>(a.table + ((size_t)t * 6 + a.k_scale) * a.D);
   uint2* hr = reinterpret_cast<uint2*>(a.h + (size_t)row * a.D);
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int j = lane + 64 * i;
     if (j < nv) {
-      const u16x4 s4 = sh[j], c4 = sc[j];
+      const u16x4 s4 = s4v[i], c4 = c4v[i];
       const float o0 = (v[i].x - mean) * rstd * (1.0f + bf2f(c4[0])) + bf2f(s4[0]);
       const float o1 = (v[i].y - mean) * rstd * (1.0f + bf2f(c4[1])) + bf2f(s4[1]);
       const float o2 = (v[i].z - mean) * rstd * (1.0f + bf2f(c4[2])) + bf2f(s4[2]);
