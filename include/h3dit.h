@@ -35,9 +35,11 @@
  *     W[out][in].  n_pad = h3_padded_rows(n_rows) (a multiple of 256).
  *   - Modality tags must lie in [0, n_tags).  They are not checked unless
  *     H3_CHECK=1 is set in the environment: then every call that reads tags
- *     first scans them on the device (one small kernel and a wait for the
- *     stream, so not under stream capture) and returns H3_ERR_INVALID_ARG,
- *     with nothing else enqueued, if any lies outside that range.
+ *     first scans them on the device (one small kernel counting into a
+ *     4-byte counter in the library's static device memory, and a wait for
+ *     the stream, so not under stream capture; check-mode calls that overlap
+ *     on one device share the counter) and returns H3_ERR_INVALID_ARG, with
+ *     nothing else enqueued, if any lies outside that range.
  *
  * Supported shapes: hidden % 256 == 0 and hidden <= 8192; head_dim in
  * {96, 128}; ffn % 128 == 0 and (ffn + 256) * hidden * 2 < 2^32; rope_split

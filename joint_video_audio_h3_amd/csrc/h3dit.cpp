@@ -350,23 +350,23 @@ h3_status run_block(const h3_dims& d, float* x, const int32_t* tag, const uint16
 }
 
 // With H3_CHECK=1 in the environment, the modality tags are checked on the
-// device before anything else is enqueued: one small kernel, then a wait for
-// the stream (so not for use under stream capture).  Any tag outside
-// [0, n_tags) fails the call with nothing else enqueued.
+// device before anything else is enqueued: one small kernel counting into a
+// static device counter, then a wait for the stream (so not for use under
+// stream capture, and check-mode calls that overlap on one device share the
+// counter).  Any tag outside [0, n_tags) fails the call with nothing else
+// enqueued.
 h3_status check_tags(const h3_dims& d, const int32_t* tag, int64_t n, hipStream_t s) {
   const char* e = std::getenv("H3_CHECK");
   if (!e || std::strcmp(e, "1") != 0) return H3_OK;
   unsigned int* bad = nullptr;
   unsigned int host = 0;
   h3_status st;
-  if ((st = hip_ok(hipMalloc(&bad, sizeof(unsigned int)), "H3_CHECK buffer")) != H3_OK) return st;
+  if ((st = hip_ok(h3::bad_tags_counter(&bad), "H3_CHECK counter")) != H3_OK) return st;
   hipError_t r = hipMemsetAsync(bad, 0, sizeof(unsigned int), s);
   if (r == hipSuccess) r = h3::launch_count_bad_tags(tag, n, d.n_tags, bad, s);
   if (r == hipSuccess) r = hipMemcpyAsync(&host, bad, sizeof(unsigned int), hipMemcpyDeviceToHost, s);
   if (r == hipSuccess) r = hipStreamSynchronize(s);
-  const hipError_t rf = hipFree(bad);
   if ((st = hip_ok(r, "H3_CHECK tag scan")) != H3_OK) return st;
-  if ((st = hip_ok(rf, "H3_CHECK buffer")) != H3_OK) return st;
   if (host != 0)
     return fail(H3_ERR_INVALID_ARG, "%u modality tags outside [0, %d) (H3_CHECK)", host, d.n_tags);
   return H3_OK;

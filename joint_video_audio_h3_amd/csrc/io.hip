@@ -107,6 +107,25 @@ __global__ __launch_bounds__(256) void count_bad_tags_kernel(const int32_t* tag,
   if (c) atomicAdd(bad, c);
 }
 
+// The check's counter lives in the library's static device memory (one per
+// device, allocated with the code object), so the check allocates nothing.
+static __device__ __align__(256) unsigned int g_bad_tags;
+
+hipError_t bad_tags_counter(unsigned int** ptr) {
+  static unsigned int* addr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_bad_tags))) != hipSuccess) return e;
+    addr[dev] = static_cast<unsigned int*>(p);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 hipError_t launch_count_bad_tags(const int32_t* tag, int64_t n, int n_tags, unsigned int* bad, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = (n + 255) / 256;

@@ -82,6 +82,8 @@ hipError_t launch_patch_embed(const PatchArgs& a, hipStream_t s);
 // z[0..n) += dt * v[0..n)  (one Euler pass of a latent)
 hipError_t launch_euler(float* z, const float* v, float dt, int64_t n, hipStream_t s);
 
+// device address of the tag check's counter on the current device
+hipError_t bad_tags_counter(unsigned int** ptr);
 // *bad += number of tag[0..n) outside [0, n_tags)
 hipError_t launch_count_bad_tags(const int32_t* tag, int64_t n, int n_tags, unsigned int* bad, hipStream_t s);
 
