@@ -963,7 +963,8 @@ h3_status h3_velocity_forward(const h3_dims* dims, const h3_io_dims* io_dims,
   }
   if ((st = check_device()) != H3_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if ((st = check_tags(*dims, tag, n, s)) != H3_OK) return st;
+  // the tags are read only by the blocks (tag may be NULL when none runs)
+  if (n_blocks > 0 && (st = check_tags(*dims, tag, n, s)) != H3_OK) return st;
   if ((st = run_embed(*dims, *io_dims, *io_weights, sg, text, cond, audio, video, x_packed, s)) != H3_OK)
     return st;
   uint16_t* h = static_cast<uint16_t*>(workspace);

@@ -73,3 +73,32 @@ def test_check_mode_covers_step_calls(case, monkeypatch):
     h = torch.empty(wl.n_rows, wl.dims.hidden, dtype=torch.int16, device="cuda")
     with pytest.raises(lib.H3Error):
         lib.adaln_modulate(wl.dims, dev(x), dev(t), dev(table[0]), 0, h)
+
+
+def test_check_mode_velocity_forward_without_blocks_reads_no_tags(monkeypatch):
+    """With no block to run the velocity forward reads no tag, so tag may be
+    NULL: under H3_CHECK=1 the call still succeeds and matches the run without
+    the check bit for bit."""
+    dims, io = synth.TINY_DIMS, synth.TINY_IO
+    say("check mode: velocity forward, n_blocks = 0, tag NULL")
+    wl = synth.Workload("io", dims, 0, 16, 8, 20, (2, 8, 8))
+    inp = synth.make_io_inputs(wl, io, seed=72)
+    w = {k: (None if v is None else dev(v)) for k, v in synth.make_io_weights(dims, io, seed=72).items()}
+    ftab = dev(synth.make_final_table(dims, seed=72))
+    d = {k: (dev(v) if len(v) else None) for k, v in inp.items()}
+    sg = lib.segments_of(d["text"], d["cond"], d["audio"], d["video"])
+    ws = torch.empty(lib.heads_workspace_size(dims, sg), dtype=torch.uint8, device="cuda")
+
+    def run():
+        x = torch.empty(wl.n_rows, dims.hidden, dtype=torch.float32, device="cuda")
+        va = torch.empty(wl.A, io.audio_patch, dtype=torch.float32, device="cuda")
+        vv = torch.empty(128, io.video_patch, dtype=torch.float32, device="cuda")
+        lib.velocity_forward(dims, io, w, d["text"], d["cond"], d["audio"], d["video"],
+                             None, None, None, [], ftab, x, va, vv, ws)
+        torch.cuda.synchronize()
+        return va.cpu().numpy(), vv.cpu().numpy()
+
+    ref = run()
+    monkeypatch.setenv("H3_CHECK", "1")
+    got = run()
+    assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
