@@ -40,7 +40,8 @@
 // pairs (v_dot2), and only when some lane's 16 probabilities of a half sum
 // above 2^8 (so that no p can exceed 2^8, or overflow) is the half's maximum
 // formed, m raised, O and the running sum rescaled and p recomputed.  After
-// the first tile this is rare.  The first half always sets m to its maximum.
+// the first tile this is rare.  The first half always sets m to its maximum
+// (O and the sum are zero then, so nothing is rescaled).
 // Keys at or beyond n are masked in the last tile; padded rows of q/k/v^T are
 // zeros written by the QKV epilogue, so every operand is finite.
 //
@@ -243,11 +244,16 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float sh = first ? mx : fmaxf(mx, 0.f);
-      const float alpha = __builtin_amdgcn_exp2f(-sh);
       m_ref += sh;
-      l_run *= alpha;
+      // O and the running sum are still zero on the first half: nothing to
+      // rescale (and exp2(-sh) would overflow when every first score is far
+      // below zero)
+      if (!first) {
+        const float alpha = __builtin_amdgcn_exp2f(-sh);
+        l_run *= alpha;
 #pragma unroll
-      for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+        for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+      }
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[v] -= sh;
       shift_other(sh);

@@ -212,6 +212,37 @@ def make_activation_bf16(n: int, width: int, name: str, seed: int = 0, std: floa
     return f32_to_bf16_bits(a * np.float32(std))
 
 
+def make_peaked_qkv(heads: int, n: int, d: int, seed: int = 0) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Attention inputs whose softmax is sharply peaked: bf16 bits q, k, v [heads, n, d].
+
+    q is given in the attention kernels' convention (already multiplied by
+    log2(e)/sqrt(d)), so q . k is a score in log2 units.  Channel 0 carries a
+    key ramp: keys of the first 64 rows sit at -8, the later keys rise linearly
+    to +8 at the last row; every query scales that ramp by b ~ U(-1, 4), and the
+    other channels are N(0, 1) noise on both sides (a score spread of about 11
+    log2 units per query).  So scores span tens of log2 units and, for most
+    queries, the running maximum keeps rising tile after tile up to the last
+    (possibly partial) tile.  Row 0 of every head is 20 * e_0: its first 64
+    scores are -160 and its maximum is the last key; row 1 is -20 * e_0: its
+    maximum is in the first tile and the later scores fall to -160.
+    """
+    r = _rng(seed, 0, "q")
+    ramp = np.full(n, -8.0, np.float32)
+    if n > 65:
+        ramp[64:] = np.linspace(-8.0, 8.0, n - 64, dtype=np.float32)
+    k = _rng(seed, 0, "k").standard_normal((heads, n, d), dtype=np.float32)
+    k[:, :, 0] = ramp
+    q = r.standard_normal((heads, n, d), dtype=np.float32)
+    q[:, :, 0] = r.uniform(-1.0, 4.0, (heads, n)).astype(np.float32)
+    q[:, 0, :] = 0.0
+    q[:, 0, 0] = 20.0
+    if n > 1:
+        q[:, 1, :] = 0.0
+        q[:, 1, 0] = -20.0
+    v = _rng(seed, 0, "v").standard_normal((heads, n, d), dtype=np.float32)
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
 def make_tags(n: int, n_tags: int = 3, seed: int = 0) -> np.ndarray:
     """Random modality tags int32 [n] (for steps tested away from a packed layout)."""
     return _rng(seed, 0, "tags").integers(0, n_tags, n).astype(np.int32)
