@@ -119,3 +119,46 @@ def test_global_position_shift_invariance():
     a = _run_forward(wl, x, tags, pos, table, weights, 1)
     b = _run_forward(wl, x, tags, pos + np.float32([16, 8, 4]), table, weights, 1)
     assert rel_l2(b - x, a - x) < 1e-2
+
+
+@pytest.mark.timeout(900)
+def test_depth_parity_h3_width_fifty_blocks():
+    """The full depth: 50 H3-width blocks at N = 1,192 against the oracle, bar
+    3e-2 on x_out.  Each block's host weights are drawn, copied to the device,
+    used by the oracle and dropped, so the host never holds more than two
+    blocks (about 1.5 GB); the GPU side is one h3_dit_forward over the 50
+    device blocks (38.5 GB)."""
+    import concurrent.futures as cf
+
+    wl = synth.WORKLOADS["h3_1blk_n1192"]
+    dims, nb = wl.dims, 50
+    say("depth parity h3 x50: N =", wl.n_rows)
+    tags, pos = synth.packed_layout(wl)
+    x = synth.make_x(wl, dims, seed=51)
+    table = synth.make_table(dims, nb, seed=51)
+    ref = x.astype(np.float64)
+    devs = []
+    with cf.ThreadPoolExecutor(max_workers=1) as ex:
+        nxt = ex.submit(synth.make_block_weights, dims, 0, 51)
+        for b in range(nb):
+            host = nxt.result()
+            if b + 1 < nb:
+                nxt = ex.submit(synth.make_block_weights, dims, b + 1, 51)
+            devs.append(lib.to_device_block(host))
+            ref = oracle.block_forward(ref, tags, pos, table[b], host, dims)
+            del host
+            if b % 5 == 4:
+                say("  oracle and weights: block", b + 1, "of", nb)
+    xd = dev(x)
+    ws = lib.alloc_workspace(dims, wl.n_rows)
+    lib.dit_forward(dims, xd, dev(tags), dev(pos), dev(table), devs, ws)
+    torch.cuda.synchronize()
+    got = xd.cpu().numpy().astype(np.float64)
+    del devs, ws, xd
+    torch.cuda.empty_cache()
+    x64 = x.astype(np.float64)
+    e, du = rel_l2(got, ref), rel_l2(got - x64, ref - x64)
+    say(f"  rel-L2 after 50 blocks: x_out {e:.3e}  update {du:.3e}")
+    assert np.isfinite(got).all()
+    assert e < TOL_DEPTH
+    assert du < TOL_DEPTH

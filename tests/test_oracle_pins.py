@@ -372,3 +372,22 @@ def test_dit_forward_gates_zero_depth_identity(tiny_inputs):
     t[:, :, 5] = 0
     out = oracle.dit_forward(x, tags, pos, t, lambda b: weights[b], 2, wl.dims)
     np.testing.assert_array_equal(out, x.astype(np.float64))
+
+
+@pytest.mark.parametrize("live", [0, 1])
+def test_dit_forward_runs_each_block_with_its_own_table_and_weights(tiny_inputs, live):
+    """With every residual gate of one block zero, that block is the identity
+    (bit for bit), so the 2-block forward equals the other block alone, with
+    that block's own table slice and weights.  A forward that used block 0's
+    table or weights for every block, or the blocks in the wrong order, fails."""
+    wl, (x, tags, pos, table, weights) = tiny_inputs
+    dead = 1 - live
+    t = table.copy()
+    t[dead, :, 2] = 0
+    t[dead, :, 5] = 0
+    out = oracle.dit_forward(x, tags, pos, t, lambda b: weights[b], 2, wl.dims)
+    alone = oracle.block_forward(x, tags, pos, table[live], weights[live], wl.dims)
+    np.testing.assert_array_equal(out, alone)
+    # and the two blocks really differ: the other block alone gives another answer
+    other = oracle.block_forward(x, tags, pos, table[dead], weights[dead], wl.dims)
+    assert np.abs(other - alone).max() > 1e-2
