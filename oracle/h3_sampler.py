@@ -20,12 +20,20 @@ With these, the video (12) and audio (3) schedules of 40 passes meet at exactly
 three base points (b = 1; 0.5 with 0.8; 0.2 with 0.5), 80 - 3 = 77.  Text and
 condition rows are not denoised.
 
-Whole-velocity reuse (H3-metal digest, "4. Choose a speed/quality preset"):
+Whole-velocity reuse (H3-metal digest, "4. Choose a speed/quality preset":
 with reuse r, a 20-pass run makes 20, 11 or 8 fresh model evaluations for
-r = 1, 2, 3, and the skipped transitions are extrapolated.  Reading: pass i is
-fresh when i % r == 0 or it is the last pass (the only forward schedule that
-gives those counts and starts fresh); a skipped pass steps each latent with the
-velocity of the last fresh pass.
+r = 1, 2, 3; "Sampler and DiT controls": the first and last pass and every
+requested interval are evaluated, and the skipped video and audio velocities
+are extrapolated on their independent schedules).  Reading: pass i is fresh
+when i % r == 0 or it is the last pass (the only forward schedule that gives
+those counts and starts fresh).  A skipped pass i extrapolates each modality's
+velocity linearly in that modality's own sigma from its last two fresh
+velocities, taken at passes j0 < j1:
+
+    u_m = v_m(j1) + (sigma_m[i] - sigma_m[j1]) / (sigma_m[j1] - sigma_m[j0]) * (v_m(j1) - v_m(j0))
+
+While only one fresh velocity exists (the passes right after pass 0), the
+straight line has one point and u_m = v_m(j1).
 """
 from __future__ import annotations
 
@@ -64,20 +72,37 @@ def fresh_passes(steps: int, reuse: int = 1) -> np.ndarray:
     return (i % reuse == 0) | (i == steps - 1)
 
 
+def extrapolate(sigmas, i: int, j0: int, v0, j1: int, v1) -> np.ndarray:
+    """The velocity at pass i on the straight line through (sigma[j0], v0) and
+    (sigma[j1], v1), sigma being one modality's schedule."""
+    c = (sigmas[i] - sigmas[j1]) / (sigmas[j1] - sigmas[j0])
+    return v1 + c * (v1 - v0)
+
+
 def denoise(audio0, video0, sig_audio, sig_video,
             velocity_pair: Callable[[int, np.ndarray, np.ndarray], Tuple[np.ndarray, np.ndarray]],
             reuse: int = 1):
     """Joint Euler over both modalities: a fresh pass runs one velocity forward
-    for (v_audio, v_video) from the current latents, a skipped one (reuse > 1)
-    keeps the last fresh pair; each latent steps on its own schedule."""
+    for (v_audio, v_video) from the current latents; a skipped one (reuse > 1)
+    extrapolates each modality's last two fresh velocities in its own sigma
+    (holds the only one right after pass 0); each latent steps on its own
+    schedule."""
     a = np.asarray(audio0, np.float64).copy()
     v = np.asarray(video0, np.float64).copy()
     steps = len(sig_video) - 1
     fresh = fresh_passes(steps, reuse)
-    va = vv = None
+    hist = []          # (pass, v_audio, v_video) of the last two fresh passes
     for i in range(steps):
         if fresh[i]:
             va, vv = velocity_pair(i, a, v)
-        a = a + (sig_audio[i + 1] - sig_audio[i]) * va
-        v = v + (sig_video[i + 1] - sig_video[i]) * vv
+            hist = (hist + [(i, np.asarray(va, np.float64), np.asarray(vv, np.float64))])[-2:]
+            ua, uv = hist[-1][1], hist[-1][2]
+        elif len(hist) == 1:
+            ua, uv = hist[0][1], hist[0][2]
+        else:
+            (j0, a0, w0), (j1, a1, w1) = hist
+            ua = extrapolate(sig_audio, i, j0, a0, j1, a1)
+            uv = extrapolate(sig_video, i, j0, w0, j1, w1)
+        a = a + (sig_audio[i + 1] - sig_audio[i]) * ua
+        v = v + (sig_video[i + 1] - sig_video[i]) * uv
     return a, v

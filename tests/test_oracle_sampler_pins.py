@@ -5,8 +5,9 @@ the audio shift 3.0 evaluate 77 distinct timesteps.  The Euler update is tied
 to closed forms: a constant velocity telescopes to z0 - c, and the linear field
 dz/dsigma = lambda z gives the product of (1 + lambda dt) exactly.  Velocity
 reuse is pinned by the pages' counts of fresh evaluations (20, 11, 8 at 20
-passes for reuse 1, 2, 3), by which passes call the model, and by a linear
-field stepped along the held velocity.
+passes for reuse 1, 2, 3), by which passes call the model, by velocity fields
+linear in each modality's sigma (reproduced exactly, which a held velocity is
+not), and by the known error of extrapolating a quadratic.
 """
 import json
 import os
@@ -82,7 +83,7 @@ def test_fresh_evaluation_counts_of_the_pages_reuse_presets():
         assert fresh[0] and fresh[-1]                     # starts fresh, ends on a fresh velocity
 
 
-def test_reuse_calls_the_model_only_on_fresh_passes_and_holds_its_velocity():
+def test_reuse_calls_the_model_only_on_fresh_passes():
     sa, sv = S.schedule(5, 3.0), S.schedule(5, 12.0)
     calls = []
 
@@ -90,20 +91,74 @@ def test_reuse_calls_the_model_only_on_fresh_passes_and_holds_its_velocity():
         calls.append(i)
         return np.full(2, float(i + 1)), np.full(3, -float(i + 1))
 
-    a, v = S.denoise(np.zeros(2), np.zeros(3), sa, sv, vel, reuse=2)
+    S.denoise(np.zeros(2), np.zeros(3), sa, sv, vel, reuse=2)
     assert calls == [0, 2, 4]
-    held = np.array([1, 1, 3, 3, 5], dtype=float)         # velocity used at each pass
-    np.testing.assert_allclose(a, np.full(2, np.dot(np.diff(sa), held)), rtol=1e-13)
-    np.testing.assert_allclose(v, np.full(3, -np.dot(np.diff(sv), held)), rtol=1e-13)
+    calls.clear()
+    S.denoise(np.zeros(2), np.zeros(3), S.schedule(20, 3.0), S.schedule(20, 12.0), vel, reuse=3)
+    assert calls == [0, 3, 6, 9, 12, 15, 18, 19]
 
 
-def test_reuse_on_a_linear_field_extrapolates_along_the_held_velocity():
-    # dz/dsigma = lam z, reuse 2 over 3 passes: fresh at 0 and 2 (the last)
+@pytest.mark.parametrize("reuse", [2, 3, 5])
+def test_reuse_is_exact_on_velocities_linear_in_each_modalitys_sigma(reuse):
+    """A velocity field that is a straight line in each modality's own sigma
+    (and does not depend on the latents) is reproduced exactly by linear
+    extrapolation once two fresh velocities exist, so the reuse loop equals the
+    loop that evaluates every pass except on passes 1 .. reuse-1, which hold
+    v(sigma_0): there it differs by exactly dt_i * beta * (sigma_i - sigma_0).
+    A held (zero-order) velocity fails this, and so does extrapolating audio
+    along the video schedule (the two schedules are not proportional)."""
+    steps = 20
+    sa, sv = S.schedule(steps, 3.0), S.schedule(steps, 12.0)
+    r = np.random.default_rng(5)
+    al_a, be_a, al_v, be_v = (r.standard_normal(n) for n in (4, 4, 6, 6))
+    field = lambda i, a, v: (al_a + be_a * sa[i], al_v + be_v * sv[i])  # noqa: E731
+    a0, v0 = r.standard_normal(4), r.standard_normal(6)
+    fa, fv = S.denoise(a0, v0, sa, sv, field, reuse=1)
+    ga, gv = S.denoise(a0, v0, sa, sv, field, reuse=reuse)
+    hold = range(1, reuse)
+    np.testing.assert_allclose(ga, fa - sum((sa[i + 1] - sa[i]) * be_a * (sa[i] - sa[0]) for i in hold),
+                               rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(gv, fv - sum((sv[i + 1] - sv[i]) * be_v * (sv[i] - sv[0]) for i in hold),
+                               rtol=1e-12, atol=1e-12)
+    # the closed form of the exact Euler sum: sum_i dt_i (alpha + beta sigma_i)
+    np.testing.assert_allclose(fa, a0 + al_a * (sa[-1] - sa[0]) + be_a * np.dot(np.diff(sa), sa[:-1]),
+                               rtol=1e-12, atol=1e-12)
+    # a zero-order hold, written out, gives another answer on the same field
+    fresh = S.fresh_passes(steps, reuse)
+    held, last = a0.copy(), None
+    for i in range(steps):
+        if fresh[i]:
+            last = al_a + be_a * sa[i]
+        held = held + (sa[i + 1] - sa[i]) * last
+    assert np.abs(held - ga).max() > 1e-3
+
+
+def test_reuse_extrapolation_of_a_quadratic_has_the_known_error():
+    """v = sigma^2 (audio) and v = -3 sigma^2 (video), reuse 3 over 7 passes:
+    fresh at 0, 3 and 6; passes 1 and 2 hold v(0) (one fresh velocity so far),
+    passes 4 and 5 take the straight line through passes 0 and 3, which misses
+    sigma_i^2 by exactly (sigma_i - sigma_0)(sigma_i - sigma_3)."""
+    steps, reuse = 7, 3
+    sa, sv = S.schedule(steps, 3.0), S.schedule(steps, 12.0)
+    field = lambda i, a, v: (np.array([sa[i] ** 2]), np.array([-3.0 * sv[i] ** 2]))  # noqa: E731
+    fa, fv = S.denoise(np.zeros(1), np.zeros(1), sa, sv, field, reuse=1)
+    ga, gv = S.denoise(np.zeros(1), np.zeros(1), sa, sv, field, reuse=reuse)
+    err_a = sum((sa[i + 1] - sa[i]) * (sa[i] ** 2 - sa[0] ** 2) for i in (1, 2))
+    err_a += sum((sa[i + 1] - sa[i]) * (sa[i] - sa[0]) * (sa[i] - sa[3]) for i in (4, 5))
+    err_v = sum((sv[i + 1] - sv[i]) * -3.0 * (sv[i] ** 2 - sv[0] ** 2) for i in (1, 2))
+    err_v += sum((sv[i + 1] - sv[i]) * -3.0 * (sv[i] - sv[0]) * (sv[i] - sv[3]) for i in (4, 5))
+    np.testing.assert_allclose(fa - ga, [err_a], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(fv - gv, [err_v], rtol=1e-12, atol=1e-14)
+
+
+def test_reuse_on_a_linear_field_holds_while_one_fresh_velocity_exists():
+    # dz/dsigma = lam z, reuse 2 over 3 passes: fresh at 0 and 2 (the last);
+    # pass 1 has a single fresh velocity to go on, so it steps along it
     lam, z0 = 0.6, 1.25
     s = S.schedule(3, 12.0)
     d = np.diff(s)
     z1 = z0 + d[0] * lam * z0
-    z2 = z1 + d[1] * lam * z0                              # pass 1 reuses pass 0's velocity
+    z2 = z1 + d[1] * lam * z0
     z3 = z2 + d[2] * lam * z2
     a, v = S.denoise(np.array([z0]), np.array([z0]), s, s, lambda i, a, v: (lam * a, lam * v), reuse=2)
     np.testing.assert_allclose(a, [z3], rtol=1e-13)
