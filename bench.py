@@ -476,7 +476,7 @@ def main():
         d = {k: dv(v) for k, v in inp.items()}
         _, tags2, pos2 = synth.make_device_rows(wl2, seed=0)
         x2 = torch.empty(wl2.n_rows, dims.hidden, dtype=torch.float32, device="cuda")
-        ws2 = lib.alloc_workspace(dims, wl2.n_rows)
+        ws2 = lib.alloc_denoise_workspace(dims, io, d["text"], d["cond"], d["audio"], d["video"])
         sa, sv = lib.sigma_schedule(steps_d, 3.0), lib.sigma_schedule(steps_d, 12.0)
         def timed_loop(reuse):
             run = lambda: lib.denoise(dims, io, iw, d["text"], d["cond"], d["audio"], d["video"], tags2,  # noqa: E731

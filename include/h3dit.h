@@ -346,10 +346,15 @@ H3DIT_API h3_status h3_sigma_schedule(int32_t n_steps, double shift, double* sig
  * mod_tables + i*n_blocks*T*6*D and the final table final_tables + i*2*2*D);
  * then every pass steps, per modality,  z += (sigma[i+1] - sigma[i]) * v.
  * Whole-velocity reuse (H3-metal digest, "4. Choose a speed/quality preset":
- * at 20 passes, reuse 1, 2, 3 make 20, 11, 8 fresh evaluations and extrapolate
- * the skipped transitions): pass i is fresh when i % reuse == 0 or it is the
- * last pass; a skipped pass steps with the last fresh velocities.  reuse >= 1
- * (1: every pass fresh).
+ * at 20 passes, reuse 1, 2, 3 make 20, 11, 8 fresh evaluations; "Sampler and
+ * DiT controls": the skipped video and audio velocities are extrapolated on
+ * their independent schedules): pass i is fresh when i % reuse == 0 or it is
+ * the last pass.  A skipped pass i steps each modality m along
+ *   v1 + (sigma_m[i] - sigma_m[j1]) / (sigma_m[j1] - sigma_m[j0]) * (v1 - v0),
+ * the straight line in that modality's sigma through its last two fresh
+ * velocities v0 (pass j0) and v1 (pass j1 > j0); while only one fresh velocity
+ * exists (right after pass 0) it steps along that one.  reuse >= 1 (1: every
+ * pass fresh).
  *   audio fp32 [audio][audio_patch], video fp32 [video][video_patch]: the
  *         latents, updated in place (text and condition inputs stay fixed)
  *   mod_tables bf16 [n_steps][n_blocks][T][6][D]; final_tables bf16
@@ -357,7 +362,14 @@ H3DIT_API h3_status h3_sigma_schedule(int32_t n_steps, double shift, double* sig
  *         timesteps, precomputed as in "AdaLN precompute")
  *   sigmas_audio, sigmas_video: host double [n_steps + 1] (h3_sigma_schedule)
  *   x_packed fp32 [N][D]: scratch for the stream; workspace at least
- *         h3_workspace_size(dims, N) bytes.  n_blocks >= 1. */
+ *         h3_denoise_workspace_size() bytes: the block workspace, then the
+ *         last two fresh velocities of each modality.  n_blocks >= 1. */
+/* Workspace bytes of h3_denoise: h3_workspace_size(dims, N) plus two fp32
+ * velocity slots per modality ([audio][audio_patch] and [video][video_patch]),
+ * each rounded up to 256 bytes.  0 on invalid arguments.  Pure host function. */
+H3DIT_API size_t h3_denoise_workspace_size(const h3_dims* dims, const h3_io_dims* io_dims,
+                                          const h3_segments* segments);
+
 H3DIT_API h3_status h3_denoise(const h3_dims* dims, const h3_io_dims* io_dims,
                                const h3_io_weights* io_weights, const h3_segments* segments,
                                const uint16_t* text, const float* cond, float* audio, float* video,

@@ -541,6 +541,19 @@ const float* act_scales(const h3_dims& d, const void* act, int64_t n, int64_t K)
   return reinterpret_cast<const float*>(static_cast<const char*>(act) + qa_scale_offset(n, K));
 }
 
+// Velocity history of the denoising loop, after the block arena: two slots per
+// modality (the last two fresh velocities), each 256-byte aligned.
+struct VelHistory {
+  size_t a_bytes, v_bytes, bytes;
+};
+VelHistory vel_history(const h3_io_dims& io, const h3_segments& sg) {
+  VelHistory h{};
+  h.a_bytes = up256((size_t)sg.audio * io.audio_patch * 4);
+  h.v_bytes = up256((size_t)sg.video * io.video_patch * 4);
+  h.bytes = 2 * (h.a_bytes + h.v_bytes);
+  return h;
+}
+
 }  // namespace
 
 extern "C" {
@@ -635,6 +648,11 @@ h3_status h3_denoise(const h3_dims* dims, const h3_io_dims* io_dims, const h3_io
   if ((st = check_forward_common(dims, x_packed, tag, positions, mod_tables, n, workspace,
                                  workspace_bytes)) != H3_OK)
     return st;
+  const size_t arena = carve(*dims, n, nullptr).bytes;
+  const VelHistory vh = vel_history(*io_dims, sg);
+  if (workspace_bytes < arena + vh.bytes)
+    return fail(H3_ERR_WORKSPACE, "workspace is %zu bytes, %zu needed (h3_denoise_workspace_size)",
+                workspace_bytes, arena + vh.bytes);
   if (!weights) return fail(H3_ERR_INVALID_ARG, "weights is NULL");
   for (int b = 0; b < n_blocks; ++b) {
     if ((st = check_weights(dims, &weights[b], true, true, true, true)) != H3_OK) {
@@ -642,27 +660,24 @@ h3_status h3_denoise(const h3_dims* dims, const h3_io_dims* io_dims, const h3_io
       return fail(st, "block %d: %s", b, m.c_str());
     }
   }
-  // the velocities live in the attention-output arena, dead after the last block
-  const size_t va_bytes = up256((size_t)sg.audio * io_dims->audio_patch * 4);
-  const size_t vv_bytes = up256((size_t)sg.video * io_dims->video_patch * 4);
-  const size_t o_bytes = (size_t)pad_rows(n) * dims->heads * dims->head_dim * 2;
-  if (va_bytes + vv_bytes > o_bytes)
-    return fail(H3_ERR_UNSUPPORTED, "velocities (%zu bytes) exceed the attention-output arena (%zu)",
-                va_bytes + vv_bytes, o_bytes);
   if ((st = check_device()) != H3_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if ((st = check_tags(*dims, tag, n, s)) != H3_OK) return st;
   const Arena ar = carve(*dims, n, static_cast<char*>(workspace));
-  float* vel_a = reinterpret_cast<float*>(ar.o);
-  float* vel_v = reinterpret_cast<float*>(reinterpret_cast<char*>(ar.o) + va_bytes);
+  char* hist = static_cast<char*>(workspace) + arena;
+  float* vel_a[2] = {reinterpret_cast<float*>(hist), reinterpret_cast<float*>(hist + vh.a_bytes)};
+  float* vel_v[2] = {reinterpret_cast<float*>(hist + 2 * vh.a_bytes),
+                     reinterpret_cast<float*>(hist + 2 * vh.a_bytes + vh.v_bytes)};
   if ((st = hip_ok(do_rope(*dims, positions, n, ar.cs, s), "rope table")) != H3_OK) return st;
   const size_t tstride = (size_t)dims->n_tags * 6 * dims->hidden;
   const size_t fstride = (size_t)4 * dims->hidden;
+  const int64_t na = sg.audio * io_dims->audio_patch, nv = sg.video * io_dims->video_patch;
+  int fresh_count = 0, j0 = -1, j1 = -1;   // the last two fresh passes (j0 < j1)
   for (int i = 0; i < n_steps; ++i) {
-    // a skipped pass keeps the velocities of the last fresh one: nothing else
-    // writes the attention-output arena between passes
     const bool fresh = i % reuse == 0 || i == n_steps - 1;
     if (fresh) {
+      // the new velocities go to the slot not holding the last fresh ones
+      const int slot = fresh_count % 2;
       if ((st = run_embed(*dims, *io_dims, *io_weights, sg, text, cond, audio, video, x_packed, s)) != H3_OK)
         return fail(st, "step %d: %s", i, std::string(g_err).c_str());
       const uint16_t* tab = mod_tables + (size_t)i * n_blocks * tstride;
@@ -670,18 +685,41 @@ h3_status h3_denoise(const h3_dims* dims, const h3_io_dims* io_dims, const h3_io
         if ((st = run_block(*dims, x_packed, tag, tab + b * tstride, weights[b], n, ar, s)) != H3_OK)
           return fail(st, "step %d block %d: %s", i, b, std::string(g_err).c_str());
       }
-      if ((st = run_heads(*dims, *io_dims, *io_weights, sg, x_packed, final_tables + i * fstride, vel_a,
-                          vel_v, ar.h, s)) != H3_OK)
+      if ((st = run_heads(*dims, *io_dims, *io_weights, sg, x_packed, final_tables + i * fstride,
+                          vel_a[slot], vel_v[slot], ar.h, s)) != H3_OK)
         return fail(st, "step %d: %s", i, std::string(g_err).c_str());
+      ++fresh_count;
+      j0 = j1;
+      j1 = i;
     }
-    const float dta = (float)(sigmas_audio[i + 1] - sigmas_audio[i]);
-    const float dtv = (float)(sigmas_video[i + 1] - sigmas_video[i]);
-    if ((st = hip_ok(h3::launch_euler(audio, vel_a, dta, sg.audio * io_dims->audio_patch, s), "euler audio")) != H3_OK)
-      return st;
-    if ((st = hip_ok(h3::launch_euler(video, vel_v, dtv, sg.video * io_dims->video_patch, s), "euler video")) != H3_OK)
-      return st;
+    const int cur = (fresh_count - 1) % 2, prev = 1 - cur;
+    const double dta = sigmas_audio[i + 1] - sigmas_audio[i];
+    const double dtv = sigmas_video[i + 1] - sigmas_video[i];
+    if (fresh || j0 < 0) {
+      // a fresh velocity, or the only one there is
+      if ((st = hip_ok(h3::launch_euler(audio, vel_a[cur], (float)dta, na, s), "euler audio")) != H3_OK) return st;
+      if ((st = hip_ok(h3::launch_euler(video, vel_v[cur], (float)dtv, nv, s), "euler video")) != H3_OK) return st;
+    } else {
+      // extrapolated on each modality's own schedule through (sigma[j0], v0) and (sigma[j1], v1)
+      const double ca = (sigmas_audio[i] - sigmas_audio[j1]) / (sigmas_audio[j1] - sigmas_audio[j0]);
+      const double cv = (sigmas_video[i] - sigmas_video[j1]) / (sigmas_video[j1] - sigmas_video[j0]);
+      if ((st = hip_ok(h3::launch_euler2(audio, vel_a[cur], vel_a[prev], (float)(dta * (1.0 + ca)),
+                                         (float)(-dta * ca), na, s), "euler audio")) != H3_OK)
+        return st;
+      if ((st = hip_ok(h3::launch_euler2(video, vel_v[cur], vel_v[prev], (float)(dtv * (1.0 + cv)),
+                                         (float)(-dtv * cv), nv, s), "euler video")) != H3_OK)
+        return st;
+    }
   }
   return H3_OK;
+}
+
+size_t h3_denoise_workspace_size(const h3_dims* dims, const h3_io_dims* io_dims,
+                                 const h3_segments* segments) {
+  if (check_io(dims, io_dims, segments) != H3_OK) return 0;
+  const h3_segments& sg = *segments;
+  return carve(*dims, sg.text + sg.cond + sg.audio + sg.video, nullptr).bytes +
+         vel_history(*io_dims, sg).bytes;
 }
 
 size_t h3_quantized_bytes(int64_t n_rows, int32_t width) {

@@ -81,6 +81,9 @@ hipError_t launch_patch_embed(const PatchArgs& a, hipStream_t s);
 
 // z[0..n) += dt * v[0..n)  (one Euler pass of a latent)
 hipError_t launch_euler(float* z, const float* v, float dt, int64_t n, hipStream_t s);
+// z[0..n) += a * v1[0..n) + b * v0[0..n)  (an Euler pass along an extrapolated velocity)
+hipError_t launch_euler2(float* z, const float* v1, const float* v0, float a, float b, int64_t n,
+                         hipStream_t s);
 
 // device address of the tag check's counter on the current device
 hipError_t bad_tags_counter(unsigned int** ptr);

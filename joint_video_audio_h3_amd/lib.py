@@ -80,6 +80,7 @@ _SIGS = {
     "h3_heads_workspace_size": (c_sz, [_PD, _PSG]),
     "h3_quantized_bytes": (c_sz, [c_i64, c_i32]),
     "h3_sigma_schedule": (c_i32, [c_i32, ctypes.c_double, ctypes.POINTER(ctypes.c_double)]),
+    "h3_denoise_workspace_size": (c_sz, [_PD, _PIO, _PSG]),
     "h3_denoise": (c_i32, [_PD, _PIO, _PW, _PSG, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                            ctypes.POINTER(H3BlockWeights), c_i32, c_vp,
                            ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), c_i32,
@@ -263,11 +264,27 @@ def sigma_schedule(n_steps: int, shift: float):
     return list(buf)
 
 
+def denoise_workspace_size(dims, io, segments: "H3Segments") -> int:
+    sz = load().h3_denoise_workspace_size(ctypes.byref(make_dims(dims)), ctypes.byref(make_io_dims(io)),
+                                          ctypes.byref(segments))
+    if sz == 0:
+        raise H3Error(H3_ERR_INVALID_ARG, last_error())
+    return sz
+
+
+def alloc_denoise_workspace(dims, io, text, cond, audio, video, device="cuda"):
+    import torch
+    sg = segments_of(text, cond, audio, video)
+    return torch.empty(denoise_workspace_size(dims, io, sg), dtype=torch.uint8, device=device)
+
+
 def denoise(dims, io, io_w: Dict, text, cond, audio, video, tag, positions, mod_tables,
             blocks: Sequence[Dict], final_tables, sigmas_audio, sigmas_video, x, workspace,
             stream=None, reuse: int = 1):
     """len(sigmas) - 1 Euler passes; audio / video latents updated in place.
-    reuse r: fresh velocities at passes i % r == 0 and the last, held between."""
+    reuse r: fresh velocities at passes i % r == 0 and the last; a skipped pass
+    extrapolates each modality's last two fresh velocities in its own sigma.
+    ``workspace``: alloc_denoise_workspace()."""
     sg = segments_of(text, cond, audio, video)
     w = make_io_weights(io_w)
     arr = (H3BlockWeights * len(blocks))(*[make_weights(b) for b in blocks])

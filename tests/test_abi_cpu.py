@@ -231,3 +231,15 @@ def test_denoise_argument_errors_before_launch(L):
     assert call(n_blocks=0) == lib.H3_ERR_INVALID_ARG
     assert call(sa=None) == lib.H3_ERR_INVALID_ARG and "sigmas" in lib.last_error()
     assert call(ws_bytes=ws - 256) == lib.H3_ERR_WORKSPACE
+
+
+def test_denoise_workspace_adds_two_velocity_slots_per_modality(L):
+    d, io = synth.H3_DIMS, synth.H3_IO
+    sg = lib.make_segments(256, 1024, 200, 48360)
+    n = 256 + 1024 + 200 + 48360
+    up = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    slots = 2 * (up(200 * io.audio_patch * 4) + up(48360 * io.video_patch * 4))
+    assert lib.denoise_workspace_size(d, io, sg) == lib.workspace_size(d, n) + slots
+    sg_bad = lib.make_segments(-1, 0, 0, 10)
+    assert L.h3_denoise_workspace_size(ctypes.byref(lib.make_dims(d)), ctypes.byref(lib.make_io_dims(io)),
+                                       ctypes.byref(sg_bad)) == 0

@@ -3,9 +3,11 @@
 Each pass of the oracle runs its own velocity forward (inputs, blocks, final
 AdaLN and heads) with that pass's tables; the latents step on the video (12)
 and audio (3) shifted schedules.  One GPU pass also equals one velocity
-forward followed by the Euler update.  With velocity reuse 2 over 4 passes
-(fresh at 0, 2 and 3) the loop matches the oracle's reuse schedule, and the
-skipped pass moves each latent by its step times the held velocity.
+forward followed by the Euler update.  With velocity reuse the loop matches
+the oracle's reuse loop: 2 over 4 passes (fresh at 0, 2 and 3; pass 1 steps
+along the only fresh velocity), 3 over 7 passes (fresh at 0, 3 and 6; passes 4
+and 5 extrapolate each modality's velocity in its own sigma through passes 0
+and 3), and 5 over 3 passes (first and last only).
 """
 import numpy as np
 import pytest
@@ -38,7 +40,7 @@ def _case(dims, io, L, C, A, vgrid, nb, steps, seed):
 def _gpu(dims, io, wl, tags, pos, tables, finals, blocks, inp, w, sa, sv, reuse=1):
     d = {k: (dev(v) if len(v) else None) for k, v in inp.items()}
     x = torch.empty(wl.n_rows, dims.hidden, dtype=torch.float32, device="cuda")
-    ws = lib.alloc_workspace(dims, wl.n_rows)
+    ws = lib.alloc_denoise_workspace(dims, io, d["text"], d["cond"], d["audio"], d["video"])
     iw = {k: (None if v is None else dev(v)) for k, v in w.items()}
     lib.denoise(dims, io, iw, d["text"], d["cond"], d["audio"], d["video"], dev(tags), dev(pos),
                 dev(np.ascontiguousarray(tables)), [lib.to_device_block(b) for b in blocks],
@@ -132,3 +134,36 @@ def test_reuse_beyond_steps_runs_first_and_last_pass_only():
     ra, rv = oracle.denoise(inp["audio"], inp["video"], np.array(sa), np.array(sv), vel, reuse=5)
     assert calls == [0, 2]
     assert rel_l2(ga, ra) < TOL_DEPTH and rel_l2(gv, rv) < TOL_DEPTH
+
+
+def test_denoise_reuse_extrapolates_skipped_velocities(monkeypatch):
+    """Reuse 3 over 7 passes: fresh at 0, 3 and 6; passes 1 and 2 step along
+    the velocity of pass 0, passes 4 and 5 along the straight line in each
+    modality's sigma through the velocities of passes 0 and 3."""
+    dims, io = synth.TINY_DIMS, synth.TINY_IO
+    steps, reuse = 7, 3
+    say("denoise reuse", reuse, steps)
+    wl, tags, pos, tables, finals, blocks, inp, w = _case(dims, io, 16, 8, 20, (2, 8, 8), 2, steps, seed=44)
+    sa, sv = lib.sigma_schedule(steps, 3.0), lib.sigma_schedule(steps, 12.0)
+    ga, gv = _gpu(dims, io, wl, tags, pos, tables, finals, blocks, inp, w, sa, sv, reuse=reuse)
+    calls = []
+
+    def vel(i, a, v):
+        calls.append(i)
+        return oracle.velocity_forward(inp["text"], inp["cond"], a.astype(np.float32), v.astype(np.float32),
+                                       w, finals[i], tags, pos, tables[i], lambda b: blocks[b], 2, dims)
+
+    ra, rv = oracle.denoise(inp["audio"], inp["video"], np.array(sa), np.array(sv), vel, reuse=reuse)
+    assert calls == [0, 3, 6]
+    ea, ev = rel_l2(ga, ra), rel_l2(gv, rv)
+    da = rel_l2(ga - inp["audio"], ra - inp["audio"])
+    dv = rel_l2(gv - inp["video"], rv - inp["video"])
+    say("denoise reuse 3 rel-L2 audio", ea, "video", ev, "| updates", da, dv)
+    assert ea < TOL_DEPTH and ev < TOL_DEPTH and da < 2 * TOL_DEPTH and dv < 2 * TOL_DEPTH
+    # the extrapolation matters at this size: the oracle with held velocities
+    # on passes 4 and 5 lands much farther from the GPU result
+    import oracle.h3_sampler as sampler
+    monkeypatch.setattr(sampler, "extrapolate", lambda sig, i, j0, v0, j1, v1: v1)
+    ha, hv = oracle.denoise(inp["audio"], inp["video"], np.array(sa), np.array(sv), vel, reuse=reuse)
+    say("  held instead: rel-L2 audio", rel_l2(ga, ha), "video", rel_l2(gv, hv))
+    assert rel_l2(gv - inp["video"], hv - inp["video"]) > 5 * dv
