@@ -142,6 +142,26 @@ H3DIT_API h3_status h3_dit_forward(const h3_dims* dims, float* x_packed, const i
                                    int64_t n_rows, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/* Size of the library's own scratch array on each GPU (128 MiB), the largest
+ * workspace h3_dit_forward_noalloc can use. */
+#define H3_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* h3_dit_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same blocks, kernels and results, with the workspace taken from the
+ * library's static scratch array (H3_NOALLOC_SCRATCH_BYTES per GPU, held from
+ * the library's first use of that GPU until the process ends) instead of a
+ * caller buffer.  Calls nothing that allocates.  Fails with H3_ERR_WORKSPACE
+ * when h3_workspace_size(dims, n_rows) exceeds the array: at H3 width that is
+ * above 1,792 rows with bf16 or INT8 weights and above 1,536 rows with W8A8.
+ * Every call on one GPU uses the same array (nothing in it has to start at
+ * zero, and the last call's contents stay there): calls that overlap on one
+ * GPU, on any streams, race and give undefined results. */
+H3DIT_API h3_status h3_dit_forward_noalloc(const h3_dims* dims, float* x_packed, const int32_t* tag,
+                                           const float* positions, const uint16_t* mod_table,
+                                           const h3_block_weights* weights, int32_t n_blocks,
+                                           int64_t n_rows, void* stream);
+
 /* h3_dit_forward with block-sparse attention in every block (see
  * h3_attention_sparse): block b reads its selection from the CSR offsets
  * tile_off + b * (heads*nq + 1), which index the one array tile_idx.  Each

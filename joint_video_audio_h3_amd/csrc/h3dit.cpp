@@ -801,6 +801,26 @@ h3_status h3_dit_forward(const h3_dims* dims, float* x, const int32_t* tag, cons
   return H3_OK;
 }
 
+h3_status h3_dit_forward_noalloc(const h3_dims* dims, float* x, const int32_t* tag,
+                                 const float* positions, const uint16_t* mod_table,
+                                 const h3_block_weights* weights, int32_t n_blocks, int64_t n_rows,
+                                 void* stream) {
+  g_err.clear();
+  h3_status st;
+  if ((st = check_dims(dims)) != H3_OK || (st = check_rows(n_rows)) != H3_OK) return st;
+  const size_t need = carve(*dims, n_rows, nullptr).bytes;
+  if (need > H3_NOALLOC_SCRATCH_BYTES)
+    return fail(H3_ERR_WORKSPACE,
+                "h3_dit_forward_noalloc: %lld rows need a %zu-byte workspace, above the %zu-byte "
+                "static scratch array (use h3_dit_forward with a caller workspace)",
+                (long long)n_rows, need, (size_t)H3_NOALLOC_SCRATCH_BYTES);
+  if ((st = check_device()) != H3_OK) return st;
+  void* ws = nullptr;
+  if ((st = hip_ok(h3::noalloc_scratch(&ws), "scratch array address")) != H3_OK) return st;
+  return h3_dit_forward(dims, x, tag, positions, mod_table, weights, n_blocks, n_rows, ws,
+                        H3_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 h3_status h3_rope_table(const h3_dims* dims, const float* positions, int64_t n_rows, float* cs,
                         void* stream) {
   g_err.clear();

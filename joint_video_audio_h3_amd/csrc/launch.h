@@ -87,6 +87,9 @@ hipError_t launch_euler2(float* z, const float* v1, const float* v0, float a, fl
 
 // device address of the tag check's counter on the current device
 hipError_t bad_tags_counter(unsigned int** ptr);
+// device address of the library's static scratch array (H3_NOALLOC_SCRATCH_BYTES)
+// on the current device, looked up once per device
+hipError_t noalloc_scratch(void** ptr);
 // *bad += number of tag[0..n) outside [0, n_tags)
 hipError_t launch_count_bad_tags(const int32_t* tag, int64_t n, int n_tags, unsigned int* bad, hipStream_t s);
 

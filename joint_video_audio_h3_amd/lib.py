@@ -66,6 +66,8 @@ _SIGS = {
                                      ctypes.POINTER(H3BlockWeights), c_i64, c_vp, c_sz, c_vp]),
     "h3_dit_forward": (c_i32, [ctypes.POINTER(H3Dims), c_vp, c_vp, c_vp, c_vp,
                                ctypes.POINTER(H3BlockWeights), c_i32, c_i64, c_vp, c_sz, c_vp]),
+    "h3_dit_forward_noalloc": (c_i32, [ctypes.POINTER(H3Dims), c_vp, c_vp, c_vp, c_vp,
+                                       ctypes.POINTER(H3BlockWeights), c_i32, c_i64, c_vp]),
     "h3_rope_table": (c_i32, [ctypes.POINTER(H3Dims), c_vp, c_i64, c_vp, c_vp]),
     "h3_adaln_modulate": (c_i32, [ctypes.POINTER(H3Dims), c_vp, c_vp, c_vp, c_i32, c_i64, c_vp, c_vp]),
     "h3_qkv_rope": (c_i32, [ctypes.POINTER(H3Dims), c_vp, ctypes.POINTER(H3BlockWeights), c_vp,
@@ -183,6 +185,15 @@ def dit_forward(dims, x, tag, positions, mod_table, blocks: Sequence[Dict], work
     _check(load().h3_dit_forward(ctypes.byref(d), x.data_ptr(), tag.data_ptr(), positions.data_ptr(),
                                  mod_table.data_ptr(), arr, len(blocks), x.shape[0],
                                  workspace.data_ptr(), workspace.numel(), _stream(stream)))
+
+
+def dit_forward_noalloc(dims, x, tag, positions, mod_table, blocks: Sequence[Dict], stream=None):
+    """h3_dit_forward on the library's static scratch array (no workspace argument)."""
+    d = make_dims(dims)
+    arr = (H3BlockWeights * len(blocks))(*[make_weights(b) for b in blocks])
+    _check(load().h3_dit_forward_noalloc(ctypes.byref(d), x.data_ptr(), tag.data_ptr(), positions.data_ptr(),
+                                         mod_table.data_ptr(), arr, len(blocks), x.shape[0],
+                                         _stream(stream)))
 
 
 def rope_table(dims, positions, n_rows, cs, stream=None):

@@ -243,3 +243,14 @@ def test_denoise_workspace_adds_two_velocity_slots_per_modality(L):
     sg_bad = lib.make_segments(-1, 0, 0, 10)
     assert L.h3_denoise_workspace_size(ctypes.byref(lib.make_dims(d)), ctypes.byref(lib.make_io_dims(io)),
                                        ctypes.byref(sg_bad)) == 0
+
+
+def test_noalloc_forward_refuses_rows_beyond_its_scratch_array(L):
+    """The no-allocation forward checks on the host that the workspace fits its
+    static 128 MiB array: 1,792 rows at H3 width do, 1,793 (2,048 padded) do not."""
+    d = synth.H3_DIMS
+    assert lib.workspace_size(d, 1792) <= (128 << 20) < lib.workspace_size(d, 1793)
+    w = (lib.H3BlockWeights * 1)()
+    st = L.h3_dit_forward_noalloc(ctypes.byref(lib.make_dims(d)), FAKE, FAKE, FAKE, FAKE, w, 1, 1793, None)
+    assert st == lib.H3_ERR_WORKSPACE
+    assert "static scratch" in lib.last_error()
