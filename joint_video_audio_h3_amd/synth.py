@@ -33,7 +33,9 @@ Readings (stated once, used everywhere):
   ~ N(0, 0.1) (variance 0.1) bf16.
 * INT8 weight-only: symmetric, groups of 32 along K, one bf16 scale per group:
   s = bf16(max|w_g| / 127) (s = 0 gives q = 0), q = clamp(round-half-even(w/s),
-  -127, 127).  W8A8 weights: the same with one group per output row.
+  -127, 127).  W8A8 weights: the same with groups of dims.w8a8_group along K
+  and the scales stored group-major [K / group][out] (per output row for FC2
+  in its per-row form).
 """
 from __future__ import annotations
 
@@ -69,6 +71,8 @@ class Dims:
     ln_eps: float = 1e-6
     qk_eps: float = 1e-6
     wfmt: int = WFMT_BF16
+    w8a8_group: int = 0          # W8A8: K elements per scale group (64, 256, 448 or 896)
+    w8a8_row_fc2: int = 0        # W8A8: FC2 with one scale per row instead of per group
 
     @property
     def inner(self) -> int:
@@ -77,6 +81,10 @@ class Dims:
 
 H3_DIMS = Dims(hidden=5376, heads=56, head_dim=128, ffn=14336)
 TINY_DIMS = Dims(hidden=256, heads=4, head_dim=96, ffn=768, rope_split=(24, 36, 36))
+# group-scaled W8A8 trunk, group 896 as in the pages' example (the tiny model's
+# widths 256 / 384 / 768 take only the group of 64)
+H3_W8A8_DIMS = dataclasses.replace(H3_DIMS, wfmt=WFMT_W8A8, w8a8_group=896)
+TINY_W8A8_DIMS = dataclasses.replace(TINY_DIMS, wfmt=WFMT_W8A8, w8a8_group=64)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -116,12 +124,9 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("h3_50blk_n49840", H3_DIMS, 50, 256, 1024, 200, (31, 30, 52)),
         Workload("h3_1blk_n1192_int8",
                  dataclasses.replace(H3_DIMS, wfmt=WFMT_INT8_G32), 1, 128, 0, 40, (1, 32, 32)),
-        Workload("h3_1blk_n1192_w8a8",
-                 dataclasses.replace(H3_DIMS, wfmt=WFMT_W8A8), 1, 128, 0, 40, (1, 32, 32)),
-        Workload("h3_50blk_n6437_w8a8",
-                 dataclasses.replace(H3_DIMS, wfmt=WFMT_W8A8), 50, 256, 0, 37, (6, 32, 32)),
-        Workload("h3_50blk_n49840_w8a8",
-                 dataclasses.replace(H3_DIMS, wfmt=WFMT_W8A8), 50, 256, 1024, 200, (31, 30, 52)),
+        Workload("h3_1blk_n1192_w8a8", H3_W8A8_DIMS, 1, 128, 0, 40, (1, 32, 32)),
+        Workload("h3_50blk_n6437_w8a8", H3_W8A8_DIMS, 50, 256, 0, 37, (6, 32, 32)),
+        Workload("h3_50blk_n49840_w8a8", H3_W8A8_DIMS, 50, 256, 1024, 200, (31, 30, 52)),
     ]
 }
 
@@ -142,18 +147,34 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
 
 
 def quantize_int8_rows(w_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """Symmetric INT8 codes with one bf16 scale per output row (the W8A8 weights).
+    """Symmetric INT8 codes with one bf16 scale per output row (W8A8 FC2 in its
+    per-row form).
 
     ``w_bits`` bf16 [out, in]; returns (q int8 [out, in], s bf16 bits [out]):
     s = bf16(max|w_row| / 127), q = clamp(round-half-even(w / s), -127, 127).
     """
-    w = bf16_bits_to_f32(w_bits).astype(np.float64)
-    amax = np.abs(w).max(axis=1)
+    q, s = quantize_int8_groups(w_bits, w_bits.shape[1])
+    return q, s[0]
+
+
+def quantize_int8_groups(w_bits: np.ndarray, group: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Symmetric INT8 codes with one bf16 scale per output row and group of
+    ``group`` consecutive K elements (the group-scaled W8A8 weights).
+
+    ``w_bits`` bf16 [out, in]; returns (q int8 [out, in], s bf16 bits
+    [in / group, out]), group-major: s[g, o] = bf16(max|w[o, g]| / 127),
+    q = clamp(round-half-even(w / s), -127, 127) (s = 0 gives q = 0).
+    """
+    out_f, in_f = w_bits.shape
+    assert in_f % group == 0
+    w = bf16_bits_to_f32(w_bits).astype(np.float64).reshape(out_f, in_f // group, group)
+    amax = np.abs(w).max(axis=2)
     s_bits = f32_to_bf16_bits((amax / 127.0).astype(np.float32))
-    s = bf16_bits_to_f32(s_bits).astype(np.float64)[:, None]
+    s = bf16_bits_to_f32(s_bits).astype(np.float64)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.where(s > 0, np.rint(w / np.where(s > 0, s, 1.0)), 0.0)
-    return np.clip(q, -127, 127).astype(np.int8), s_bits
+    q = np.clip(q, -127, 127).astype(np.int8).reshape(out_f, in_f)
+    return q, np.ascontiguousarray(s_bits.T)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -277,8 +298,10 @@ def make_block_weights(dims: Dims, block: int, seed: int = 0,
     """Host weights of one block in PyTorch Linear layout W[out][in].
 
     bf16 layers: ``w_*`` are uint16 bit patterns.  INT8 layers (dims.wfmt == 1):
-    ``w_*`` are int8 codes and ``s_*`` are bf16 scale bits [out, in/32]; both
-    are derived from the same seeded bf16 draw the bf16 build would use.
+    ``w_*`` are int8 codes and ``s_*`` are bf16 scale bits [out, in/32]; W8A8
+    layers (dims.wfmt == 2): int8 codes and bf16 scale bits [in/G, out] (G =
+    dims.w8a8_group; [out] for FC2 when dims.w8a8_row_fc2).  All are derived
+    from the same seeded bf16 draw the bf16 build would use.
     Rows of ``w_qkv`` are interleaved per head: [h0: q, k, v][h1: q, k, v]...
     and ``w_fc1`` stacks [gate; value].
     """
@@ -292,7 +315,9 @@ def make_block_weights(dims: Dims, block: int, seed: int = 0,
         if dims.wfmt == WFMT_INT8_G32:
             return quantize_int8_g32(bits)
         if dims.wfmt == WFMT_W8A8:
-            return quantize_int8_rows(bits)
+            if k == "fc2" and dims.w8a8_row_fc2:
+                return quantize_int8_rows(bits)
+            return quantize_int8_groups(bits, dims.w8a8_group)
         return bits, None
 
     # independent streams per tensor: drawing them concurrently changes no value
@@ -456,7 +481,9 @@ def make_device_weights(dims: Dims, n_blocks: int, seed: int = 0, device: str = 
             if dims.wfmt == WFMT_INT8_G32:
                 wb["w_" + k], wb["s_" + k] = _quantize_int8_g32_torch(w.to(torch.bfloat16))
             elif dims.wfmt == WFMT_W8A8:
-                wb["w_" + k], wb["s_" + k] = _quantize_int8_rows_torch(w.to(torch.bfloat16))
+                grp = i if (k == "fc2" and dims.w8a8_row_fc2) else dims.w8a8_group
+                wq, ws = _quantize_int8_groups_torch(w.to(torch.bfloat16), grp)
+                wb["w_" + k], wb["s_" + k] = wq, (ws[0].contiguous() if grp == i else ws)
             else:
                 wb["w_" + k], wb["s_" + k] = w.to(torch.bfloat16), None
             del w
@@ -480,12 +507,14 @@ def _quantize_int8_g32_torch(w_bf16):
     return q.clamp_(-127, 127).to(torch.int8).view(o, i).contiguous(), s.contiguous()
 
 
-def _quantize_int8_rows_torch(w_bf16):
+def _quantize_int8_groups_torch(w_bf16, group):
+    """Device twin of quantize_int8_groups: (codes [o, i], bf16 scales [i/group, o])."""
     import torch
 
-    w = w_bf16.float()
-    s = (w.abs().amax(dim=1) / 127.0).to(torch.bfloat16)
+    o, i = w_bf16.shape
+    w = w_bf16.float().view(o, i // group, group)
+    s = (w.abs().amax(dim=2) / 127.0).to(torch.bfloat16)
     sf = s.float().unsqueeze(-1)
     q = torch.where(sf > 0, torch.round(w / torch.where(sf > 0, sf, torch.ones_like(sf))),
                     torch.zeros_like(w))
-    return q.clamp_(-127, 127).to(torch.int8).contiguous(), s.contiguous()
+    return q.clamp_(-127, 127).to(torch.int8).view(o, i).contiguous(), s.t().contiguous()

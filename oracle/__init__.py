@@ -11,7 +11,7 @@ from .h3_block import (  # noqa: F401
     rope_angles, round_to_bf16, silu, swiglu, weight,
 )
 from .h3_io import SEGMENTS, embed_inputs, final_heads, segment_rows, velocity_forward  # noqa: F401
-from .h3_w8a8 import linear_w8a8, quantize_rows  # noqa: F401
+from .h3_w8a8 import ACCEPTED_GROUPS, linear_w8a8, linear_w8a8_grouped, quantize_groups, quantize_rows  # noqa: F401
 from .h3_sparse import attention_sparse, selected_keys  # noqa: F401
 from .h3_sampler import (  # noqa: F401
     base_grid, denoise, euler, extrapolate, fresh_passes, schedule, shift_sigmas,

@@ -41,7 +41,8 @@ theta^(-2j/d_axis); softmax scale 1/sqrt(d); all biases optional (absent = 0),
 QK gains optional (absent = 1).  INT8 weight-only layers use
 W = bf16(q * s) with s one bf16 scale per 32 consecutive K elements (the GPU
 feeds the same dequantised bf16 values to its matrix cores).  W8A8 layers
-(int8 weights and activations, one scale per row) follow ``h3_w8a8``.
+(int8 weights and activations with one scale per group of K elements) follow
+``h3_w8a8``.
 """
 from __future__ import annotations
 
@@ -94,17 +95,23 @@ def bias(w, name: str, n_out: int) -> np.ndarray:
     return np.zeros(n_out) if b is None else bf16_to_f64(b)
 
 
-WFMT_W8A8 = 2   # int8 weights with one bf16 scale per output row, activations quantized per row
+WFMT_W8A8 = 2   # group-scaled int8 weights and activations (h3_w8a8)
 
 
 def linear(act: np.ndarray, w, name: str, n_out: int, dims) -> np.ndarray:
     """Trunk linear ``name``: act W^T + b, or its W8A8 form (h3_w8a8) when the
-    weights are W8A8: the activation, rounded to bf16 as the bf16 path stores
-    it, is quantized per row and multiplied in integers."""
+    weights are W8A8: the activation, a bf16 tensor in the model, is quantized
+    per group of dims.w8a8_group K elements (FC2 per row when
+    dims.w8a8_row_fc2) and multiplied in integers."""
     if getattr(dims, "wfmt", 0) == WFMT_W8A8:
-        from .h3_w8a8 import linear_w8a8, quantize_rows
-        q, s = quantize_rows(round_to_bf16(act))
-        return linear_w8a8(q, s, w["w_" + name], w["s_" + name], bias(w, name, n_out))
+        from .h3_w8a8 import linear_w8a8, linear_w8a8_grouped, quantize_groups, quantize_rows
+        a = round_to_bf16(act)
+        if name == "fc2" and getattr(dims, "w8a8_row_fc2", 0):
+            q, s = quantize_rows(a)
+            return linear_w8a8(q, s, w["w_" + name], w["s_" + name], bias(w, name, n_out))
+        G = dims.w8a8_group
+        q, s = quantize_groups(a, G)
+        return linear_w8a8_grouped(q, s, w["w_" + name], w["s_" + name], bias(w, name, n_out), G)
     return act @ weight(w, name).T + bias(w, name, n_out)
 
 
