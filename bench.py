@@ -111,30 +111,35 @@ def step_breakdown_w8a8(lib, dims, wl_rows, table, block, reps, torch):
     x, tags, pos = wl_rows
     n = x.shape[0]
     D, Di, F, H, d = dims.hidden, dims.inner, dims.ffn, dims.heads, dims.head_dim
+    G = dims.w8a8_group
+    Gf = F if dims.w8a8_row_fc2 else G
     np_ = lib.padded_rows(n)
     dev = x.device
     cs = torch.empty(np_, d // 2, 2, dtype=torch.float32, device=dev)
-    hq = torch.empty(lib.quantized_bytes(n, D), dtype=torch.uint8, device=dev)
+    h = torch.empty(n, D, dtype=torch.int16, device=dev)
+    hq = torch.empty(lib.quantized_bytes(n, D, G), dtype=torch.uint8, device=dev)
     q = torch.empty(H, np_, d, dtype=torch.int16, device=dev)
     k = torch.empty_like(q)
     vt = torch.empty(H, d, np_, dtype=torch.int16, device=dev)
     o = torch.empty(n, Di, dtype=torch.int16, device=dev)
-    oq = torch.empty(lib.quantized_bytes(n, Di), dtype=torch.uint8, device=dev)
+    oq = torch.empty(lib.quantized_bytes(n, Di, G), dtype=torch.uint8, device=dev)
     a = torch.empty(n, F, dtype=torch.int16, device=dev)
-    aq = torch.empty(lib.quantized_bytes(n, F), dtype=torch.uint8, device=dev)
+    aq = torch.empty(lib.quantized_bytes(n, F, Gf), dtype=torch.uint8, device=dev)
     xs = x.clone()
     t0 = table[0]
     lib.rope_table(dims, pos, n, cs)
     w = perf_model.block_work(n, D, Di, F)
     I8 = perf_model.PEAK_INT8_TOPS
+    qbytes = lambda K, g: 2.0 * n * K + n * K + 4.0 * n * K / g  # noqa: E731
     steps = {
-        "adaln_quant": (lambda: lib.adaln_modulate(dims, xs, tags, t0, 0, hq), None, 4.0 * n * D + n * D, None),
+        "adaln": (lambda: lib.adaln_modulate(dims, xs, tags, t0, 0, h), None, 6.0 * n * D, None),
+        "quant_h": (lambda: lib.quantize_groups(h, G, hq), None, qbytes(D, G), None),
         "qkv_rope": (lambda: lib.qkv_rope(dims, hq, block, cs, n, q, k, vt), w.qkv_flop, None, I8),
         "attention": (lambda: lib.attention(dims, q, k, vt, n, o), w.attn_flop, None, PEAK),
-        "quant_o": (lambda: lib.quantize_rows(o, oq), None, 3.0 * n * Di, None),
+        "quant_o": (lambda: lib.quantize_groups(o, G, oq), None, qbytes(Di, G), None),
         "out_proj_resid": (lambda: lib.out_proj_residual(dims, oq, block, t0, tags, xs), w.out_flop, None, I8),
         "fc1_swiglu": (lambda: lib.mlp_fc1_swiglu(dims, hq, block, a), w.fc1_flop, None, I8),
-        "quant_a": (lambda: lib.quantize_rows(a, aq), None, 3.0 * n * F, None),
+        "quant_a": (lambda: lib.quantize_groups(a, Gf, aq), None, qbytes(F, Gf), None),
         "fc2_resid": (lambda: lib.mlp_fc2_residual(dims, aq, block, t0, tags, xs), w.fc2_flop, None, I8),
     }
     out = {}
@@ -538,8 +543,8 @@ def main():
         log(f"sparse forward: {secs * 1e3:.1f} ms")
         del ws, x, offd, idxd
     if args.w8a8:
-        # the same forwards with the W8A8 trunk (int8 weights and activations,
-        # per-row scales) on the int8 matrix cores
+        # the same forwards with the group-scaled W8A8 trunk (int8 weights and
+        # activations, one scale per 896 K elements) on the int8 matrix cores
         del table, blocks
         torch.cuda.empty_cache()
         result["w8a8"] = {}

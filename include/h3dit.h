@@ -71,14 +71,19 @@ typedef enum h3_wfmt {
   H3_W_BF16 = 0,     /* weights bf16 [out][in]                                    */
   H3_W_INT8_G32 = 1, /* weights int8 [out][in] + bf16 scales [out][in/32]:
                         W = bf16(q * s), one scale per 32 consecutive K elements  */
-  H3_W_W8A8 = 2      /* W8A8: weights int8 [out][in] + one bf16 scale per output
-                        row [out]; each linear's bf16 input is quantized per row
-                        (amax = max|a|, q = clamp(rint(a * (127 / amax)), +-127),
-                        scale amax / 127, all in float32) and the product is
-                        accumulated in int32 on the int8 matrix cores:
-                        y = s_a[r] * s_w[c] * sum_k q_a q_w + b.  (mlx-h3 README,
-                        "Generate": the 200 trunk linears as group-scaled W8A8;
-                        here the group is the whole K.)                        */
+  H3_W_W8A8 = 2      /* group-scaled W8A8 (mlx-h3 README, "Generate": the 200
+                        trunk linears as group-scaled W8A8, groups of 64, 256,
+                        448 or 896 along K): weights int8 [out][in] + bf16
+                        scales [in/G][out] (group-major), G = dims->w8a8_group;
+                        each linear's bf16 input is quantized per row and group
+                        (amax = max|a| over the group, q = clamp(rint(a *
+                        (127 / amax)), +-127), scale amax / 127, in float32) and
+                        y = b + sum_g s_a[r][g] s_w[g][c] sum_{k in g} q_a q_w,
+                        each group's sum in int32 on the int8 matrix cores.
+                        With dims->w8a8_row_fc2 = 1, FC2 alone takes one scale
+                        per activation row and per weight output row (scales
+                        [out]; H3-metal digest, "4. Choose a speed/quality
+                        preset": the per-row FC2 option).                      */
 } h3_wfmt;
 
 typedef struct h3_dims {
@@ -92,6 +97,10 @@ typedef struct h3_dims {
   float ln_eps;          /* AdaLN layer-norm epsilon (1e-6)                    */
   float qk_eps;          /* QK RMSNorm epsilon (1e-6)                          */
   int32_t wfmt;          /* h3_wfmt of the four linear layers                  */
+  int32_t w8a8_group;    /* H3_W_W8A8: K elements per scale group, one of 64,
+                            256, 448, 896, dividing hidden, heads*head_dim and
+                            ffn (ffn not needed with w8a8_row_fc2); else ignored */
+  int32_t w8a8_row_fc2;  /* H3_W_W8A8: 1 = FC2 with per-row scales, 0 = grouped */
 } h3_dims;
 
 /* Device pointers of one block's weights.  w_qkv [3*H*d][D] rows interleaved
@@ -179,15 +188,18 @@ H3DIT_API h3_status h3_dit_forward_sparse(const h3_dims* dims, float* x_packed, 
 H3DIT_API const char* h3_last_error(void);
 
 
-/* W8A8 activation buffer: int8 codes [n_rows][width], then fp32 row scales
- * [n_rows] at byte offset roundup(n_rows * width, 256).  Bytes it needs (pure;
- * 0 for non-positive sizes). */
-H3DIT_API size_t h3_quantized_bytes(int64_t n_rows, int32_t width);
+/* W8A8 activation buffer of width K and scale group G (G = K: one scale per
+ * row): int8 codes [n_rows][K], then at byte offset roundup(n_rows * K, 256)
+ * fp32 scales [K/G][n_pad] (group-major, n_pad = h3_padded_rows(n_rows), the
+ * rows past n_rows holding 0).  Bytes it needs (pure; 0 for invalid sizes). */
+H3DIT_API size_t h3_quantized_bytes(int64_t n_rows, int32_t width, int32_t group);
 
-/* Per-row int8 quantization (the H3_W_W8A8 rule) of in bf16 [n_rows][width]
- * into the activation buffer out.  width % 8 == 0, width <= 16384. */
-H3DIT_API h3_status h3_quantize_rows(const uint16_t* in, int64_t n_rows, int32_t width, void* out,
-                                     void* stream);
+/* Symmetric int8 quantization (the H3_W_W8A8 rule) of in bf16 [n_rows][width]
+ * per row and group of `group` consecutive elements (64, 256, 448, 896, or
+ * group == width for one scale per row) into the activation buffer out.
+ * width % 8 == 0, width % group == 0, width <= 16384. */
+H3DIT_API h3_status h3_quantize_groups(const uint16_t* in, int64_t n_rows, int32_t width,
+                                       int32_t group, void* out, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Around the block stack: inputs -> packed stream -> velocity               */
@@ -280,8 +292,10 @@ H3DIT_API h3_status h3_velocity_forward(const h3_dims* dims, const h3_io_dims* i
 /* Step entry points: each runs one step of the block on caller buffers.     */
 /* They are the kernels h3_dit_block_forward launches, exposed for parity   */
 /* tests and per-step timing.  With dims->wfmt == H3_W_W8A8 the bf16         */
-/* activations below (h, h2, o, a) are W8A8 activation buffers instead       */
-/* (h3_quantized_bytes), written by h3_adaln_modulate / h3_quantize_rows.   */
+/* inputs of the four linears (h, h2, o, a) are W8A8 activation buffers     */
+/* instead (h3_quantized_bytes with the linear's group: w8a8_group, or K    */
+/* for FC2 with w8a8_row_fc2), made by h3_quantize_groups from the bf16     */
+/* tensors (h3_adaln_modulate always writes bf16).                          */
 /* ------------------------------------------------------------------------ */
 
 /* Rotary table: cs fp32 [n_pad][d/2][2] = (cos, sin) of the angle of every

@@ -25,6 +25,10 @@
 // reads of the next 16-wide k step are scheduled behind the current step's
 // first MFMA.
 //
+// W8A8, group-scaled (gemm_w8a8g_kernel): int8 MFMAs into int32 accumulators
+// per group of K elements, folded into fp32 with the group's activation and
+// weight scales; four wavefronts of 64 x 128 tiles.
+//
 // INT8 weights (gemm_w8_kernel): eight wavefronts of 64 x 128 tiles; A streams
 // in by DMA, int8 codes go through registers, where they are dequantised to
 // bf16(q * s) (one bf16 scale per 32 K elements) on their way into a
@@ -916,6 +920,224 @@ __global__ __launch_bounds__(512) void gemm_w8_kernel(GemmArgs p) {
   }
 }
 
+// ============================================================ W8A8, group-scaled
+// Group-scaled W8A8 (mlx-h3 README, "Generate": the trunk linears as
+// group-scaled W8A8, one scale per group of G = 64, 256, 448 or 896 K elements
+// on both operands):
+//   y[r][c] = sum_g s_a[g][r] * s_w[g][c] * sum_{k in g} q_a[r][k] * q_w[c][k]
+// Each group's integer sum is exact in int32 (|sum| <= 896 * 127^2 < 2^24, so
+// also exact as fp32), then folded into fp32 accumulators at the group's end.
+// Both accumulator sets live through the K loop, so the wave tile is 64 x 128
+// (128 int32 + 128 fp32 registers): four wavefronts stacked 4 x 1 on a 256 x
+// 128 block tile (256 x 96 for the 96-wide head sections of the small model),
+// each wave owning whole head sections as the QKV epilogue needs.
+// v_mfma_i32_32x32x32_i8 takes 32 K per step, so a 128-byte stage row holds 4
+// steps and every group ends on an even step.  Stages (A 32 KB + B 16 KB) move
+// by DMA into a 3-stage ring with the bf16 kernel's swizzle; with each stage
+// come the scales of the (at most two) groups it touches: s_a for the 256 rows
+// (1 KB) and s_w for the tile's columns, both contiguous in their group-major
+// layouts.  The first step of a group starts its int32 accumulators from zero
+// (the MFMA's C operand), the last one is followed by the fold
+//   f[r][c] += float(i[r][c]) * (s_a[r] * s_w[c]).
+template <int EPI, int SEC, int BN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w8a8g_kernel(GemmArgs p) {
+  constexpr int BM = 256, WM = 4, WN = 1;
+  constexpr int TM = BM / WM, TN = BN / WN;       // 64 x BN
+  constexpr int FM = TM / 32, FN = TN / 32;       // 2 x (4 or 3)
+  constexpr int SK = 128;                         // K (bytes) per stage row
+  constexpr int ABYTES = BM * SK, BBYTES = BN * SK;
+  constexpr int STAGE = ABYTES + BBYTES;
+  constexpr int NST = 3;                          // ring of stages
+  constexpr int SCL = 4096;                       // per stage: s_a of 2 groups, then s_w of 2 groups
+  constexpr int NA = BM / 32, NB = BN / 32;       // 1 KB (8-row) loads per wave per stage
+  constexpr int PER = NA + NB + 1;                // DMA instructions per wave per stage
+  static_assert(EPI != EPI_QKV || TN == SEC, "QKV wave tile must be one head section");
+  static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU needs paired gate/value tiles");
+  static_assert(NST * STAGE + NST * SCL <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) char ring[NST * STAGE + NST * SCL];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave;                            // WN == 1
+  const TileCoord tc = tile_coord<EPI, BM, BN>(p);
+  const int m0 = tc.tm * BM, n0 = tc.tn * BN;
+  const int K = p.K, G = p.group;
+  const int ng = K / G, GK = G / 32;              // groups; MFMA steps per group
+  const int KT = K / SK;
+  const uint32_t rowb = (uint32_t)K;
+  const uint32_t ring0 = lds_addr(ring);
+  const uint32_t scl0 = ring0 + NST * STAGE;
+
+  // A / B loads: load s of a wave covers rows 8*(wave + 4s) .. +7; lane l fills
+  // row 8*(wave + 4s) + l/8, position l%8, which holds global chunk (l%8) ^ f(row)
+  const char* baseA = reinterpret_cast<const char*>(p.A) + (size_t)m0 * rowb;
+  const int b0 = weight_row_base<EPI, BN>(tc.tn);
+  const char* baseB = reinterpret_cast<const char*>(p.B) + (size_t)b0 * rowb;
+  uint32_t voA[NA], voB[NB];
+#pragma unroll
+  for (int s = 0; s < NA; ++s) {
+    const int r = 8 * (wave + 4 * s) + lane / 8;
+    voA[s] = (uint32_t)(min(m0 + r, p.M - 1) - m0) * rowb + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+  }
+#pragma unroll
+  for (int s = 0; s < NB; ++s) {
+    const int r = 8 * (wave + 4 * s) + lane / 8;
+    voB[s] = (uint32_t)(weight_row<EPI, BN, TN>(p, tc.tn, r) - b0) * rowb + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+  }
+  // scale loads, one per wave per stage: waves 0 / 1 bring s_a of the stage's
+  // first / last group (256 rows, 16 B per lane), waves 2 / 3 s_w of the same
+  // groups (BN columns, 8 per lane; lanes past them repeat lane 0's piece)
+  const bool sa_wave = wave < 2;
+  uint32_t vo_s;
+  if (sa_wave) {
+    vo_s = (uint32_t)(m0 + 4 * lane) * 4;
+  } else {
+    const int c = lane < BN / 8 ? 8 * lane : 0;
+    vo_s = (uint32_t)weight_row<EPI, BN, TN>(p, tc.tn, c) * 2;
+  }
+  const int nw = EPI == EPI_SWIGLU ? 2 * p.ffn : p.n_out;   // weight rows (s_w row length)
+  auto group_lo = [&](int kt) { return (kt * SK) / G; };
+  auto group_hi = [&](int kt) { return min((kt * SK + SK - 1) / G, ng - 1); };
+
+  auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
+    const uint32_t so = (uint32_t)slot * STAGE;
+    const char* sa_ = baseA + (size_t)kt * SK;
+    const char* sb_ = baseB + (size_t)kt * SK;
+    const uint32_t mw = __builtin_amdgcn_readfirstlane(ring0 + so + wave * 1024);
+#pragma unroll
+    for (int s = 0; s < NA; ++s) dma16s(voA[s], sa_, mw + s * 4096);
+#pragma unroll
+    for (int s = 0; s < NB; ++s) dma16s(voB[s], sb_, mw + ABYTES + s * 4096);
+    const int g = (wave & 1) ? group_hi(kt) : group_lo(kt);
+    const uintptr_t sb = sa_wave ? reinterpret_cast<uintptr_t>(p.sa + (size_t)g * p.sa_ld)
+                                 : reinterpret_cast<uintptr_t>(p.Bs + (size_t)g * nw);
+    // wave-uniform (the wave index is), so it can live in SGPRs
+    // (readfirstlane returns int: each half goes through uint32_t, or the low
+    // half would sign-extend into the high one)
+    const uint64_t sbu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32)) << 32) |
+                         (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb);
+    dma16s(vo_s, reinterpret_cast<const char*>(sbu),
+           __builtin_amdgcn_readfirstlane(scl0 + slot * SCL + (sa_wave ? 0 : 2048) + (wave & 1) * 1024));
+  };
+
+  // fragment reads: row lane%32 of each 32-row tile, chunk 2*kk + lane/32 at
+  // its swizzled position; per-lane bases for the two row parities and four
+  // steps of a stage, plus the stage's slot offset
+  const int fr = lane & 31, hl = lane >> 5;
+  uint32_t rA[2][4], rB[2][4];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      rA[par][kk] = ring0 + (wm * TM + fr) * SK + (((2 * kk + hl) ^ swz(fr + 32 * par)) * 16);
+      rB[par][kk] = ring0 + ABYTES + fr * SK + (((2 * kk + hl) ^ swz(fr + 32 * par)) * 16);
+    }
+  auto read_frags = [&](uint32_t so, int kk, i32x4 (&fa)[FM], i32x4 (&fb)[FN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[i] = __builtin_bit_cast(i32x4, lds_read16(rA[i & 1][kk] + so + i * 32 * SK));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[j] = __builtin_bit_cast(i32x4, lds_read16(rB[j & 1][kk] + so + j * 32 * SK));
+  };
+
+  i32x16 iacc[FM][FN];
+  f32x16 facc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) facc[i][j] = f32x16{};
+  const i32x16 zero = {};
+  auto mfmas = [&](const i32x4 (&fa)[FM], const i32x4 (&fb)[FN], bool first) __attribute__((always_inline)) {
+    if (first) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) iacc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], zero, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          iacc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], iacc[i][j], 0, 0, 0);
+    }
+  };
+  // f += float(i) * s_a[row] * s_w[col] with the group's scales from the
+  // stage's scale slot (sub = 0: the stage's first group, 1: its last)
+  auto fold = [&](int slot, int sub) __attribute__((always_inline)) {
+    const float* sa_l = reinterpret_cast<const float*>(ring + NST * STAGE + slot * SCL + sub * 1024);
+    const uint16_t* sw_l = reinterpret_cast<const uint16_t*>(ring + NST * STAGE + slot * SCL + 2048 + sub * 1024);
+    float sw[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) sw[j] = bf2f(sw_l[j * 32 + fr]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      float sr[16];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float4 s4 = *reinterpret_cast<const float4*>(sa_l + wm * TM + i * 32 + 8 * t + 4 * hl);
+        sr[4 * t] = s4.x;
+        sr[4 * t + 1] = s4.y;
+        sr[4 * t + 2] = s4.z;
+        sr[4 * t + 3] = s4.w;
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          facc[i][j][v] = __builtin_fmaf((float)iacc[i][j][v] * sw[j], sr[v], facc[i][j][v]);
+    }
+  };
+
+  issue(0, 0);
+  if (KT > 1) issue(1, 1);
+  i32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  int ks = 0;   // global MFMA step
+  for (int kt = 0; kt < KT; ++kt) {
+    const int slot = kt % NST;
+    const uint32_t so = (uint32_t)slot * STAGE;
+    if (kt + 1 < KT) {
+      wait_vmcnt<PER>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0): the previous stage fully read
+    __builtin_amdgcn_s_barrier();
+    if (kt + 2 < KT) issue(kt + 2, (kt + 2) % NST);
+    const int glo = group_lo(kt);
+    read_frags(so, 0, fa0, fb0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      i32x4 (&fa)[FM] = (kk & 1) ? fa1 : fa0;
+      i32x4 (&fb)[FN] = (kk & 1) ? fb1 : fb0;
+      if (kk < 3) {
+        if (kk & 1) read_frags(so, kk + 1, fa0, fb0);
+        else read_frags(so, kk + 1, fa1, fb1);
+      }
+      mfmas(fa, fb, ks % GK == 0);
+      if ((ks + 1) % GK == 0) fold(slot, ks / GK == glo ? 0 : 1);
+      ++ks;
+    }
+  }
+  __syncthreads();
+  if constexpr (EPI == EPI_RESID) {
+    int* s_tag = reinterpret_cast<int*>(ring + 4 * 32 * RSTRIDE * sizeof(float));
+    s_tag[tid] = p.tag[min(m0 + tid, p.M - 1)];
+    __syncthreads();
+    resid_epilogue_lds<true, TM, TN, FM, FN>(p, facc, m0 + wm * TM, n0, lane,
+                                             reinterpret_cast<float*>(ring) + wave * 32 * RSTRIDE, s_tag + wm * TM);
+  } else if constexpr (EPI == EPI_QKV && SEC == 128) {
+    const int sec = n0 / SEC;
+    if (sec < 3 * p.heads)
+      qkv_epilogue_lds<TM, FM, FN>(p, facc, m0 + wm * TM, sec, lane,
+                                   reinterpret_cast<float*>(ring) + wave * 32 * QSTRIDE);
+  } else if constexpr (EPI == EPI_SWIGLU && TN == 128) {
+    swiglu_epilogue_lds<TM, TN, FM, FN>(p, facc, m0 + wm * TM, tc.tn * (BN / 2), lane,
+                                        reinterpret_cast<float*>(ring) + wave * 32 * SSTRIDE);
+  } else {
+    epilogue<BM, BN, WM, WN, EPI, SEC>(p, facc, m0, n0, tc.tn, wm, 0, lane, nullptr);
+  }
+}
+
 // ============================================================ dispatch
 template <int BM, int BN>
 static dim3 grid_for(int epi, const GemmArgs& a) {
@@ -927,6 +1149,12 @@ static dim3 grid_for(int epi, const GemmArgs& a) {
 template <int EPI, int SEC, int BN, bool I8 = false>
 static hipError_t run_direct(const GemmArgs& a, hipStream_t s) {
   gemm_direct_kernel<EPI, SEC, BN, I8><<<grid_for<256, BN>(EPI, a), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int EPI, int SEC, int BN>
+static hipError_t run_w8a8g(const GemmArgs& a, hipStream_t s) {
+  gemm_w8a8g_kernel<EPI, SEC, BN><<<grid_for<256, BN>(EPI, a), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -969,7 +1197,18 @@ static bool resid_prefers_192(const GemmArgs& a) { return resid_tile_width(a, fa
 hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
   if (a.K % 64 != 0) return hipErrorInvalidValue;
   if (wfmt != 0 && a.K % 128 != 0) return hipErrorInvalidValue;   // INT8: 128-element stages
-  if (wfmt == 2) {   // W8A8: int8 activations and weights, per-row scales
+  if (wfmt == 2 && a.group > 0) {   // W8A8, one scale per group of K elements on both operands
+    if (a.K % a.group != 0 || a.group % 64 != 0 || a.n_out % 32 != 0) return hipErrorInvalidValue;
+    switch (epi) {
+      case EPI_RESID: return run_w8a8g<EPI_RESID, 0, 128>(a, s);
+      case EPI_SWIGLU: return run_w8a8g<EPI_SWIGLU, 0, 128>(a, s);
+      case EPI_QKV:
+        if (a.head_dim == 128) return run_w8a8g<EPI_QKV, 128, 128>(a, s);
+        if (a.head_dim == 96) return run_w8a8g<EPI_QKV, 96, 96>(a, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (wfmt == 2) {   // W8A8 with one scale per row (FC2's per-row form)
     switch (epi) {
       case EPI_RESID:
         switch (resid_tile_width(a, true)) {

@@ -68,8 +68,26 @@ h3_status check_dims(const h3_dims* d) {
     return fail(H3_ERR_INVALID_ARG, "rope_theta must be > 0 and epsilons >= 0");
   if (d->wfmt != H3_W_BF16 && d->wfmt != H3_W_INT8_G32 && d->wfmt != H3_W_W8A8)
     return fail(H3_ERR_INVALID_ARG, "wfmt=%d unknown", d->wfmt);
+  if (d->wfmt == H3_W_W8A8) {
+    const int g = d->w8a8_group;
+    if (g != 64 && g != 256 && g != 448 && g != 896)
+      return fail(H3_ERR_UNSUPPORTED, "w8a8_group=%d: accepted 64, 256, 448, 896", g);
+    if (d->w8a8_row_fc2 != 0 && d->w8a8_row_fc2 != 1)
+      return fail(H3_ERR_INVALID_ARG, "w8a8_row_fc2=%d must be 0 or 1", d->w8a8_row_fc2);
+    const int di = d->heads * d->head_dim;
+    if (d->hidden % g != 0 || di % g != 0 || (!d->w8a8_row_fc2 && d->ffn % g != 0))
+      return fail(H3_ERR_UNSUPPORTED,
+                  "w8a8_group=%d must divide hidden=%d, heads*head_dim=%d%s (ffn=%d)", g, d->hidden, di,
+                  d->w8a8_row_fc2 ? "" : " and ffn", d->ffn);
+  }
   return H3_OK;
 }
+
+// W8A8: the scale group of the linear with input width K (FC2 with per-row
+// scales: one group spanning K).
+int w8_group(const h3_dims& d, int K, bool fc2) { return (fc2 && d.w8a8_row_fc2) ? K : d.w8a8_group; }
+// the same for GemmArgs::group: 0 selects the per-row kernel
+int gemm_group(const h3_dims& d, int K, bool fc2) { return (fc2 && d.w8a8_row_fc2) ? 0 : w8_group(d, K, fc2); }
 
 h3_status check_rows(int64_t n) {
   if (n <= 0 || n > kMaxRows) return fail(H3_ERR_INVALID_ARG, "n_rows=%lld out of [1, 2^24]", (long long)n);
@@ -132,8 +150,8 @@ h3_status hip_ok(hipError_t e, const char* what) {
 struct Arena {
   float* cs;
   uint16_t *h, *q, *k, *vt, *o, *a;
-  int8_t* qa;   // W8A8: int8 codes of o, then of a (h's codes live in h)
-  float* qs;    // W8A8: the row scales of the activation being consumed
+  int8_t* qa;   // W8A8: int8 codes of the activation about to be consumed (h, o, h2 or a)
+  float* qs;    // W8A8: its scales [K/G][n_pad]
   size_t bytes;
 };
 
@@ -163,10 +181,14 @@ Arena carve(const h3_dims& d, int64_t n, char* base) {
   a.a = reinterpret_cast<uint16_t*>(qkv);
   a.o = reinterpret_cast<uint16_t*>(take(np * Di * 2));
   if (d.wfmt == H3_W_W8A8) {
-    // W8A8 activation codes: h's in the h arena; o's and a's (consecutive
-    // lifetimes) here; one scale vector at a time
-    a.qa = reinterpret_cast<int8_t*>(take(np * std::max(Di, F)));
-    a.qs = reinterpret_cast<float*>(take(np * 4));
+    // W8A8: the codes and scales of one activation at a time (h, o, h2, a in
+    // turn), sized for the widest input and the most groups
+    const size_t kmax = std::max<size_t>(std::max<size_t>(D, Di), F);
+    const size_t ng = std::max<size_t>(std::max<size_t>(D / w8_group(d, (int)D, false),
+                                                        Di / w8_group(d, (int)Di, false)),
+                                       F / w8_group(d, (int)F, true));
+    a.qa = reinterpret_cast<int8_t*>(take(np * kmax));
+    a.qs = reinterpret_cast<float*>(take(np * ng * 4));
   }
   a.bytes = off;
   return a;
@@ -205,15 +227,12 @@ hipError_t do_rope(const h3_dims& d, const float* pos, int64_t n, float* cs, hip
 }
 
 hipError_t do_adaln(const h3_dims& d, const float* x, const int32_t* tag, const uint16_t* table,
-                    int which, int64_t n, uint16_t* h, hipStream_t s, int8_t* hq = nullptr,
-                    float* hs = nullptr) {
+                    int which, int64_t n, uint16_t* h, hipStream_t s) {
   h3::AdalnArgs a{};
   a.x = x;
   a.tag = tag;
   a.table = table;
   a.h = h;
-  a.hq = hq;
-  a.hs = hs;
   a.n = (int)n;
   a.D = d.hidden;
   a.k_shift = 3 * which;
@@ -222,23 +241,35 @@ hipError_t do_adaln(const h3_dims& d, const float* x, const int32_t* tag, const 
   return h3::launch_adaln(a, s);
 }
 
-hipError_t do_quant(const uint16_t* in, int64_t n, int K, int8_t* q, float* sc, hipStream_t s) {
+// int8 codes and scales [K/group][n_pad] of a bf16 activation [n][K]
+hipError_t do_quant(const uint16_t* in, int64_t n, int K, int group, int8_t* q, float* sc, hipStream_t s) {
   h3::QuantArgs a{};
   a.in = in;
   a.q = q;
   a.s = sc;
   a.n = (int)n;
   a.K = K;
-  return h3::launch_quant_rows(a, s);
+  a.group = group;
+  a.ld = (int)pad_rows(n);
+  return h3::launch_quant(a, s);
 }
 
-// sa: the W8A8 row scales of the int8 activation h (ignored otherwise)
+// W8A8 operands of a GEMM: the activation's scales (row stride n_pad) and the
+// linear's scale group (nothing for other formats)
+void set_w8(const h3_dims& d, h3::GemmArgs& g, const float* sa, int64_t n, bool fc2) {
+  if (d.wfmt != H3_W_W8A8) return;
+  g.sa = sa;
+  g.sa_ld = (int)pad_rows(n);
+  g.group = gemm_group(d, g.K, fc2);
+}
+
+// sa: the W8A8 scales of the int8 activation h (ignored otherwise)
 hipError_t do_qkv(const h3_dims& d, const uint16_t* h, const h3_block_weights& w, const float* cs,
                   int64_t n, uint16_t* q, uint16_t* k, uint16_t* vt, hipStream_t s,
                   const float* sa = nullptr) {
   const int Di = d.heads * d.head_dim;
   h3::GemmArgs g = gemm_base(d, h, w.w_qkv, w.s_qkv, w.b_qkv, (int)n, d.hidden, 3 * Di);
-  g.sa = sa;
+  set_w8(d, g, sa, n, false);
   g.q = q;
   g.k = k;
   g.vt = vt;
@@ -283,7 +314,7 @@ hipError_t do_resid(const h3_dims& d, const uint16_t* A, const void* W, const ui
                     const uint16_t* b, int K, const uint16_t* table, int kgate, const int32_t* tag,
                     int64_t n, float* x, hipStream_t s, const float* sa = nullptr) {
   h3::GemmArgs g = gemm_base(d, A, W, S, b, (int)n, K, d.hidden);
-  g.sa = sa;
+  set_w8(d, g, sa, n, kgate == 5);
   g.x = x;
   g.ldx = d.hidden;
   g.gate_tab = table + (size_t)kgate * d.hidden;
@@ -295,35 +326,37 @@ hipError_t do_resid(const h3_dims& d, const uint16_t* A, const void* W, const ui
 hipError_t do_fc1(const h3_dims& d, const uint16_t* h2, const h3_block_weights& w, int64_t n,
                   uint16_t* a, hipStream_t s, const float* sa = nullptr) {
   h3::GemmArgs g = gemm_base(d, h2, w.w_fc1, w.s_fc1, w.b_fc1, (int)n, d.hidden, 2 * d.ffn);
-  g.sa = sa;
+  set_w8(d, g, sa, n, false);
   g.out = a;
   g.ffn = d.ffn;
   return h3::launch_gemm(h3::EPI_SWIGLU, d.wfmt, g, s);
 }
 
-// W8A8 block: each linear's input is quantized per row right after it is made
-// (AdaLN writes the codes directly; o and a go through the row quantizer).
+// W8A8 block: each linear's bf16 input is quantized (per row and scale group)
+// right after it is made, into the arena's code and scale buffers.
 h3_status run_block_w8a8(const h3_dims& d, float* x, const int32_t* tag, const uint16_t* table,
                          const h3_block_weights& w, int64_t n, const Arena& ar, hipStream_t s,
                          const Sparse* sp) {
-  const int Di = d.heads * d.head_dim;
-  const uint16_t* hq = reinterpret_cast<const uint16_t*>(ar.h);      // int8 codes in the h arena
+  const int D = d.hidden, Di = d.heads * d.head_dim, F = d.ffn;
   const uint16_t* qa = reinterpret_cast<const uint16_t*>(ar.qa);
-  int8_t* hq_w = reinterpret_cast<int8_t*>(ar.h);
   h3_status st;
-  if ((st = hip_ok(do_adaln(d, x, tag, table, 0, n, nullptr, s, hq_w, ar.qs), "adaln (attention)")) != H3_OK)
+  if ((st = hip_ok(do_adaln(d, x, tag, table, 0, n, ar.h, s), "adaln (attention)")) != H3_OK) return st;
+  if ((st = hip_ok(do_quant(ar.h, n, D, w8_group(d, D, false), ar.qa, ar.qs, s), "quantize h")) != H3_OK)
     return st;
-  if ((st = hip_ok(do_qkv(d, hq, w, ar.cs, n, ar.q, ar.k, ar.vt, s, ar.qs), "qkv+rope")) != H3_OK) return st;
+  if ((st = hip_ok(do_qkv(d, qa, w, ar.cs, n, ar.q, ar.k, ar.vt, s, ar.qs), "qkv+rope")) != H3_OK) return st;
   if ((st = hip_ok(do_attn(d, ar.q, ar.k, ar.vt, n, ar.o, s, sp), "attention")) != H3_OK) return st;
-  if ((st = hip_ok(do_quant(ar.o, n, Di, ar.qa, ar.qs, s), "quantize o")) != H3_OK) return st;
+  if ((st = hip_ok(do_quant(ar.o, n, Di, w8_group(d, Di, false), ar.qa, ar.qs, s), "quantize o")) != H3_OK)
+    return st;
   if ((st = hip_ok(do_resid(d, qa, w.w_out, w.s_out, w.b_out, Di, table, 2, tag, n, x, s, ar.qs),
                    "out-proj+gate")) != H3_OK)
     return st;
-  if ((st = hip_ok(do_adaln(d, x, tag, table, 1, n, nullptr, s, hq_w, ar.qs), "adaln (mlp)")) != H3_OK)
+  if ((st = hip_ok(do_adaln(d, x, tag, table, 1, n, ar.h, s), "adaln (mlp)")) != H3_OK) return st;
+  if ((st = hip_ok(do_quant(ar.h, n, D, w8_group(d, D, false), ar.qa, ar.qs, s), "quantize h2")) != H3_OK)
     return st;
-  if ((st = hip_ok(do_fc1(d, hq, w, n, ar.a, s, ar.qs), "fc1+swiglu")) != H3_OK) return st;
-  if ((st = hip_ok(do_quant(ar.a, n, d.ffn, ar.qa, ar.qs, s), "quantize a")) != H3_OK) return st;
-  if ((st = hip_ok(do_resid(d, qa, w.w_fc2, w.s_fc2, w.b_fc2, d.ffn, table, 5, tag, n, x, s, ar.qs),
+  if ((st = hip_ok(do_fc1(d, qa, w, n, ar.a, s, ar.qs), "fc1+swiglu")) != H3_OK) return st;
+  if ((st = hip_ok(do_quant(ar.a, n, F, w8_group(d, F, true), ar.qa, ar.qs, s), "quantize a")) != H3_OK)
+    return st;
+  if ((st = hip_ok(do_resid(d, qa, w.w_fc2, w.s_fc2, w.b_fc2, F, table, 5, tag, n, x, s, ar.qs),
                    "fc2+gate")) != H3_OK)
     return st;
   return H3_OK;
@@ -535,7 +568,7 @@ h3_status check_sparse(int tile, const int32_t* off, const int32_t* idx) {
   return H3_OK;
 }
 
-// Row scales of a step entry point's activation buffer (W8A8), else null.
+// Scales of a step entry point's activation buffer (W8A8), else null.
 const float* act_scales(const h3_dims& d, const void* act, int64_t n, int64_t K) {
   if (d.wfmt != H3_W_W8A8) return nullptr;
   return reinterpret_cast<const float*>(static_cast<const char*>(act) + qa_scale_offset(n, K));
@@ -722,26 +755,29 @@ size_t h3_denoise_workspace_size(const h3_dims* dims, const h3_io_dims* io_dims,
          vel_history(*io_dims, sg).bytes;
 }
 
-size_t h3_quantized_bytes(int64_t n_rows, int32_t width) {
-  if (n_rows <= 0 || width <= 0) return 0;
-  return qa_scale_offset(n_rows, width) + up256((size_t)n_rows * 4);
+size_t h3_quantized_bytes(int64_t n_rows, int32_t width, int32_t group) {
+  if (n_rows <= 0 || n_rows > kMaxRows || width <= 0 || group <= 0 || width % group != 0) return 0;
+  return qa_scale_offset(n_rows, width) + up256((size_t)(width / group) * (size_t)pad_rows(n_rows) * 4);
 }
 
-h3_status h3_quantize_rows(const uint16_t* in, int64_t n_rows, int32_t width, void* out,
-                           void* stream) {
+h3_status h3_quantize_groups(const uint16_t* in, int64_t n_rows, int32_t width, int32_t group,
+                             void* out, void* stream) {
   g_err.clear();
   h3_status st;
   if ((st = check_rows(n_rows)) != H3_OK) return st;
   if (width <= 0 || width % 8 != 0 || width > 16384)
     return fail(H3_ERR_UNSUPPORTED, "width=%d: need a positive multiple of 8, at most 16384", width);
+  if (group != width && group != 64 && group != 256 && group != 448 && group != 896)
+    return fail(H3_ERR_UNSUPPORTED, "group=%d: accepted 64, 256, 448, 896, or the width (one per row)", group);
+  if (width % group != 0) return fail(H3_ERR_UNSUPPORTED, "group=%d does not divide width=%d", group, width);
   H3_NEED(in, "in");
   H3_NEED(out, "out");
   if ((st = check_device()) != H3_OK) return st;
   char* base = static_cast<char*>(out);
-  return hip_ok(do_quant(in, n_rows, width, reinterpret_cast<int8_t*>(base),
+  return hip_ok(do_quant(in, n_rows, width, group, reinterpret_cast<int8_t*>(base),
                          reinterpret_cast<float*>(base + qa_scale_offset(n_rows, width)),
                          reinterpret_cast<hipStream_t>(stream)),
-                "quantize rows");
+                "quantize groups");
 }
 
 size_t h3_workspace_size(const h3_dims* dims, int64_t n_rows) {
@@ -846,13 +882,6 @@ h3_status h3_adaln_modulate(const h3_dims* dims, const float* x, const int32_t* 
   if (which != 0 && which != 1) return fail(H3_ERR_INVALID_ARG, "which=%d must be 0 or 1", which);
   if ((st = check_device()) != H3_OK) return st;
   if ((st = check_tags(*dims, tag, n_rows, reinterpret_cast<hipStream_t>(stream))) != H3_OK) return st;
-  if (dims->wfmt == H3_W_W8A8) {   // h is a W8A8 activation buffer
-    char* base = reinterpret_cast<char*>(h);
-    return hip_ok(do_adaln(*dims, x, tag, mod_table, which, n_rows, nullptr,
-                           reinterpret_cast<hipStream_t>(stream), reinterpret_cast<int8_t*>(base),
-                           reinterpret_cast<float*>(base + qa_scale_offset(n_rows, dims->hidden))),
-                  "adaln");
-  }
   return hip_ok(do_adaln(*dims, x, tag, mod_table, which, n_rows, h,
                          reinterpret_cast<hipStream_t>(stream)),
                 "adaln");

@@ -19,30 +19,32 @@ struct AdalnArgs {
   const float* x;        // [n][D]
   const int32_t* tag;    // [n], or null: every row uses table entry 0
   const uint16_t* table; // [T][6][D]
-  uint16_t* h;           // [n][D] bf16 output, or null when hq is set
-  int8_t* hq;            // [n][D] int8 codes of the bf16 output (W8A8), or null
-  float* hs;             // [n] their row scales
+  uint16_t* h;           // [n][D] bf16 output
   int n, D, k_shift, k_scale;
   float eps;
 };
 hipError_t launch_adaln(const AdalnArgs& a, hipStream_t s);
 
-// Per-row symmetric int8 quantization of a bf16 matrix [n][K] (W8A8 activations).
+// Symmetric int8 quantization of a bf16 matrix [n][K] (W8A8 activations), one
+// scale per group of `group` consecutive K elements (group == K: per row).
 struct QuantArgs {
   const uint16_t* in;    // [n][K] bf16
   int8_t* q;             // [n][K]
-  float* s;              // [n]
-  int n, K;
+  float* s;              // [K/group][ld] group-major; rows n..ld-1 set to 0
+  int n, K, group, ld;
 };
-hipError_t launch_quant_rows(const QuantArgs& a, hipStream_t s);
+hipError_t launch_quant(const QuantArgs& a, hipStream_t s);
 
 enum Epi { EPI_RESID = 0, EPI_SWIGLU = 1, EPI_QKV = 2, EPI_STORE = 3 };
 
 struct GemmArgs {
-  const uint16_t* A;      // [M][K] bf16
+  const uint16_t* A;      // [M][K] bf16 (int8 codes for W8A8)
   const void* B;          // [Nw][K] bf16 or int8
-  const uint16_t* Bs;     // bf16 weight scales: [Nw][K/32] (INT8 g32) or [Nw] (W8A8)
-  const float* sa;        // [M] fp32 row scales of int8 A (W8A8)
+  const uint16_t* Bs;     // bf16 weight scales: [Nw][K/32] (INT8 g32), [K/group][Nw]
+                          // (W8A8) or [Nw] (W8A8 per row)
+  const float* sa;        // fp32 scales of int8 A (W8A8): [K/group][sa_ld], or [M] per row
+  int group;              // W8A8: K elements per scale group (0: one scale per row)
+  int sa_ld;              // W8A8: row stride of sa (the padded row count)
   const uint16_t* bias;   // [Nw] or null
   int M, K;
   int n_out;              // GEMM output columns (= B rows used)

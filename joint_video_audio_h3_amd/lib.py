@@ -27,7 +27,8 @@ class H3Error(RuntimeError):
 class H3Dims(ctypes.Structure):
     _fields_ = [("hidden", c_i32), ("heads", c_i32), ("head_dim", c_i32), ("ffn", c_i32),
                 ("n_tags", c_i32), ("rope_split", c_i32 * 3), ("rope_theta", c_f32),
-                ("ln_eps", c_f32), ("qk_eps", c_f32), ("wfmt", c_i32)]
+                ("ln_eps", c_f32), ("qk_eps", c_f32), ("wfmt", c_i32), ("w8a8_group", c_i32),
+                ("w8a8_row_fc2", c_i32)]
 
 
 WEIGHT_FIELDS = ["w_qkv", "w_out", "w_fc1", "w_fc2", "s_qkv", "s_out", "s_fc1", "s_fc2",
@@ -80,7 +81,7 @@ _SIGS = {
     "h3_mlp_fc2_residual": (c_i32, [ctypes.POINTER(H3Dims), c_vp, ctypes.POINTER(H3BlockWeights),
                                     c_vp, c_vp, c_i64, c_vp, c_vp]),
     "h3_heads_workspace_size": (c_sz, [_PD, _PSG]),
-    "h3_quantized_bytes": (c_sz, [c_i64, c_i32]),
+    "h3_quantized_bytes": (c_sz, [c_i64, c_i32, c_i32]),
     "h3_sigma_schedule": (c_i32, [c_i32, ctypes.c_double, ctypes.POINTER(ctypes.c_double)]),
     "h3_denoise_workspace_size": (c_sz, [_PD, _PIO, _PSG]),
     "h3_denoise": (c_i32, [_PD, _PIO, _PW, _PSG, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
@@ -90,7 +91,7 @@ _SIGS = {
     "h3_attention_sparse": (c_i32, [_PD, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "h3_dit_forward_sparse": (c_i32, [_PD, c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(H3BlockWeights), c_i32,
                                       c_i64, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
-    "h3_quantize_rows": (c_i32, [c_vp, c_i64, c_i32, c_vp, c_vp]),
+    "h3_quantize_groups": (c_i32, [c_vp, c_i64, c_i32, c_i32, c_vp, c_vp]),
     "h3_embed_inputs": (c_i32, [_PD, _PIO, _PW, _PSG, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "h3_final_heads": (c_i32, [_PD, _PIO, _PW, _PSG, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "h3_velocity_forward": (c_i32, [_PD, _PIO, _PW, _PSG, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
@@ -132,6 +133,8 @@ def make_dims(d) -> H3Dims:
     s.hidden, s.heads, s.head_dim, s.ffn, s.n_tags = d.hidden, d.heads, d.head_dim, d.ffn, d.n_tags
     s.rope_split[:] = list(d.rope_split)
     s.rope_theta, s.ln_eps, s.qk_eps, s.wfmt = d.rope_theta, d.ln_eps, d.qk_eps, d.wfmt
+    s.w8a8_group = getattr(d, "w8a8_group", 0)
+    s.w8a8_row_fc2 = getattr(d, "w8a8_row_fc2", 0)
     return s
 
 
@@ -311,13 +314,15 @@ def denoise(dims, io, io_w: Dict, text, cond, audio, video, tag, positions, mod_
         x.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)))
 
 
-def quantized_bytes(n_rows: int, width: int) -> int:
-    return load().h3_quantized_bytes(n_rows, width)
+def quantized_bytes(n_rows: int, width: int, group: int) -> int:
+    return load().h3_quantized_bytes(n_rows, width, group)
 
 
-def quantize_rows(x, out, stream=None):
-    """W8A8 activation buffer ``out`` (uint8, quantized_bytes) <- per-row int8 codes of bf16 x."""
-    _check(load().h3_quantize_rows(x.data_ptr(), x.shape[0], x.shape[1], out.data_ptr(), _stream(stream)))
+def quantize_groups(x, group: int, out, stream=None):
+    """W8A8 activation buffer ``out`` (uint8, quantized_bytes) <- int8 codes of bf16 x
+    [n, K] with one scale per row and group of ``group`` elements (group = K: per row)."""
+    _check(load().h3_quantize_groups(x.data_ptr(), x.shape[0], x.shape[1], group, out.data_ptr(),
+                                     _stream(stream)))
 
 
 def make_io_dims(io) -> H3IoDims:

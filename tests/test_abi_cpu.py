@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_struct_layouts_match_header():
-    assert ctypes.sizeof(lib.H3Dims) == 4 * 12
+    assert ctypes.sizeof(lib.H3Dims) == 4 * 14
     assert ctypes.sizeof(lib.H3BlockWeights) == 8 * 14
     assert ctypes.sizeof(lib.H3IoDims) == 4 * 3
     assert ctypes.sizeof(lib.H3Segments) == 8 * 4

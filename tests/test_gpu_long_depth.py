@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from joint_video_audio_h3_amd import lib, synth
-from tests.gpu_util import TOL_BLOCK, TOL_DEPTH, dev, rel_l2, say
+from tests.gpu_util import TOL_DEPTH, dev, rel_l2, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(os.environ.get("H3_LONG_TESTS") != "1",
@@ -57,11 +57,7 @@ def test_fifty_block_forward_n6437_matches_oracle(wname):
     x64 = x.astype(np.float64)
     e, du = rel_l2(got, ref), rel_l2(got - x64, ref - x64)
     say("long depth: rel-L2 x_out", e, "update", du)
-    # bf16 weights: the stated full-depth bar.  W8A8: each side quantizes its own
-    # activations per row, so a code near a rounding boundary can differ between
-    # the two, and every block adds an independent error of up to the block bar;
-    # over B blocks that grows as sqrt(B): TOL_BLOCK * sqrt(50) = 7.1e-2
-    tol = TOL_DEPTH if wl.dims.wfmt != synth.WFMT_W8A8 else TOL_BLOCK * np.sqrt(wl.n_blocks)
+    # the stated full-depth bar, for bf16 weights and the group-scaled W8A8 trunk alike
     assert np.isfinite(got).all()
-    assert e < tol
-    assert du < 2 * tol
+    assert e < TOL_DEPTH
+    assert du < 2 * TOL_DEPTH
