@@ -27,7 +27,7 @@
 //
 // W8A8, group-scaled (gemm_w8a8g_kernel): int8 MFMAs into int32 accumulators
 // per group of K elements, folded into fp32 with the group's activation and
-// weight scales; four wavefronts of 64 x 128 tiles.
+// weight scales; eight wavefronts of 32 x 128 tiles, two per SIMD.
 //
 // INT8 weights (gemm_w8_kernel): eight wavefronts of 64 x 128 tiles; A streams
 // in by DMA, int8 codes go through registers, where they are dequantised to
@@ -926,34 +926,39 @@ __global__ __launch_bounds__(512) void gemm_w8_kernel(GemmArgs p) {
 // on both operands):
 //   y[r][c] = sum_g s_a[g][r] * s_w[g][c] * sum_{k in g} q_a[r][k] * q_w[c][k]
 // Each group's integer sum is exact in int32 (|sum| <= 896 * 127^2 < 2^24, so
-// also exact as fp32), then folded into fp32 accumulators at the group's end.
-// Both accumulator sets live through the K loop, so the wave tile is 64 x 128
-// (128 int32 + 128 fp32 registers): four wavefronts stacked 4 x 1 on a 256 x
-// 128 block tile (256 x 96 for the 96-wide head sections of the small model),
-// each wave owning whole head sections as the QKV epilogue needs.
-// v_mfma_i32_32x32x32_i8 takes 32 K per step, so a 128-byte stage row holds 4
-// steps and every group ends on an even step.  Stages (A 32 KB + B 16 KB) move
-// by DMA into a 3-stage ring with the bf16 kernel's swizzle; with each stage
-// come the scales of the (at most two) groups it touches: s_a for the 256 rows
-// (1 KB) and s_w for the tile's columns, both contiguous in their group-major
-// layouts.  The first step of a group starts its int32 accumulators from zero
-// (the MFMA's C operand), the last one is followed by the fold
-//   f[r][c] += float(i[r][c]) * (s_a[r] * s_w[c]).
+// also exact as fp32), then folded into fp32 accumulators at the group's end:
+//   f[r][c] += float(i[r][c]) * s_w[c] * s_a[r].
+// Both accumulator sets live through the K loop.  The fold is VALU work that
+// depends on the group's last MFMAs, so two wavefronts share each SIMD: one's
+// fold runs beside the other's MFMAs.  That caps a wave at 256 registers, so
+// wave tiles are 32 x 128 (64 int32 + 64 fp32 accumulators): eight wavefronts
+// stacked 8 x 1 on a 256 x 128 block tile (256 x 96 for the 96-wide head
+// sections of the small model), each wave owning whole head sections as the
+// QKV epilogue needs.  v_mfma_i32_32x32x32_i8 takes 32 K per step, so a
+// 128-byte stage row holds 4 steps and every group ends on an even step.
+// Stages (A 32 KB + B 16 KB) move by DMA into a 3-stage ring with the bf16
+// kernel's swizzle; with each stage come the scales of the (at most two)
+// groups it touches: s_a for the 256 rows (1 KB) and s_w for the tile's
+// columns, both contiguous in their group-major layouts.  The first step of a
+// group starts its int32 accumulators from zero (the MFMA's C operand).
 template <int EPI, int SEC, int BN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w8a8g_kernel(GemmArgs p) {
-  constexpr int BM = 256, WM = 4, WN = 1;
-  constexpr int TM = BM / WM, TN = BN / WN;       // 64 x BN
-  constexpr int FM = TM / 32, FN = TN / 32;       // 2 x (4 or 3)
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_w8a8g_kernel(GemmArgs p) {
+  constexpr int NW = 8;                           // wavefronts
+  constexpr int BM = 256, WM = NW, WN = 1;
+  constexpr int TM = BM / WM, TN = BN / WN;       // 32 x BN
+  constexpr int FM = TM / 32, FN = TN / 32;       // 1 x (4 or 3)
   constexpr int SK = 128;                         // K (bytes) per stage row
   constexpr int ABYTES = BM * SK, BBYTES = BN * SK;
   constexpr int STAGE = ABYTES + BBYTES;
   constexpr int NST = 3;                          // ring of stages
   constexpr int SCL = 4096;                       // per stage: s_a of 2 groups, then s_w of 2 groups
-  constexpr int NA = BM / 32, NB = BN / 32;       // 1 KB (8-row) loads per wave per stage
+  constexpr int NRA = BM / 8, NRB = BN / 8;       // 8-row (1 KB) blocks of A and B
+  constexpr int NA = (NRA + NW - 1) / NW, NB = (NRB + NW - 1) / NW;   // loads per wave per stage
   constexpr int PER = NA + NB + 1;                // DMA instructions per wave per stage
   static_assert(EPI != EPI_QKV || TN == SEC, "QKV wave tile must be one head section");
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU needs paired gate/value tiles");
   static_assert(NST * STAGE + NST * SCL <= 160 * 1024, "LDS");
+  static_assert(NW * 32 * RSTRIDE * 4 + BM * 4 <= NST * STAGE + NST * SCL, "epilogue staging");
   __shared__ __attribute__((aligned(1024))) char ring[NST * STAGE + NST * SCL];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -967,26 +972,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint32_t ring0 = lds_addr(ring);
   const uint32_t scl0 = ring0 + NST * STAGE;
 
-  // A / B loads: load s of a wave covers rows 8*(wave + 4s) .. +7; lane l fills
-  // row 8*(wave + 4s) + l/8, position l%8, which holds global chunk (l%8) ^ f(row)
+  // A / B loads: load s of a wave fills 8-row block rb = wave + 8s (past the
+  // last block a wave repeats an earlier block's load, so every wave issues
+  // the same number); lane l fills row 8*rb + l/8, position l%8, which holds
+  // global chunk (l%8) ^ f(row)
   const char* baseA = reinterpret_cast<const char*>(p.A) + (size_t)m0 * rowb;
   const int b0 = weight_row_base<EPI, BN>(tc.tn);
   const char* baseB = reinterpret_cast<const char*>(p.B) + (size_t)b0 * rowb;
-  uint32_t voA[NA], voB[NB];
+  uint32_t voA[NA], voB[NB], ldA[NA], ldB[NB];
 #pragma unroll
   for (int s = 0; s < NA; ++s) {
-    const int r = 8 * (wave + 4 * s) + lane / 8;
+    const int rb = (wave + NW * s) % NRA;
+    const int r = 8 * rb + lane / 8;
     voA[s] = (uint32_t)(min(m0 + r, p.M - 1) - m0) * rowb + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+    ldA[s] = __builtin_amdgcn_readfirstlane(rb * 1024);
   }
 #pragma unroll
   for (int s = 0; s < NB; ++s) {
-    const int r = 8 * (wave + 4 * s) + lane / 8;
+    const int rb = (wave + NW * s) % NRB;
+    const int r = 8 * rb + lane / 8;
     voB[s] = (uint32_t)(weight_row<EPI, BN, TN>(p, tc.tn, r) - b0) * rowb + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+    ldB[s] = __builtin_amdgcn_readfirstlane(ABYTES + rb * 1024);
   }
-  // scale loads, one per wave per stage: waves 0 / 1 bring s_a of the stage's
-  // first / last group (256 rows, 16 B per lane), waves 2 / 3 s_w of the same
-  // groups (BN columns, 8 per lane; lanes past them repeat lane 0's piece)
-  const bool sa_wave = wave < 2;
+  // scale loads, one per wave per stage: wave w brings (w & 2 ? s_w : s_a) of
+  // the stage's (w & 1 ? last : first) group (waves 4-7 repeat waves 0-3):
+  // s_a for the 256 rows (16 B per lane), s_w for the BN columns (8 per lane;
+  // lanes past them repeat lane 0's piece)
+  const bool sa_wave = (wave & 2) == 0;
+  const int sub_w = wave & 1;
   uint32_t vo_s;
   if (sa_wave) {
     vo_s = (uint32_t)(m0 + 4 * lane) * 4;
@@ -999,42 +1012,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto group_hi = [&](int kt) { return min((kt * SK + SK - 1) / G, ng - 1); };
 
   auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
-    const uint32_t so = (uint32_t)slot * STAGE;
+    const uint32_t so = __builtin_amdgcn_readfirstlane(ring0 + (uint32_t)slot * STAGE);
     const char* sa_ = baseA + (size_t)kt * SK;
     const char* sb_ = baseB + (size_t)kt * SK;
-    const uint32_t mw = __builtin_amdgcn_readfirstlane(ring0 + so + wave * 1024);
 #pragma unroll
-    for (int s = 0; s < NA; ++s) dma16s(voA[s], sa_, mw + s * 4096);
+    for (int s = 0; s < NA; ++s) dma16s(voA[s], sa_, so + ldA[s]);
 #pragma unroll
-    for (int s = 0; s < NB; ++s) dma16s(voB[s], sb_, mw + ABYTES + s * 4096);
-    const int g = (wave & 1) ? group_hi(kt) : group_lo(kt);
+    for (int s = 0; s < NB; ++s) dma16s(voB[s], sb_, so + ldB[s]);
+    const int g = sub_w ? group_hi(kt) : group_lo(kt);
     const uintptr_t sb = sa_wave ? reinterpret_cast<uintptr_t>(p.sa + (size_t)g * p.sa_ld)
                                  : reinterpret_cast<uintptr_t>(p.Bs + (size_t)g * nw);
-    // wave-uniform (the wave index is), so it can live in SGPRs
-    // (readfirstlane returns int: each half goes through uint32_t, or the low
-    // half would sign-extend into the high one)
+    // wave-uniform (the wave index is), so it can live in SGPRs (readfirstlane
+    // returns int: each half goes through uint32_t, or the low half would
+    // sign-extend into the high one)
     const uint64_t sbu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32)) << 32) |
                          (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb);
     dma16s(vo_s, reinterpret_cast<const char*>(sbu),
-           __builtin_amdgcn_readfirstlane(scl0 + slot * SCL + (sa_wave ? 0 : 2048) + (wave & 1) * 1024));
+           __builtin_amdgcn_readfirstlane(scl0 + slot * SCL + (sa_wave ? 0 : 2048) + sub_w * 1024));
   };
 
   // fragment reads: row lane%32 of each 32-row tile, chunk 2*kk + lane/32 at
-  // its swizzled position; per-lane bases for the two row parities and four
-  // steps of a stage, plus the stage's slot offset
+  // its swizzled position; per-lane bases for the wave's A rows, the two B row
+  // parities and the four steps of a stage, plus the stage's slot offset
   const int fr = lane & 31, hl = lane >> 5;
-  uint32_t rA[2][4], rB[2][4];
+  uint32_t rA[FM][4], rB[2][4];
 #pragma unroll
-  for (int par = 0; par < 2; ++par)
+  for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      rA[par][kk] = ring0 + (wm * TM + fr) * SK + (((2 * kk + hl) ^ swz(fr + 32 * par)) * 16);
-      rB[par][kk] = ring0 + ABYTES + fr * SK + (((2 * kk + hl) ^ swz(fr + 32 * par)) * 16);
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * TM + 32 * i + fr;
+      rA[i][kk] = ring0 + r * SK + (((2 * kk + hl) ^ swz(r)) * 16);
     }
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      rB[par][kk] = ring0 + ABYTES + fr * SK + (((2 * kk + hl) ^ swz(fr + 32 * par)) * 16);
+  }
   auto read_frags = [&](uint32_t so, int kk, i32x4 (&fa)[FM], i32x4 (&fb)[FN]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      fa[i] = __builtin_bit_cast(i32x4, lds_read16(rA[i & 1][kk] + so + i * 32 * SK));
+    for (int i = 0; i < FM; ++i) fa[i] = __builtin_bit_cast(i32x4, lds_read16(rA[i][kk] + so));
 #pragma unroll
     for (int j = 0; j < FN; ++j)
       fb[j] = __builtin_bit_cast(i32x4, lds_read16(rB[j & 1][kk] + so + j * 32 * SK));
@@ -1061,7 +1076,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           iacc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], iacc[i][j], 0, 0, 0);
     }
   };
-  // f += float(i) * s_a[row] * s_w[col] with the group's scales from the
+  // f += float(i) * s_w[col] * s_a[row] with the group's scales from the
   // stage's scale slot (sub = 0: the stage's first group, 1: its last)
   auto fold = [&](int slot, int sub) __attribute__((always_inline)) {
     const float* sa_l = reinterpret_cast<const float*>(ring + NST * STAGE + slot * SCL + sub * 1024);
@@ -1120,8 +1135,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   __syncthreads();
   if constexpr (EPI == EPI_RESID) {
-    int* s_tag = reinterpret_cast<int*>(ring + 4 * 32 * RSTRIDE * sizeof(float));
-    s_tag[tid] = p.tag[min(m0 + tid, p.M - 1)];
+    int* s_tag = reinterpret_cast<int*>(ring + NW * 32 * RSTRIDE * sizeof(float));
+    if (tid < BM) s_tag[tid] = p.tag[min(m0 + tid, p.M - 1)];
     __syncthreads();
     resid_epilogue_lds<true, TM, TN, FM, FN>(p, facc, m0 + wm * TM, n0, lane,
                                              reinterpret_cast<float*>(ring) + wave * 32 * RSTRIDE, s_tag + wm * TM);
@@ -1154,7 +1169,7 @@ static hipError_t run_direct(const GemmArgs& a, hipStream_t s) {
 
 template <int EPI, int SEC, int BN>
 static hipError_t run_w8a8g(const GemmArgs& a, hipStream_t s) {
-  gemm_w8a8g_kernel<EPI, SEC, BN><<<grid_for<256, BN>(EPI, a), 256, 0, s>>>(a);
+  gemm_w8a8g_kernel<EPI, SEC, BN><<<grid_for<256, BN>(EPI, a), 512, 0, s>>>(a);
   return hipGetLastError();
 }
 
