@@ -31,3 +31,18 @@ def test_help_lists_the_sections():
     for flag in ("--steps", "--warmup", "--secondary", "--extra", "--denoise-steps", "--denoise-reuse",
                  "--sparse", "--w8a8"):
         assert flag in r.stdout
+
+
+def test_roofline_traffic_only_for_the_source_it_was_measured_on(monkeypatch):
+    import hashlib
+    import importlib
+    import sys as _sys
+    _sys.path.insert(0, ROOT)
+    bench = importlib.import_module("bench")
+    with open(os.path.join(ROOT, "joint_video_audio_h3_amd", "csrc", "attention.hip"), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    monkeypatch.setattr(bench, "TRAFFIC_BYTES", {("w", "attention"): (1.5e9, sha)})
+    assert bench.measured_traffic("w", "attention") == 1.5e9
+    monkeypatch.setattr(bench, "TRAFFIC_BYTES", {("w", "attention"): (1.5e9, "0" * 16)})
+    assert bench.measured_traffic("w", "attention") is None
+    assert bench.measured_traffic("other", "attention") is None
