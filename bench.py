@@ -122,7 +122,7 @@ def step_breakdown(lib, dims, wl_rows, table, block, reps, torch, only=None):
     return out, w
 
 
-def step_breakdown_w8a8(lib, dims, wl_rows, table, block, reps, torch):
+def step_breakdown_w8a8(lib, dims, wl_rows, table, block, reps, torch, only=None):
     """Per-kernel times of one W8A8 block's steps (int8 GEMMs against the int8 peak)."""
     x, tags, pos = wl_rows
     n = x.shape[0]
@@ -159,6 +159,13 @@ def step_breakdown_w8a8(lib, dims, wl_rows, table, block, reps, torch):
         "fc2_resid": (lambda: lib.mlp_fc2_residual(dims, aq, block, t0, tags, xs), w.fc2_flop, None, I8),
     }
     out = {}
+    if only:
+        # inputs of the later steps come from running the earlier ones once
+        for name, (fn, _, _, _) in steps.items():
+            if name == only:
+                break
+            fn()
+        steps = {only: steps[only]}
     for name, (fn, flop, nbytes, peak) in steps.items():
         ms = _time_launches(fn, reps, torch)
         r = {"ms": round(ms, 4)}
@@ -169,6 +176,8 @@ def step_breakdown_w8a8(lib, dims, wl_rows, table, block, reps, torch):
             gbs = nbytes / (ms * 1e-3) / 1e9
             r.update(gbs=round(gbs, 1), hbm_frac=round(gbs / HBM, 4))
         out[name] = r
+    if only:
+        return out, w
     lin = ("qkv_rope", "out_proj_resid", "fc1_swiglu", "fc2_resid")
     gemm_ms = sum(out[s_]["ms"] for s_ in lin)
     out["gemms_total"] = {"ms": round(gemm_ms, 4), "tops": round(w.linear_flop / gemm_ms / 1e9, 1),
@@ -394,7 +403,8 @@ def main():
                     help="also run the forwards with the W8A8 trunk (0: skip)")
     ap.add_argument("--only-step", default=None,
                     help="time just one step kernel (adaln, qkv_rope, attention, out_proj_resid, "
-                         "fc1_swiglu, fc2_resid) on one block's weights, e.g. under a counter run")
+                         "fc1_swiglu, fc2_resid; with a W8A8 workload also quant_h, quant_o, "
+                         "quant_a) on one block's weights, e.g. under a counter run")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -418,8 +428,9 @@ def main():
             torch.cuda.synchronize()
             del src, dst
         table, blocks = synth.make_device_weights(dims, 1, seed=0)
-        bd, _ = step_breakdown(lib, dims, synth.make_device_rows(wl, seed=1), table, blocks[0],
-                               args.breakdown_reps, torch, only=args.only_step)
+        fn = step_breakdown_w8a8 if dims.wfmt == synth.WFMT_W8A8 else step_breakdown
+        bd, _ = fn(lib, dims, synth.make_device_rows(wl, seed=1), table, blocks[0],
+                   args.breakdown_reps, torch, only=args.only_step)
         print(json.dumps({"workload": wl.name, "step": args.only_step, **bd[args.only_step]}))
         return
     log(f"generating {wl.n_blocks} blocks of weights on the device")

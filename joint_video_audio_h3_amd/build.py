@@ -33,23 +33,23 @@ def _flags():
             "-I", CSRC, "-I", os.path.join(os.path.dirname(PKG), "include")]
 
 
+def _compile_one(hipcc: str, src: str, verbose: bool = False) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [hipcc] + _flags() + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr[-6000:]}")
+    if verbose and r.stderr.strip():
+        print(r.stderr)
+    return obj
+
+
 def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
-
-    def compile_one(src):
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc] + _flags() + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr[-6000:]}")
-        if verbose and r.stderr.strip():
-            print(r.stderr)
-        return obj
-
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+        objs = list(ex.map(lambda src: _compile_one(hipcc, src, verbose), SOURCES))
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -57,6 +57,54 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed:\n{r.stderr[-6000:]}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
+
+
+SAN_LIB_PATH = os.path.join(BUILD, "san", "libh3dit_san.so")
+
+
+def build_host_sanitized() -> str:
+    """The same library with its host code (the C ABI, argument checks, workspace
+    carving: ``h3dit.cpp``) built by g++ under AddressSanitizer and
+    UndefinedBehaviorSanitizer; the kernel objects are the ordinary hipcc ones.
+    For the CPU ABI tests only (load it with ``$H3DIT_LIB`` and GCC's libasan
+    preloaded).  Returns the library's path."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        raise RuntimeError("g++ not found")
+    hipcc = _hipcc()
+    os.makedirs(os.path.dirname(SAN_LIB_PATH), exist_ok=True)
+    kernels = [s for s in SOURCES if s.endswith(".hip")]
+    # the kernel objects of the last build() are reused when no source is newer
+    newest = max(os.path.getmtime(os.path.join(d, f))
+                 for d in (CSRC, os.path.join(os.path.dirname(PKG), "include")) for f in os.listdir(d))
+
+    def kernel_obj(src):
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        if os.path.exists(obj) and os.path.getmtime(obj) >= newest:
+            return obj
+        return _compile_one(hipcc, src)
+
+    with cf.ThreadPoolExecutor(max_workers=len(kernels)) as ex:
+        objs = list(ex.map(kernel_obj, kernels))
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]
+    obj = os.path.join(os.path.dirname(SAN_LIB_PATH), "h3dit_san.o")
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc)))
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fPIC", "-fno-omit-frame-pointer", "-Wall",
+           "-Wno-unused-function", "-fvisibility=hidden", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", CSRC,
+           "-I", os.path.join(os.path.dirname(PKG), "include")] + san + \
+          ["-c", os.path.join(CSRC, "h3dit.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"g++ failed on h3dit.cpp:\n{r.stderr[-6000:]}")
+    tmp = SAN_LIB_PATH + ".tmp"
+    cmd = [gxx, "-shared"] + san + ["-o", tmp, obj] + objs + \
+          ["-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{r.stderr[-6000:]}")
+    os.replace(tmp, SAN_LIB_PATH)
+    return SAN_LIB_PATH
 
 
 if __name__ == "__main__":

@@ -102,11 +102,15 @@ _SIGS = {
 _lib = None
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load the HIP library (no fallback: raises if it has not been built)."""
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the HIP library (no fallback: raises if it has not been built).
+
+    ``path`` defaults to the in-tree build, or to ``$H3DIT_LIB`` when that is
+    set (the host-sanitizer build of the same sources, for the CPU ABI tests)."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("H3DIT_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
                            "(the H3 forward has no CPU path)")
