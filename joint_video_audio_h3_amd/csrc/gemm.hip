@@ -427,9 +427,26 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(
 // 16 bytes per lane from sbase + voff (sbase wave-uniform, in SGPRs) straight
 // into LDS at lds + 16*lane (M0).  Asm keeps the compiler's wait insertion from
 // draining in-flight stages before LDS reads; completion is tracked with
-// wait_vmcnt.
+// wait_vmcnt.  The compiler does not insert hazard wait states across an asm
+// statement: on gfx9 a vector memory instruction reads its SGPR operands
+// without waiting for a VALU instruction that writes them (five wait states
+// are needed), so sbase must come from SALU arithmetic (kernel arguments,
+// offsets), never from a v_readfirstlane just before the call.
 __device__ __forceinline__ void dma16s(uint32_t voff, const char* sbase, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_from(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_from<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_from<0, N>(f);
 }
 
 // lowest weight row a tile reads (the per-lane offsets are relative to it)
@@ -941,7 +958,7 @@ __global__ __launch_bounds__(512) void gemm_w8_kernel(GemmArgs p) {
 // groups it touches: s_a for the 256 rows (1 KB) and s_w for the tile's
 // columns, both contiguous in their group-major layouts.  The first step of a
 // group starts its int32 accumulators from zero (the MFMA's C operand).
-template <int EPI, int SEC, int BN>
+template <int EPI, int SEC, int BN, int G>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_w8a8g_kernel(GemmArgs p) {
   constexpr int NW = 8;                           // wavefronts
   constexpr int BM = 256, WM = NW, WN = 1;
@@ -951,23 +968,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int ABYTES = BM * SK, BBYTES = BN * SK;
   constexpr int STAGE = ABYTES + BBYTES;
   constexpr int NST = 3;                          // ring of stages
+  constexpr int NSC = 4;                          // ring of scale slots (one more than stages)
   constexpr int SCL = 4096;                       // per stage: s_a of 2 groups, then s_w of 2 groups
   constexpr int NRA = BM / 8, NRB = BN / 8;       // 8-row (1 KB) blocks of A and B
   constexpr int NA = (NRA + NW - 1) / NW, NB = (NRB + NW - 1) / NW;   // loads per wave per stage
   constexpr int PER = NA + NB + 1;                // DMA instructions per wave per stage
   static_assert(EPI != EPI_QKV || TN == SEC, "QKV wave tile must be one head section");
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU needs paired gate/value tiles");
-  static_assert(NST * STAGE + NST * SCL <= 160 * 1024, "LDS");
-  static_assert(NW * 32 * RSTRIDE * 4 + BM * 4 <= NST * STAGE + NST * SCL, "epilogue staging");
-  __shared__ __attribute__((aligned(1024))) char ring[NST * STAGE + NST * SCL];
+  static_assert(NST * STAGE + NSC * SCL <= 160 * 1024, "LDS");
+  static_assert(NW * 32 * RSTRIDE * 4 + BM * 4 <= NST * STAGE + NSC * SCL, "epilogue staging");
+  __shared__ __attribute__((aligned(1024))) char ring[NST * STAGE + NSC * SCL];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave;                            // WN == 1
   const TileCoord tc = tile_coord<EPI, BM, BN>(p);
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
-  const int K = p.K, G = p.group;
-  const int ng = K / G, GK = G / 32;              // groups; MFMA steps per group
-  const int KT = K / SK;
+  constexpr int GK = G / 32;                      // MFMA steps per group
+  // stages per period: the shortest run of stages that holds whole groups
+  // (lcm(SK, G) / SK), so within a period every group boundary, fold and
+  // first step of a group sits at a fixed step
+  constexpr int P = (G % SK == 0) ? G / SK : (SK % G == 0 ? 1 : 2 * G / SK);
+  static_assert((P * SK) % G == 0 && (G % 64) == 0, "group layout");
+  const int K = p.K;
+  const int ng = K / G;                           // groups
+  const int KT = K / SK;                          // stages (a multiple of P)
   const uint32_t rowb = (uint32_t)K;
   const uint32_t ring0 = lds_addr(ring);
   const uint32_t scl0 = ring0 + NST * STAGE;
@@ -998,8 +1022,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // the stage's (w & 1 ? last : first) group (waves 4-7 repeat waves 0-3):
   // s_a for the 256 rows (16 B per lane), s_w for the BN columns (8 per lane;
   // lanes past them repeat lane 0's piece)
-  const bool sa_wave = (wave & 2) == 0;
-  const int sub_w = wave & 1;
+  // (the wave index through readfirstlane: the choices below are then
+  // scalar, and the scale pointer and its LDS slot are formed by SALU
+  // instructions in SGPRs)
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const bool sa_wave = (wave_u & 2) == 0;
+  const int sub_w = wave_u & 1;
   uint32_t vo_s;
   if (sa_wave) {
     vo_s = (uint32_t)(m0 + 4 * lane) * 4;
@@ -1008,11 +1036,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     vo_s = (uint32_t)weight_row<EPI, BN, TN>(p, tc.tn, c) * 2;
   }
   const int nw = EPI == EPI_SWIGLU ? 2 * p.ffn : p.n_out;   // weight rows (s_w row length)
+  const char* sbase = sa_wave ? reinterpret_cast<const char*>(p.sa) : reinterpret_cast<const char*>(p.Bs);
+  const size_t sstride = sa_wave ? (size_t)p.sa_ld * 4 : (size_t)nw * 2;   // bytes per group
+  const uint32_t sm0 = __builtin_amdgcn_readfirstlane(scl0) + (sa_wave ? 0 : 2048) + sub_w * 1024;
   auto group_lo = [&](int kt) { return (kt * SK) / G; };
   auto group_hi = [&](int kt) { return min((kt * SK + SK - 1) / G, ng - 1); };
 
   auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
     const uint32_t so = __builtin_amdgcn_readfirstlane(ring0 + (uint32_t)slot * STAGE);
+    const int sslot = kt & (NSC - 1);
     const char* sa_ = baseA + (size_t)kt * SK;
     const char* sb_ = baseB + (size_t)kt * SK;
 #pragma unroll
@@ -1020,15 +1052,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int s = 0; s < NB; ++s) dma16s(voB[s], sb_, so + ldB[s]);
     const int g = sub_w ? group_hi(kt) : group_lo(kt);
-    const uintptr_t sb = sa_wave ? reinterpret_cast<uintptr_t>(p.sa + (size_t)g * p.sa_ld)
-                                 : reinterpret_cast<uintptr_t>(p.Bs + (size_t)g * nw);
-    // wave-uniform (the wave index is), so it can live in SGPRs (readfirstlane
-    // returns int: each half goes through uint32_t, or the low half would
-    // sign-extend into the high one)
-    const uint64_t sbu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32)) << 32) |
-                         (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb);
-    dma16s(vo_s, reinterpret_cast<const char*>(sbu),
-           __builtin_amdgcn_readfirstlane(scl0 + slot * SCL + (sa_wave ? 0 : 2048) + sub_w * 1024));
+    dma16s(vo_s, sbase + (size_t)g * sstride, sm0 + sslot * SCL);
   };
 
   // fragment reads: row lane%32 of each 32-row tile, chunk 2*kk + lane/32 at
@@ -1054,6 +1078,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int j = 0; j < FN; ++j)
       fb[j] = __builtin_bit_cast(i32x4, lds_read16(rB[j & 1][kk] + so + j * 32 * SK));
   };
+  // the same from bases that already hold the stage's slot offset (one add
+  // per base per stage; the tile offsets are immediates)
+  struct Bases {
+    uint32_t a[FM][4], b[2][4];
+  };
+  auto stage_bases = [&](uint32_t so) __attribute__((always_inline)) {
+    Bases t;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) t.a[i][kk] = rA[i][kk] + so;
+      t.b[0][kk] = rB[0][kk] + so;
+      t.b[1][kk] = rB[1][kk] + so;
+    }
+    return t;
+  };
+  auto read_frags_b = [&](const Bases& t, int kk, i32x4 (&fa)[FM], i32x4 (&fb)[FN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[i] = __builtin_bit_cast(i32x4, lds_read16(t.a[i][kk]));
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[j] = __builtin_bit_cast(i32x4, lds_read16(t.b[j & 1][kk] + j * 32 * SK));
+  };
 
   i32x16 iacc[FM][FN];
   f32x16 facc[FM][FN];
@@ -1078,9 +1124,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   // f += float(i) * s_w[col] * s_a[row] with the group's scales from the
   // stage's scale slot (sub = 0: the stage's first group, 1: its last)
-  auto fold = [&](int slot, int sub) __attribute__((always_inline)) {
-    const float* sa_l = reinterpret_cast<const float*>(ring + NST * STAGE + slot * SCL + sub * 1024);
-    const uint16_t* sw_l = reinterpret_cast<const uint16_t*>(ring + NST * STAGE + slot * SCL + 2048 + sub * 1024);
+  auto fold = [&](int sslot, int sub) __attribute__((always_inline)) {
+    const float* sa_l = reinterpret_cast<const float*>(ring + NST * STAGE + sslot * SCL + sub * 1024);
+    const uint16_t* sw_l = reinterpret_cast<const uint16_t*>(ring + NST * STAGE + sslot * SCL + 2048 + sub * 1024);
     float sw[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) sw[j] = bf2f(sw_l[j * 32 + fr]);
@@ -1103,35 +1149,75 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
+  // Three stages in flight.  The barrier that hands a stage over sits in the
+  // last MFMA step of the stage before: once this wave's reads of that step
+  // have landed and the next stage's DMA is complete, the barrier frees the
+  // slot just read for the stage three ahead, and the next stage's first
+  // fragments are read while the step's MFMAs run.  Scale slots are one more
+  // than stages, so a fold after that barrier still finds its group's scales.
+  // The K loop is unrolled over a period of P stages, so folds and group
+  // starts are compile-time and the only branches in it hold no LDS reads
+  // (the compiler's LDS waits then track the prefetch exactly).
   issue(0, 0);
   if (KT > 1) issue(1, 1);
+  if (KT > 2) issue(2, 2);
+  if (KT > 2) {
+    wait_vmcnt<2 * PER>();
+  } else if (KT > 1) {
+    wait_vmcnt<PER>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  __builtin_amdgcn_s_barrier();
   i32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  int ks = 0;   // global MFMA step
-  for (int kt = 0; kt < KT; ++kt) {
-    const int slot = kt % NST;
-    const uint32_t so = (uint32_t)slot * STAGE;
-    if (kt + 1 < KT) {
-      wait_vmcnt<PER>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0): the previous stage fully read
-    __builtin_amdgcn_s_barrier();
-    if (kt + 2 < KT) issue(kt + 2, (kt + 2) % NST);
-    const int glo = group_lo(kt);
-    read_frags(so, 0, fa0, fb0);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      i32x4 (&fa)[FM] = (kk & 1) ? fa1 : fa0;
-      i32x4 (&fb)[FN] = (kk & 1) ? fb1 : fb0;
-      if (kk < 3) {
-        if (kk & 1) read_frags(so, kk + 1, fa0, fb0);
-        else read_frags(so, kk + 1, fa1, fb1);
-      }
-      mfmas(fa, fb, ks % GK == 0);
-      if ((ks + 1) % GK == 0) fold(slot, ks / GK == glo ? 0 : 1);
-      ++ks;
-    }
+  read_frags(0, 0, fa0, fb0);
+  for (int kt0 = 0; kt0 < KT; kt0 += P) {
+    static_for<P>([&](auto U_) __attribute__((always_inline)) {
+      constexpr int U = decltype(U_)::value;
+      const int kt = kt0 + U;
+      const uint32_t so = (uint32_t)(kt % NST) * STAGE;
+      const uint32_t so_next = (uint32_t)((kt + 1) % NST) * STAGE;
+      const int sslot = kt & (NSC - 1);
+      const Bases bs = stage_bases(so);
+      static_for<4>([&](auto KK_) __attribute__((always_inline)) {
+        constexpr int KK = decltype(KK_)::value;
+        constexpr int KS = 4 * U + KK;                 // MFMA step within the period
+        i32x4 (&fa)[FM] = (KK & 1) ? fa1 : fa0;
+        i32x4 (&fb)[FN] = (KK & 1) ? fb1 : fb0;
+        i32x4 (&ga)[FM] = (KK & 1) ? fa0 : fa1;
+        i32x4 (&gb)[FN] = (KK & 1) ? fb0 : fb1;
+        constexpr bool FOLD = (KS + 1) % GK == 0;   // the step ends a group
+        if constexpr (KK < 3) {
+          // a fold inside the stage reads the next fragments after it
+          // (fewer registers live across the fold)
+          if constexpr (!FOLD) read_frags_b(bs, KK + 1, ga, gb);
+        } else {
+          // the next stage (past the last one this reads a slot nobody
+          // writes any more; the values are not used)
+          if (kt + 2 < KT) {
+            wait_vmcnt<PER>();
+          } else {
+            wait_vmcnt<0>();
+          }
+          __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0): this stage fully read
+          __builtin_amdgcn_s_barrier();
+          if (kt + 3 < KT) issue(kt + 3, kt % NST);
+          read_frags(so_next, 0, ga, gb);
+        }
+        mfmas(fa, fb, KS % GK == 0);
+        if constexpr (FOLD) {
+          // the group just finished: its scales sit in this stage's slot,
+          // first (sub 0) if it is the stage's first group
+          constexpr int GREL = KS / GK;                           // group within the period
+          constexpr int GLO = (U * SK) / G;                       // the stage's first group
+          // kept in place: hoisting its scale loads over the MFMAs costs registers
+          __builtin_amdgcn_sched_barrier(0);
+          fold(sslot, GREL == GLO ? 0 : 1);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (KK < 3) read_frags_b(bs, KK + 1, ga, gb);
+        }
+      });
+    });
   }
   __syncthreads();
   if constexpr (EPI == EPI_RESID) {
@@ -1169,7 +1255,16 @@ static hipError_t run_direct(const GemmArgs& a, hipStream_t s) {
 
 template <int EPI, int SEC, int BN>
 static hipError_t run_w8a8g(const GemmArgs& a, hipStream_t s) {
-  gemm_w8a8g_kernel<EPI, SEC, BN><<<grid_for<256, BN>(EPI, a), 512, 0, s>>>(a);
+  const dim3 grid = grid_for<256, BN>(EPI, a);
+  // the K loop runs whole periods of lcm(128, group) elements
+  if (a.K % 128 != 0 || a.K % a.group != 0) return hipErrorInvalidValue;
+  switch (a.group) {
+    case 64: gemm_w8a8g_kernel<EPI, SEC, BN, 64><<<grid, 512, 0, s>>>(a); break;
+    case 256: gemm_w8a8g_kernel<EPI, SEC, BN, 256><<<grid, 512, 0, s>>>(a); break;
+    case 448: gemm_w8a8g_kernel<EPI, SEC, BN, 448><<<grid, 512, 0, s>>>(a); break;
+    case 896: gemm_w8a8g_kernel<EPI, SEC, BN, 896><<<grid, 512, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
