@@ -1175,9 +1175,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     static_for<P>([&](auto U_) __attribute__((always_inline)) {
       constexpr int U = decltype(U_)::value;
       const int kt = kt0 + U;
-      const uint32_t so = (uint32_t)(kt % NST) * STAGE;
-      const uint32_t so_next = (uint32_t)((kt + 1) % NST) * STAGE;
-      const int sslot = kt & (NSC - 1);
+      uint32_t so = (uint32_t)(kt % NST) * STAGE;
+      uint32_t so_next = (uint32_t)((kt + 1) % NST) * STAGE;
+      int sslot = kt & (NSC - 1);
+      // formed here, not hoisted to the top of the period (with two folds per
+      // period the hoisted copies of later stages' offsets spill registers)
+      asm volatile("" : "+s"(so), "+s"(so_next), "+s"(sslot));
       const Bases bs = stage_bases(so);
       static_for<4>([&](auto KK_) __attribute__((always_inline)) {
         constexpr int KK = decltype(KK_)::value;
