@@ -12,8 +12,17 @@ one h3_dit_forward call, which must reproduce the block-by-block result bit for
 bit.  The oracle's 50 blocks at N = 6,437 are about 307 TFLOP of float64 work
 on the host (about ten minutes on 16 cores), so these run only when
 H3_LONG_TESTS=1 is set.
+
+Bounds: the first block is held to the one-block bar and the bf16 model to the
+full-depth bar (3e-2).  The W8A8 trunk at depth is held to twice the spread
+between two oracle forwards whose inputs differ by a relative 1e-7 (float32
+rounding level), measured on the same inputs by tests/golden/w8a8_conditioning.py
+(stored in w8a8_conditioning.json): its int8 codes turn sub-ulp differences
+into whole code steps, so correct implementations drift apart by that much
+along the 50 blocks whatever their arithmetic.
 """
 import dataclasses
+import json
 import os
 
 import numpy as np
@@ -22,7 +31,7 @@ import torch
 
 import oracle
 from joint_video_audio_h3_amd import lib, synth
-from tests.gpu_util import TOL_DEPTH, dev, rel_l2, say
+from tests.gpu_util import TOL_BLOCK, TOL_DEPTH, dev, rel_l2, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(os.environ.get("H3_LONG_TESTS") != "1",
@@ -31,6 +40,23 @@ pytestmark = [pytest.mark.gpu,
 CASES = {"h3_50blk_n6437": synth.WORKLOADS["h3_50blk_n6437"],
          "h3_50blk_n6437_w8a8": synth.WORKLOADS["h3_50blk_n6437_w8a8"],
          "h3_50blk_n1192_w8a8": dataclasses.replace(synth.WORKLOADS["h3_1blk_n1192_w8a8"], n_blocks=50)}
+# the conditioning trace measured on the same inputs
+SPREAD_CASE = {"h3_50blk_n6437_w8a8": "n6437", "h3_50blk_n1192_w8a8": "n1192"}
+COND = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "w8a8_conditioning.json")
+
+
+def depth_bounds(wname):
+    """(bound on x_out, bound on the update) after the last block."""
+    if wname not in SPREAD_CASE:
+        return TOL_DEPTH, 2 * TOL_DEPTH
+    with open(COND) as f:
+        cond = json.load(f)
+    if SPREAD_CASE[wname] not in cond:
+        pytest.skip(f"conditioning of {wname} not measured yet: "
+                    f"python tests/golden/w8a8_conditioning.py {SPREAD_CASE[wname]}")
+    last = cond[SPREAD_CASE[wname]]["w8a8_group896"][-1]
+    assert last["block"] == 50
+    return 2 * last["x"], 2 * last["update"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -44,6 +70,7 @@ def _lib():
 def test_fifty_block_forward_matches_oracle(wname):
     import concurrent.futures as cf
 
+    bx, bu = depth_bounds(wname)
     wl = CASES[wname]
     dims, nb = wl.dims, wl.n_blocks
     say("long depth:", wname, nb, "blocks at N =", wl.n_rows)
@@ -74,7 +101,8 @@ def test_fifty_block_forward_matches_oracle(wname):
     torch.cuda.synchronize()
     assert torch.equal(x2, xd)
     e, du = errs[-1]
-    say("long depth:", wname, "rel-L2 x_out", e, "update", du)
+    say("long depth:", wname, "rel-L2 x_out", e, "update", du, "bounds", bx, bu)
     assert np.isfinite(got).all()
-    assert e < TOL_DEPTH
-    assert du < 2 * TOL_DEPTH
+    assert errs[0][0] < TOL_BLOCK
+    assert e < bx
+    assert du < bu
