@@ -392,7 +392,7 @@ def main():
                     help="with --only-step: first run a 1 GiB device-to-device copy three times, "
                          "the known-size reference for HBM byte counters")
     ap.add_argument("--single-block", type=int, default=1,
-                    help="also time one H3 block at N=1192 with bf16 and INT8 weights (0: skip)")
+                    help="also time one H3 block at N=1192 with bf16 and INT8 weights, and whole INT8 and bf16 blocks at N=1192 and the primary size (0: skip)")
     ap.add_argument("--denoise-reuse", type=int, default=2,
                     help="also time the denoising loop with this whole-velocity reuse (1: skip)")
     ap.add_argument("--denoise-steps", type=int, default=4,
@@ -633,6 +633,31 @@ def main():
             result["single_block"][name] = {"weights": "int8 g32 + bf16 scales" if wl1.dims.wfmt else "bf16",
                                             "per_step_kernels": bd1}
             del t1, b1
+        # whole INT8 W8A16 blocks against bf16 blocks (HIP events): with the full
+        # workspace the forward dequantises each linear's weights once and runs
+        # the bf16 GEMM; with the smaller one, the kernel that dequantises in LDS
+        result["int8_w8a16_block"] = {}
+        d8 = synth.WORKLOADS["h3_1blk_n1192_int8"].dims
+        for wname in ("h3_1blk_n1192", wl.name):
+            wlr = synth.WORKLOADS[wname]
+            rows_ = synth.make_device_rows(wlr, seed=1)
+            r = {"n_rows": wlr.n_rows}
+            for key, dd in (("bf16", wlr.dims), ("int8", d8)):
+                t1, b1 = synth.make_device_weights(dd, 1, seed=0)
+                full = lib.alloc_workspace(dd, wlr.n_rows)
+                wss = {"": full}
+                if dd.wfmt:
+                    wss["_lds_dequant"] = full[:lib.workspace_size(wlr.dims, wlr.n_rows)]
+                for suffix, ws_ in wss.items():
+                    xs = rows_[0].clone()
+                    ms = _time_launches(lambda: lib.dit_block_forward(dd, xs, rows_[1], rows_[2], t1[0], b1[0], ws_),
+                                        args.breakdown_reps, torch)
+                    r[f"{key}{suffix}_block_ms"] = round(ms, 4)
+                del t1, b1, full, wss
+                torch.cuda.empty_cache()
+            r["int8_over_bf16"] = round(r["int8_block_ms"] / r["bf16_block_ms"], 4)
+            result["int8_w8a16_block"][wname] = r
+            del rows_
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(n, wl.n_blocks, dims)

@@ -123,7 +123,14 @@ typedef struct h3_block_weights {
 H3DIT_API int64_t h3_padded_rows(int64_t n_rows);
 
 /* Bytes of scratch a forward over n_rows needs.  Pure: touches no device.
- * Returns 0 if dims or n_rows are invalid (h3_last_error() says why). */
+ * Returns 0 if dims or n_rows are invalid (h3_last_error() says why).
+ * With INT8 weights (H3_W_INT8_G32) this includes one linear's dequantised
+ * bf16 weights (2 * 2 * ffn * hidden bytes, FC1's, the largest: 308 MB at H3
+ * width): the forward then forms each linear's bf16 weights there once and
+ * runs the bf16 GEMM on them.  A workspace that lacks only that buffer is
+ * accepted too, and runs the INT8 GEMMs on the kernel that dequantises the
+ * weights in LDS per row tile (same values, the weights round to
+ * RNE_bf16(q * s) either way). */
 H3DIT_API size_t h3_workspace_size(const h3_dims* dims, int64_t n_rows);
 
 /* One DiT block in place.

@@ -152,6 +152,7 @@ struct Arena {
   uint16_t *h, *q, *k, *vt, *o, *a;
   int8_t* qa;   // W8A8: int8 codes of the activation about to be consumed (h, o, h2 or a)
   float* qs;    // W8A8: its scales [K/G][n_pad]
+  uint16_t* wdq;  // INT8 weights, when the workspace holds it: one linear's bf16 weights at a time
   size_t bytes;
 };
 
@@ -159,8 +160,10 @@ size_t up256(size_t b) { return (b + 255) / 256 * 256; }
 
 // Lifetimes inside a block: cs (whole forward); h (norm1 -> QKV, then norm2 ->
 // FC1); q/k/vt (QKV -> attention); o (attention -> out-proj); a (FC1 -> FC2)
-// reuses the q/k/vt arena, which is dead once attention has run.
-Arena carve(const h3_dims& d, int64_t n, char* base) {
+// reuses the q/k/vt arena, which is dead once attention has run.  With INT8
+// weights and `wdq`, one more buffer takes each linear's dequantised bf16
+// weights just before its GEMM (sized for FC1's, the largest).
+Arena carve(const h3_dims& d, int64_t n, char* base, bool wdq = false) {
   const size_t np = (size_t)pad_rows(n);
   const size_t D = d.hidden, Di = (size_t)d.heads * d.head_dim, F = d.ffn;
   Arena a{};
@@ -190,8 +193,20 @@ Arena carve(const h3_dims& d, int64_t n, char* base) {
     a.qa = reinterpret_cast<int8_t*>(take(np * kmax));
     a.qs = reinterpret_cast<float*>(take(np * ng * 4));
   }
+  if (wdq && d.wfmt == H3_W_INT8_G32) {
+    const size_t wmax = std::max(std::max(3 * Di * D, D * Di), std::max(2 * F * D, D * F));
+    a.wdq = reinterpret_cast<uint16_t*>(take(wmax * 2));
+  }
   a.bytes = off;
   return a;
+}
+
+// The full workspace of a forward: with the dequantised-weight buffer for INT8
+// weights (what h3_workspace_size reports).  A smaller workspace that still
+// holds the rest runs the INT8 GEMMs on the dequantising kernel instead.
+size_t full_arena_bytes(const h3_dims& d, int64_t n) { return carve(d, n, nullptr, true).bytes; }
+Arena carve_ws(const h3_dims& d, int64_t n, void* ws, size_t ws_bytes) {
+  return carve(d, n, static_cast<char*>(ws), ws_bytes >= full_arena_bytes(d, n));
 }
 
 // W8A8 activation buffer of the step entry points: codes [n][K], then the fp32
@@ -264,11 +279,33 @@ void set_w8(const h3_dims& d, h3::GemmArgs& g, const float* sa, int64_t n, bool 
 }
 
 // sa: the W8A8 scales of the int8 activation h (ignored otherwise)
+// INT8 weights with a dequantisation buffer: the layer's bf16 weights are
+// formed there first and the GEMM runs on them as bf16 (wfmt is updated)
+hipError_t predequant(const h3_dims& d, h3::GemmArgs& g, int rows, uint16_t* wdq, int& wfmt,
+                      hipStream_t s) {
+  wfmt = d.wfmt;
+  if (!wdq || d.wfmt != H3_W_INT8_G32) return hipSuccess;
+  h3::DequantArgs a{};
+  a.q = static_cast<const int8_t*>(g.B);
+  a.s = g.Bs;
+  a.out = wdq;
+  a.rows = rows;
+  a.K = g.K;
+  hipError_t e = h3::launch_dequant_w8(a, s);
+  if (e != hipSuccess) return e;
+  g.B = wdq;
+  g.Bs = nullptr;
+  wfmt = H3_W_BF16;
+  return hipSuccess;
+}
+
 hipError_t do_qkv(const h3_dims& d, const uint16_t* h, const h3_block_weights& w, const float* cs,
                   int64_t n, uint16_t* q, uint16_t* k, uint16_t* vt, hipStream_t s,
-                  const float* sa = nullptr) {
+                  const float* sa = nullptr, uint16_t* wdq = nullptr) {
   const int Di = d.heads * d.head_dim;
   h3::GemmArgs g = gemm_base(d, h, w.w_qkv, w.s_qkv, w.b_qkv, (int)n, d.hidden, 3 * Di);
+  int wfmt;
+  if (hipError_t e = predequant(d, g, 3 * Di, wdq, wfmt, s); e != hipSuccess) return e;
   set_w8(d, g, sa, n, false);
   g.q = q;
   g.k = k;
@@ -281,7 +318,7 @@ hipError_t do_qkv(const h3_dims& d, const uint16_t* h, const h3_block_weights& w
   g.cs = cs;
   g.qk_eps = d.qk_eps;
   g.q_scale = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
-  return h3::launch_gemm(h3::EPI_QKV, d.wfmt, g, s);
+  return h3::launch_gemm(h3::EPI_QKV, wfmt, g, s);
 }
 
 // Block-sparse attention selection of one block (null = full attention).
@@ -312,24 +349,28 @@ hipError_t do_attn(const h3_dims& d, const uint16_t* q, const uint16_t* k, const
 
 hipError_t do_resid(const h3_dims& d, const uint16_t* A, const void* W, const uint16_t* S,
                     const uint16_t* b, int K, const uint16_t* table, int kgate, const int32_t* tag,
-                    int64_t n, float* x, hipStream_t s, const float* sa = nullptr) {
+                    int64_t n, float* x, hipStream_t s, const float* sa = nullptr, uint16_t* wdq = nullptr) {
   h3::GemmArgs g = gemm_base(d, A, W, S, b, (int)n, K, d.hidden);
+  int wfmt;
+  if (hipError_t e = predequant(d, g, d.hidden, wdq, wfmt, s); e != hipSuccess) return e;
   set_w8(d, g, sa, n, kgate == 5);
   g.x = x;
   g.ldx = d.hidden;
   g.gate_tab = table + (size_t)kgate * d.hidden;
   g.tag = tag;
   g.tag_stride = 6 * d.hidden;
-  return h3::launch_gemm(h3::EPI_RESID, d.wfmt, g, s);
+  return h3::launch_gemm(h3::EPI_RESID, wfmt, g, s);
 }
 
 hipError_t do_fc1(const h3_dims& d, const uint16_t* h2, const h3_block_weights& w, int64_t n,
-                  uint16_t* a, hipStream_t s, const float* sa = nullptr) {
+                  uint16_t* a, hipStream_t s, const float* sa = nullptr, uint16_t* wdq = nullptr) {
   h3::GemmArgs g = gemm_base(d, h2, w.w_fc1, w.s_fc1, w.b_fc1, (int)n, d.hidden, 2 * d.ffn);
+  int wfmt;
+  if (hipError_t e = predequant(d, g, 2 * d.ffn, wdq, wfmt, s); e != hipSuccess) return e;
   set_w8(d, g, sa, n, false);
   g.out = a;
   g.ffn = d.ffn;
-  return h3::launch_gemm(h3::EPI_SWIGLU, d.wfmt, g, s);
+  return h3::launch_gemm(h3::EPI_SWIGLU, wfmt, g, s);
 }
 
 // W8A8 block: each linear's bf16 input is quantized (per row and scale group)
@@ -369,14 +410,16 @@ h3_status run_block(const h3_dims& d, float* x, const int32_t* tag, const uint16
   const int Di = d.heads * d.head_dim;
   h3_status st;
   if ((st = hip_ok(do_adaln(d, x, tag, table, 0, n, ar.h, s), "adaln (attention)")) != H3_OK) return st;
-  if ((st = hip_ok(do_qkv(d, ar.h, w, ar.cs, n, ar.q, ar.k, ar.vt, s), "qkv+rope")) != H3_OK) return st;
+  if ((st = hip_ok(do_qkv(d, ar.h, w, ar.cs, n, ar.q, ar.k, ar.vt, s, nullptr, ar.wdq), "qkv+rope")) != H3_OK)
+    return st;
   if ((st = hip_ok(do_attn(d, ar.q, ar.k, ar.vt, n, ar.o, s, sp), "attention")) != H3_OK) return st;
-  if ((st = hip_ok(do_resid(d, ar.o, w.w_out, w.s_out, w.b_out, Di, table, 2, tag, n, x, s),
+  if ((st = hip_ok(do_resid(d, ar.o, w.w_out, w.s_out, w.b_out, Di, table, 2, tag, n, x, s, nullptr, ar.wdq),
                    "out-proj+gate")) != H3_OK)
     return st;
   if ((st = hip_ok(do_adaln(d, x, tag, table, 1, n, ar.h, s), "adaln (mlp)")) != H3_OK) return st;
-  if ((st = hip_ok(do_fc1(d, ar.h, w, n, ar.a, s), "fc1+swiglu")) != H3_OK) return st;
-  if ((st = hip_ok(do_resid(d, ar.a, w.w_fc2, w.s_fc2, w.b_fc2, d.ffn, table, 5, tag, n, x, s),
+  if ((st = hip_ok(do_fc1(d, ar.h, w, n, ar.a, s, nullptr, ar.wdq), "fc1+swiglu")) != H3_OK) return st;
+  if ((st = hip_ok(do_resid(d, ar.a, w.w_fc2, w.s_fc2, w.b_fc2, d.ffn, table, 5, tag, n, x, s, nullptr,
+                            ar.wdq),
                    "fc2+gate")) != H3_OK)
     return st;
   return H3_OK;
@@ -633,7 +676,7 @@ h3_status h3_dit_forward_sparse(const h3_dims* dims, float* x, const int32_t* ta
   if ((st = check_device()) != H3_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if ((st = check_tags(*dims, tag, n_rows, s)) != H3_OK) return st;
-  const Arena ar = carve(*dims, n_rows, static_cast<char*>(workspace));
+  const Arena ar = carve_ws(*dims, n_rows, workspace, workspace_bytes);
   if ((st = hip_ok(do_rope(*dims, positions, n_rows, ar.cs, s), "rope table")) != H3_OK) return st;
   const size_t tstride = (size_t)dims->n_tags * 6 * dims->hidden;
   const int64_t nq = (n_rows + tile - 1) / tile;
@@ -681,7 +724,7 @@ h3_status h3_denoise(const h3_dims* dims, const h3_io_dims* io_dims, const h3_io
   if ((st = check_forward_common(dims, x_packed, tag, positions, mod_tables, n, workspace,
                                  workspace_bytes)) != H3_OK)
     return st;
-  const size_t arena = carve(*dims, n, nullptr).bytes;
+  const size_t arena = full_arena_bytes(*dims, n);
   const VelHistory vh = vel_history(*io_dims, sg);
   if (workspace_bytes < arena + vh.bytes)
     return fail(H3_ERR_WORKSPACE, "workspace is %zu bytes, %zu needed (h3_denoise_workspace_size)",
@@ -696,7 +739,7 @@ h3_status h3_denoise(const h3_dims* dims, const h3_io_dims* io_dims, const h3_io
   if ((st = check_device()) != H3_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if ((st = check_tags(*dims, tag, n, s)) != H3_OK) return st;
-  const Arena ar = carve(*dims, n, static_cast<char*>(workspace));
+  const Arena ar = carve(*dims, n, static_cast<char*>(workspace), true);
   char* hist = static_cast<char*>(workspace) + arena;
   float* vel_a[2] = {reinterpret_cast<float*>(hist), reinterpret_cast<float*>(hist + vh.a_bytes)};
   float* vel_v[2] = {reinterpret_cast<float*>(hist + 2 * vh.a_bytes),
@@ -751,7 +794,7 @@ size_t h3_denoise_workspace_size(const h3_dims* dims, const h3_io_dims* io_dims,
                                  const h3_segments* segments) {
   if (check_io(dims, io_dims, segments) != H3_OK) return 0;
   const h3_segments& sg = *segments;
-  return carve(*dims, sg.text + sg.cond + sg.audio + sg.video, nullptr).bytes +
+  return full_arena_bytes(*dims, sg.text + sg.cond + sg.audio + sg.video) +
          vel_history(*io_dims, sg).bytes;
 }
 
@@ -782,7 +825,7 @@ h3_status h3_quantize_groups(const uint16_t* in, int64_t n_rows, int32_t width, 
 
 size_t h3_workspace_size(const h3_dims* dims, int64_t n_rows) {
   if (check_dims(dims) != H3_OK || check_rows(n_rows) != H3_OK) return 0;
-  return carve(*dims, n_rows, nullptr).bytes;
+  return full_arena_bytes(*dims, n_rows);
 }
 
 const char* h3_last_error(void) { return g_err.c_str(); }
@@ -800,7 +843,7 @@ h3_status h3_dit_block_forward(const h3_dims* dims, float* x, const int32_t* tag
   if ((st = check_device()) != H3_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if ((st = check_tags(*dims, tag, n_rows, s)) != H3_OK) return st;
-  const Arena ar = carve(*dims, n_rows, static_cast<char*>(workspace));
+  const Arena ar = carve_ws(*dims, n_rows, workspace, workspace_bytes);
   if ((st = hip_ok(do_rope(*dims, positions, n_rows, ar.cs, s), "rope table")) != H3_OK) return st;
   return run_block(*dims, x, tag, mod_table, *weights, n_rows, ar, s);
 }
@@ -825,7 +868,7 @@ h3_status h3_dit_forward(const h3_dims* dims, float* x, const int32_t* tag, cons
   if ((st = check_device()) != H3_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if ((st = check_tags(*dims, tag, n_rows, s)) != H3_OK) return st;
-  const Arena ar = carve(*dims, n_rows, static_cast<char*>(workspace));
+  const Arena ar = carve_ws(*dims, n_rows, workspace, workspace_bytes);
   if ((st = hip_ok(do_rope(*dims, positions, n_rows, ar.cs, s), "rope table")) != H3_OK) return st;
   const size_t tstride = (size_t)dims->n_tags * 6 * dims->hidden;
   for (int b = 0; b < n_blocks; ++b) {
@@ -1056,7 +1099,7 @@ h3_status h3_velocity_forward(const h3_dims* dims, const h3_io_dims* io_dims,
     return st;
   uint16_t* h = static_cast<uint16_t*>(workspace);
   if (n_blocks > 0) {
-    const Arena ar = carve(*dims, n, static_cast<char*>(workspace));
+    const Arena ar = carve_ws(*dims, n, workspace, workspace_bytes);
     if ((st = hip_ok(do_rope(*dims, positions, n, ar.cs, s), "rope table")) != H3_OK) return st;
     const size_t tstride = (size_t)dims->n_tags * 6 * dims->hidden;
     for (int b = 0; b < n_blocks; ++b) {

@@ -60,6 +60,15 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s);
 
+// bf16 weights [rows][K] = RNE_bf16(q * s) from INT8 group-32 codes and scales
+struct DequantArgs {
+  const int8_t* q;       // [rows][K]
+  const uint16_t* s;     // [rows][K/32] bf16
+  uint16_t* out;         // [rows][K] bf16
+  int rows, K;
+};
+hipError_t launch_dequant_w8(const DequantArgs& a, hipStream_t s);
+
 struct AttnArgs {
   const uint16_t *q, *k, *vt;  // [H][n_pad][d], [H][n_pad][d], [H][d][n_pad]
   uint16_t* o;                 // [n][H*d]

@@ -55,6 +55,25 @@ def test_padded_rows_and_workspace(L):
     assert 3.3e9 < ws < 3.6e9
 
 
+def test_int8_workspace_holds_one_dequantised_linear(L):
+    """INT8 weights: the full workspace adds FC1's bf16 weights (the largest
+    linear) to the bf16 model's arena; a workspace without that buffer is still
+    accepted (the forward then dequantises in LDS), one byte less is not."""
+    n = 1192
+    d8 = synth.WORKLOADS["h3_1blk_n1192_int8"].dims
+    full = lib.workspace_size(d8, n)
+    base = lib.workspace_size(synth.H3_DIMS, n)
+    assert full - base == (2 * 2 * d8.ffn * d8.hidden + 255) // 256 * 256
+    dd = lib.make_dims(d8)
+    w = _full_weights()
+    for f in ("s_qkv", "s_out", "s_fc1", "s_fc2"):
+        setattr(w, f, FAKE)
+    assert _block_call(L, dd, w, n=n, ws_bytes=base - 1) == lib.H3_ERR_WORKSPACE
+    # the workspace checks pass; the call then stops for want of a device here
+    for ws_bytes in (base, full):
+        assert _block_call(L, dd, w, n=n, ws_bytes=ws_bytes) == lib.H3_ERR_NO_DEVICE, lib.last_error()
+
+
 @pytest.mark.parametrize("field,value,code", [
     ("hidden", 300, lib.H3_ERR_UNSUPPORTED),
     ("head_dim", 64, lib.H3_ERR_UNSUPPORTED),
