@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from joint_video_audio_h3_amd import lib, synth
-from tests.gpu_util import (TOL_ATTN, TOL_BF16_OUT, TOL_BLOCK, TOL_RESID_DELTA, dev, host_bf16,
+from tests.gpu_util import (TOL_ATTN, TOL_BF16_OUT, TOL_BLOCK, TOL_DEPTH, TOL_RESID_DELTA, dev, host_bf16,
                             rel_l2, say)
 
 pytestmark = pytest.mark.gpu
@@ -213,3 +213,31 @@ def test_full_depth_properties(wname, fifty_blocks):
     lib.dit_forward(H3, c, tags, pos, t0, blocks, ws)
     torch.cuda.synchronize()
     assert torch.equal(c, x)
+
+
+@pytest.mark.parametrize("wname", ["h3_50blk_n6437", "h3_50blk_n49840"])
+def test_full_depth_permutation_equivariance(wname, fifty_blocks):
+    """The 50-block forward at full size commutes with any permutation of the
+    packed rows taken together with their tags and positions (full attention
+    over the packed sequence, modality only through the per-row tag): the
+    permuted run, put back in order, matches the plain run within the depth
+    bound (the keys' tile order changes the rounding, not the result).  At
+    N = 49,840 no oracle runs 50 blocks; this checks every row of the stack."""
+    wl = synth.WORKLOADS[wname]
+    say("full depth, permuted rows", wname)
+    table, blocks = fifty_blocks
+    x, tags, pos = synth.make_device_rows(wl, seed=5)
+    ws = lib.alloc_workspace(H3, wl.n_rows)
+    perm = torch.from_numpy(np.random.default_rng(9).permutation(wl.n_rows)).cuda()
+    a = x.clone()
+    lib.dit_forward(H3, a, tags, pos, table, blocks, ws)
+    b = x[perm].contiguous()
+    lib.dit_forward(H3, b, tags[perm].contiguous(), pos[perm].contiguous(), table, blocks, ws)
+    torch.cuda.synchronize()
+    back = torch.empty_like(b)
+    back[perm] = b
+    ga, gb, x0 = (t.double().cpu().numpy() for t in (a, back, x))
+    e, du = rel_l2(gb, ga), rel_l2(gb - x0, ga - x0)
+    say("permuted vs plain: rel-L2 x_out", e, "update", du)
+    assert np.isfinite(gb).all()
+    assert e < TOL_DEPTH and du < 2 * TOL_DEPTH
