@@ -405,7 +405,8 @@ def main():
                     help="time just one step kernel (adaln, qkv_rope, attention, out_proj_resid, "
                          "fc1_swiglu, fc2_resid; with a W8A8 workload also quant_h, quant_o, "
                          "quant_a) on one block's weights, e.g. under a counter run; "
-                         "vendor_fc1 times the vendor library's plain GEMM of the FC1 shape")
+                         "vendor_fc1 / vendor_gemms time the vendor library's plain GEMMs of the "
+                         "FC1 / all four linear shapes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -428,25 +429,34 @@ def main():
                 dst.copy_(src)
             torch.cuda.synchronize()
             del src, dst
-        if args.only_step == "vendor_fc1":
-            # the vendor library's plain bf16 GEMM of the FC1 shape (bf16 out, no
-            # epilogue), timed for comparison with the fused FC1 + SwiGLU kernel
-            n, K, N = wl.n_rows, dims.hidden, 2 * dims.ffn
-            a = torch.randn(n, K, dtype=torch.bfloat16, device="cuda")
-            w = torch.randn(N, K, dtype=torch.bfloat16, device="cuda")
-            for _ in range(2):
-                c = a @ w.t()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(True), torch.cuda.Event(True)
-            e0.record()
-            for _ in range(args.breakdown_reps):
-                c = a @ w.t()
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / args.breakdown_reps
-            del c
-            print(json.dumps({"workload": wl.name, "step": "vendor_fc1", "ms": round(ms, 4),
-                              "tflops": round(2.0 * n * K * N / ms / 1e9, 1)}))
+        if args.only_step in ("vendor_fc1", "vendor_gemms"):
+            # the vendor library's plain bf16 GEMMs of the block's linear shapes
+            # (bf16 out, no epilogue), timed for comparison with the fused kernels
+            n, D, Di, F = wl.n_rows, dims.hidden, dims.inner, dims.ffn
+            shapes = {"fc1": (D, 2 * F)}
+            if args.only_step == "vendor_gemms":
+                shapes = {"qkv": (D, 3 * Di), "out_proj": (Di, D), "fc1": (D, 2 * F), "fc2": (F, D)}
+            out = {"workload": wl.name, "step": args.only_step}
+            total = 0.0
+            for name, (K, N) in shapes.items():
+                a = torch.randn(n, K, dtype=torch.bfloat16, device="cuda")
+                w = torch.randn(N, K, dtype=torch.bfloat16, device="cuda")
+                for _ in range(2):
+                    c = a @ w.t()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(True), torch.cuda.Event(True)
+                e0.record()
+                for _ in range(args.breakdown_reps):
+                    c = a @ w.t()
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / args.breakdown_reps
+                total += ms
+                out[name] = {"ms": round(ms, 4), "tflops": round(2.0 * n * K * N / ms / 1e9, 1)}
+                del a, w, c
+            if len(shapes) > 1:
+                out["sum_ms"] = round(total, 4)
+            print(json.dumps(out))
             return
         table, blocks = synth.make_device_weights(dims, 1, seed=0)
         fn = step_breakdown_w8a8 if dims.wfmt == synth.WFMT_W8A8 else step_breakdown

@@ -224,16 +224,12 @@ __device__ __forceinline__ void resid_epilogue_lds(const GemmArgs& p, f32x16 (&a
     const u16x4 bb = *reinterpret_cast<const u16x4*>(p.bias + gcol);
     b4 = make_float4(bf2f(bb[0]), bf2f(bb[1]), bf2f(bb[2]), bf2f(bb[3]));
   }
-  // 32 rows at a time: stage the accumulators, then issue every gate and x load
-  // of the 32 rows before the first store, so the chunk waits for memory once
-  // rather than once per row (the stores could alias the loads otherwise)
+  // 32 rows at a time: issue every gate and x load of the 32 rows, stage the
+  // accumulators while they are in flight, then combine and store, so the
+  // chunk waits for memory once rather than once per row (the stores could
+  // alias the loads otherwise)
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        stage[(8 * (v / 4) + 4 * hl + (v % 4)) * RSTRIDE + j * 32 + lc] = acc[i][j][v];
     float4 xv[16];
     u16x4 gv[16];
 #pragma unroll
@@ -246,6 +242,11 @@ __device__ __forceinline__ void resid_epilogue_lds(const GemmArgs& p, f32x16 (&a
         xv[it] = *reinterpret_cast<const float4*>(p.x + (size_t)row * p.ldx + gcol);
       }
     }
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        stage[(8 * (v / 4) + 4 * hl + (v % 4)) * RSTRIDE + j * 32 + lc] = acc[i][j][v];
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
       const int r = 2 * it + hl;
