@@ -1217,6 +1217,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           // kept in place: hoisting its scale loads over the MFMAs costs registers
           __builtin_amdgcn_sched_barrier(0);
           fold(sslot, GREL == GLO ? 0 : 1);
+          // the folded sums are marked as defined here: otherwise the compiler
+          // sinks a fold inside a stage (groups of 64 or 448) below the next
+          // group's MFMAs, keeping both int32 accumulator sets live (spills)
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(facc[i][j]));
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (KK < 3) read_frags_b(bs, KK + 1, ga, gb);
         }
