@@ -1355,6 +1355,72 @@ static int resid_tile_width(const GemmArgs& a, bool allow128) {
 }
 static bool resid_prefers_192(const GemmArgs& a) { return resid_tile_width(a, false) == 192; }
 
+// Rows of a gated-residual GEMM are independent, so one call may also run as
+// two launches over disjoint row ranges: whole 256-row tiles [0, rows1) at
+// width bn, the rest at 128-wide tiles.  With the same cost model per launch
+// (plus a twentieth of a 256-wide tile for the second launch), this wins when
+// the last wave of the wide tiles would be mostly empty and the remaining rows
+// fill one wave of narrow tiles: at H3 width and 7,461 rows, 24 row tiles at
+// 256 wide make two full waves (504 tiles) and the last 6 row tiles one wave
+// of 252 narrow tiles, against three waves of 256-wide tiles in one launch.
+struct ResidPlan {
+  int bn;      // tile width of the first launch
+  int rows1;   // rows of the first launch (M: no second launch)
+};
+static ResidPlan resid_plan(const GemmArgs& a) {
+  const long tiles_m = (a.M + 255) / 256, cus = device_cus();
+  auto cost = [&](long rt, long bn) {
+    const long tiles = rt * ((a.n_out + bn - 1) / bn);
+    return (tiles + cus - 1) / cus * bn * (bn == 256 ? 100 : bn == 192 ? 105 : 125);
+  };
+  ResidPlan best{resid_tile_width(a, true), a.M};
+  long bc = cost(tiles_m, best.bn);
+  for (int bn : {256, 192}) {
+    for (long r = 1; r < tiles_m; ++r) {
+      const long c = cost(r, bn) + cost(tiles_m - r, 128) + 256 * 100 / 20;
+      if (c < bc) {
+        bc = c;
+        best = {bn, (int)(r * 256)};
+      }
+    }
+  }
+  return best;
+}
+// the call's rows [r0, M) as a call of their own
+static GemmArgs resid_rows_from(const GemmArgs& a, int r0, bool int8_a) {
+  GemmArgs b = a;
+  b.A = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(a.A) +
+                                          (size_t)r0 * a.K * (int8_a ? 1 : 2));
+  b.x = a.x + (size_t)r0 * a.ldx;
+  b.tag = a.tag + r0;
+  if (int8_a) b.sa = a.sa + r0;   // one activation scale per row
+  b.M = a.M - r0;
+  return b;
+}
+// WF: 0 bf16 weights, 1 INT8 W8A16, 2 W8A8 with one scale per row
+template <int WF>
+static hipError_t run_resid_width(int bn, const GemmArgs& a, hipStream_t s) {
+  if constexpr (WF == 1) {
+    if (bn == 128) return run_w8<EPI_RESID, 0, 128>(a, s);
+    if (bn == 192) return run_w8<EPI_RESID, 0, 192>(a, s);
+    return run_w8<EPI_RESID, 0, 256>(a, s);
+  } else {
+    if (bn == 128) return run_direct<EPI_RESID, 0, 128, WF == 2>(a, s);
+    if (bn == 192) return run_direct<EPI_RESID, 0, 192, WF == 2>(a, s);
+    return run_direct<EPI_RESID, 0, 256, WF == 2>(a, s);
+  }
+}
+template <int WF>
+static hipError_t run_resid(const GemmArgs& a, hipStream_t s) {
+  const ResidPlan pl = resid_plan(a);
+  if (pl.rows1 >= a.M) return run_resid_width<WF>(pl.bn, a, s);
+  GemmArgs first = a;
+  first.M = pl.rows1;
+  const hipError_t e = run_resid_width<WF>(pl.bn, first, s);
+  if (e != hipSuccess) return e;
+  return run_resid_width<WF>(128, resid_rows_from(a, pl.rows1, WF == 2), s);
+}
+
 hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
   if (a.K % 64 != 0) return hipErrorInvalidValue;
   if (wfmt != 0 && a.K % 128 != 0) return hipErrorInvalidValue;   // INT8: 128-element stages
@@ -1371,12 +1437,7 @@ hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
   }
   if (wfmt == 2) {   // W8A8 with one scale per row (FC2's per-row form)
     switch (epi) {
-      case EPI_RESID:
-        switch (resid_tile_width(a, true)) {
-          case 128: return run_direct<EPI_RESID, 0, 128, true>(a, s);
-          case 192: return run_direct<EPI_RESID, 0, 192, true>(a, s);
-          default: return run_direct<EPI_RESID, 0, 256, true>(a, s);
-        }
+      case EPI_RESID: return run_resid<2>(a, s);
       case EPI_SWIGLU: return run_direct<EPI_SWIGLU, 0, 256, true>(a, s);
       case EPI_QKV:
         if (a.head_dim == 128) return run_direct<EPI_QKV, 128, 256, true>(a, s);
@@ -1386,12 +1447,7 @@ hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
   }
   if (wfmt == 0) {
     switch (epi) {
-      case EPI_RESID:
-        switch (resid_tile_width(a, true)) {
-          case 128: return run_direct<EPI_RESID, 0, 128>(a, s);
-          case 192: return run_direct<EPI_RESID, 0, 192>(a, s);
-          default: return run_direct<EPI_RESID, 0, 256>(a, s);
-        }
+      case EPI_RESID: return run_resid<0>(a, s);
       case EPI_STORE:
         if (resid_prefers_192(a)) return run_direct<EPI_STORE, 0, 192>(a, s);
         return run_direct<EPI_STORE, 0, 256>(a, s);
@@ -1403,12 +1459,7 @@ hipError_t launch_gemm(int epi, int wfmt, const GemmArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   }
   switch (epi) {   // (EPI_STORE layers have bf16 weights only)
-    case EPI_RESID:
-      switch (resid_tile_width(a, true)) {
-        case 128: return run_w8<EPI_RESID, 0, 128>(a, s);
-        case 192: return run_w8<EPI_RESID, 0, 192>(a, s);
-        default: return run_w8<EPI_RESID, 0, 256>(a, s);
-      }
+    case EPI_RESID: return run_resid<1>(a, s);
     case EPI_SWIGLU: return run_w8<EPI_SWIGLU, 0, 256>(a, s);
     case EPI_QKV:
       if (a.head_dim == 128) return run_w8<EPI_QKV, 128, 256>(a, s);

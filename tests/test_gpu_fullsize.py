@@ -119,9 +119,12 @@ def test_fullsize_attention(n):
         assert rel_l2(got[:, hd * d:(hd + 1) * d], ref) < TOL_ATTN, hd
 
 
-@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("n", SIZES + [7461])
 @pytest.mark.parametrize("which", ["out", "fc2"])
 def test_fullsize_gated_residual(n, which, block_weights):
+    """At 7,461 rows the call runs as two launches (rows [0, 6144) in 256-wide
+    tiles, the rest in 128-wide ones); the sampled rows include both sides of
+    that boundary."""
     say("fullsize residual", which, n)
     host, devw = block_weights
     K = H3.inner if which == "out" else H3.ffn
@@ -134,6 +137,8 @@ def test_fullsize_gated_residual(n, which, block_weights):
     fn(H3, a.view(torch.int16), devw, dev(table), dev(tags), x)
     torch.cuda.synchronize()
     rows = _rows(n, 16, seed=2)
+    if n > 6144:
+        rows = np.unique(np.concatenate([rows, [6143, 6144]]))
     ridx = torch.from_numpy(rows).cuda()
     got = (x[ridx] - x0[ridx]).cpu().numpy().astype(np.float64)
     name = "out" if which == "out" else "fc2"
@@ -157,7 +162,7 @@ def test_fullsize_fc1_swiglu(n, block_weights):
     assert rel_l2(host_bf16(a[ridx]), oracle.swiglu(z, H3.ffn)) < TOL_BF16_OUT
 
 
-@pytest.mark.parametrize("wname", ["h3_50blk_n6437", "h3_50blk_n49840"])
+@pytest.mark.parametrize("wname", ["h3_50blk_n6437", "h3_50blk_n7461", "h3_50blk_n49840"])
 def test_fullsize_block_sampled_rows(wname, block_weights):
     """One whole block at the 50-block workloads' packed layouts (N = 6,437 and
     N = 49,840), compared on sampled output rows; keys and values use every row

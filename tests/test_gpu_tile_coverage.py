@@ -6,7 +6,8 @@ whole group (8 x 8 row tiles when K < 7168, 8 x 4 when K >= 7168).  At these
 row counts both regions are present for both group sizes, or only the
 remainder: 49,840 (195 row tiles), 16,640 (65) and 8,449 (34, the last holding
 one row); at 1,192 (5 row tiles) the gated-residual GEMMs take 128-wide
-column tiles.  All three weight formats run: bf16 (the direct-to-LDS kernel),
+column tiles, and at 7,461 and 16,640 rows they run as two launches (the
+first 24 or 59 row tiles at 256 wide, the rest at 128 wide).  All three weight formats run: bf16 (the direct-to-LDS kernel),
 INT8 group-32 (the dequantising kernel, with its own wave layout) and
 group-scaled W8A8 (eight 32 x 128 wave tiles, its own K loop; its inputs are
 the activations' group-896 int8 codes and scales).  Outputs start as NaN (bf16 and q/k/v^T) and every element must
@@ -24,7 +25,7 @@ pytestmark = pytest.mark.gpu
 H3 = synth.H3_DIMS
 INT8_H3 = synth.WORKLOADS["h3_1blk_n1192_int8"].dims   # INT8 group-32 weights, own kernel
 W8A8_H3 = synth.H3_W8A8_DIMS                            # group-scaled W8A8, own kernel
-SIZES = [1192, 8449, 16640, 49840]
+SIZES = [1192, 7461, 8449, 16640, 49840]
 FORMATS = {"bf16": H3, "int8": INT8_H3, "w8a8": W8A8_H3}
 BF16_NAN = 0x7FC0
 
