@@ -5,6 +5,12 @@
 // packed sequence; "Performance": flash-style, the score matrix is never
 // materialised).
 //
+// Two dense kernels share one design.  attn48_kernel (head_dim 128, the H3
+// width) gives each wavefront 48 queries on 16x16x32 MFMAs, so every K or V^T
+// fragment read from LDS feeds three MFMAs; it is described at its definition.
+// attn_kernel (head_dim 96, and the block-sparse variant below) is described
+// here.
+//
 // Work split: a block of 8 wavefronts takes 256 queries of one head; each
 // wavefront owns 32 queries and walks all keys in tiles of 64, processed as
 // two 32-key halves.  Blocks are dealt round-robin to the 8 XCDs; when the
@@ -77,6 +83,18 @@ __device__ __forceinline__ void att_wait_vmcnt() {
 }
 template <int V>
 using att_ic = std::integral_constant<int, V>;
+// f(att_ic<0>), ..., f(att_ic<N-1>) in order, each index a compile-time constant
+template <int I, int N, class F>
+__device__ __forceinline__ void att_static_for_from(F&& f) {
+  if constexpr (I < N) {
+    f(att_ic<I>{});
+    att_static_for_from<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void att_static_for(F&& f) {
+  att_static_for_from<0, N>(f);
+}
 
 constexpr int ATT_WAVES = 8;            // wavefronts per block, 32 queries each (dense)
 constexpr int ATT_BQ = ATT_WAVES * 32;  // queries per block (256, dense)
@@ -413,10 +431,308 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
 }
 
+// ============================================================ dense, head_dim 128: 48 queries per wave
+// The same ring, DMA, XCD mapping and lazy-rescale softmax as attn_kernel, on
+// v_mfma_f32_16x16x32_bf16 with 48 queries (three groups of 16) per wavefront:
+// every K or V^T fragment read from LDS feeds three MFMAs, one per query group,
+// so a key costs two thirds of the LDS reads it costs with one 32-query group
+// per fragment, at about the same register count (two waves per SIMD).
+//   A (16 x 32): lane l holds row l%16, k elements 8*(l/16) .. +7
+//   B (32 x 16): lane l holds column l%16, k elements 8*(l/16) .. +7
+//   D (16 x 16): lane l holds rows 4*(l/16) .. +3 of column l%16
+// Scores are S^T = K Q^T in 16-key slices: A = K rows, B = Q^T of a group.  A
+// 32-key half is two slices, and slice j's A row r reads key
+// 8*(r/4) + 4*j + r%4, so the lane holding D rows 4g .. 4g+3 of both slices
+// holds keys 8g .. 8g+7 of its query: exactly the k elements of P^T that the
+// product O^T += V^T P^T takes as its B operand, with V^T's A fragment reading
+// keys 8*(l/16) .. +7.  Each query's softmax state lives in the four lanes
+// l%16 of its group and is kept equal in them.
+constexpr int A48_QW = 48;                   // queries per wavefront
+constexpr int A48_WAVES = 8;
+constexpr int A48_BQ = A48_WAVES * A48_QW;   // queries per block
+
+__device__ __forceinline__ f32x4 a48_mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// key (within a 32-key half) read by A row r of score slice j
+__device__ __forceinline__ int a48_krow(int j, int r) { return 8 * (r >> 2) + 4 * j + (r & 3); }
+// K rows: chunk c at position c ^ a48_kswz(row).  The eight rows one 8-lane
+// group of a fragment read touches differ in (row & 3) and bit 3, which this
+// maps to eight distinct positions modulo 8 (distinct banks).
+__device__ __forceinline__ int a48_kswz(int r) { return (r & 3) | ((r >> 1) & 4); }
+// V^T rows (64 keys = 8 chunks): chunk c at position c ^ (row & 7)
+__device__ __forceinline__ int a48_vswz(int r) { return r & 7; }
+
+__global__ __launch_bounds__(A48_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn48_kernel(
+    AttnArgs p) {
+  constexpr int HD = 128, W = A48_WAVES, SLOTS = 4;
+  constexpr int DC = HD / 32;              // 32-wide d chunks (score product k steps)
+  constexpr int DT = HD / 16;              // 16-row d tiles of O^T
+  constexpr int NG = A48_QW / 16;          // query groups per wave
+  constexpr int KROW = 256, VROW = ATT_BKV * 2;
+  constexpr int KBYTES = ATT_BKV * KROW, VBYTES = HD * VROW, STAGE = KBYTES + VBYTES;
+  constexpr int NK = KBYTES / 1024, NV = VBYTES / 1024;
+  constexpr int NIK = NK / W, NI = (NK + NV) / W;
+  static_assert(NK % W == 0 && NV % W == 0, "loads split evenly over the waves");
+  // the K tiles of all slots fill the first 64 KB of the ring and the V^T tiles
+  // the second, so every fragment read is a per-lane base plus an immediate
+  // below 64 KB; a slot's K and V^T tiles sit at the same offset in their halves
+  static_assert(KBYTES == 16384 && VBYTES == 16384 && SLOTS * KBYTES == 65536, "ring halves");
+  __shared__ __attribute__((aligned(1024))) char ring[SLOTS * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int qb = blockIdx.x, head = blockIdx.y;
+  if (gridDim.y % 8 == 0) {   // XCD x runs whole heads x, x+8, ... (as attn_kernel)
+    const int id = blockIdx.x + gridDim.x * blockIdx.y;
+    const int local = id / 8;
+    qb = local % gridDim.x;
+    head = id % 8 + 8 * (local / gridDim.x);
+  }
+  const int q0 = qb * A48_BQ + wave * A48_QW;
+  const int lr = lane & 15, lg = lane >> 4;
+  const size_t hoff = (size_t)head * p.n_pad * HD;
+
+  // Q^T fragments (B operand): query q0 + 16*gr + lr, channels 32*dc + 8*lg .. +7
+  // (rows past n_pad, in the last block, read row n_pad - 1; their outputs are not stored)
+  bf16x8 qf[DC][NG];
+#pragma unroll
+  for (int gr = 0; gr < NG; ++gr) {
+    const uint16_t* qp = p.q + hoff + (size_t)min(q0 + 16 * gr + lr, p.n_pad - 1) * HD + 8 * lg;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) qf[dc][gr] = *reinterpret_cast<const bf16x8*>(qp + 32 * dc);
+  }
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0): see attn_kernel
+
+  // DMA: K load j fills rows 4j .. 4j+3 (lane -> row l/16, position l%16 holding
+  // chunk (l%16) ^ kswz(row)); V^T load j fills d rows 8j .. 8j+7 (lane -> row
+  // l/8, position l%8 holding key chunk (l%8) ^ vswz(row))
+  const char* kbase0 = reinterpret_cast<const char*>(p.k + hoff);
+  const char* vbase0 = reinterpret_cast<const char*>(p.vt + (size_t)head * HD * p.n_pad);
+  const uint32_t ring0 = att_lds_addr(ring);
+  uint32_t dvo[NI], dm[NI];
+#pragma unroll
+  for (int s = 0; s < NI; ++s) {
+    const int j = wave + W * s;
+    if (s < NIK) {
+      const int r = 4 * j + lane / 16;
+      dvo[s] = (uint32_t)(r * HD + ((lane & 15) ^ a48_kswz(r)) * 8) * 2;
+      dm[s] = __builtin_amdgcn_readfirstlane(ring0 + j * 1024);
+    } else {
+      const int jv = j - NK;
+      const int r = 8 * jv + lane / 8;
+      dvo[s] = (uint32_t)r * (uint32_t)p.n_pad * 2 + (uint32_t)(((lane & 7) ^ a48_vswz(r)) * 16);
+      dm[s] = __builtin_amdgcn_readfirstlane(ring0 + 65536 + jv * 1024);
+    }
+  }
+  auto issue = [&](int kt, uint32_t slot_off) __attribute__((always_inline)) {
+    const char* kb = kbase0 + (size_t)kt * (ATT_BKV * HD * 2);
+    const char* vb = vbase0 + (size_t)kt * (ATT_BKV * 2);
+#pragma unroll
+    for (int s = 0; s < NI; ++s) att_dma16s(dvo[s], s < NIK ? kb : vb, dm[s] + slot_off);
+  };
+
+  // fragment read bases: K for slice j and d chunk dc, V^T for half h; the
+  // slot, the half's key offset (K) and the d tile (V^T) are immediates
+  uint32_t kbr[2][DC], vbr[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = a48_krow(j, lr);
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) kbr[j][dc] = ring0 + r * KROW + (((4 * dc + lg) ^ a48_kswz(r)) * 16);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) vbr[h] = ring0 + 65536 + lr * VROW + (((4 * h + lg) ^ a48_vswz(lr)) * 16);
+  // fragment u of a tile in the slot at offset SO (of each half of the ring):
+  // u = 16h + f, f < 8 the K fragment of slice f/4, chunk f%4 of half h; f >= 8
+  // the V^T fragment of d tile f-8 of half h
+  auto fread = [&](auto SO_, auto U_) __attribute__((always_inline)) {
+    constexpr int SO = decltype(SO_)::value, U = decltype(U_)::value;
+    constexpr int H = U / 16, F = U % 16;
+    if constexpr (F < 8) return att_read16(kbr[F / 4][F % 4] + (SO + H * 32 * KROW));
+    else return att_read16(vbr[H] + (SO + (F - 8) * 16 * VROW));
+  };
+  auto fread_rt = [&](uint32_t so, auto U_) __attribute__((always_inline)) {
+    constexpr int U = decltype(U_)::value;
+    constexpr int H = U / 16, F = U % 16;
+    if constexpr (F < 8) return att_read16(kbr[F / 4][F % 4] + so + H * 32 * KROW);
+    else return att_read16(vbr[H] + so + (F - 8) * 16 * VROW);
+  };
+
+  f32x4 oacc[DT][NG];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int gr = 0; gr < NG; ++gr) oacc[t][gr] = f32x4{};
+  float m_ref[NG], l_run[NG];
+#pragma unroll
+  for (int gr = 0; gr < NG; ++gr) m_ref[gr] = l_run[gr] = 0.f;
+  const att_bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const int KT = (p.n + ATT_BKV - 1) / ATT_BKV;
+
+  // p = exp2(s) for a group's 8 scores (slice j, row i -> k element 4j + i) as
+  // bf16 and the sum of those bf16 values
+  auto probs = [&](const f32x4 (&s)[2], bf16x8& pf) __attribute__((always_inline)) {
+    float rs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const att_bf16x2 pr = {(__bf16)__builtin_amdgcn_exp2f(s[j][i]), (__bf16)__builtin_amdgcn_exp2f(s[j][i + 1])};
+        pf[4 * j + i] = pr[0];
+        pf[4 * j + i + 1] = pr[1];
+        rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+      }
+    return rs;
+  };
+  // the half's softmax (scores sc[gr][j], already relative to m_ref): the
+  // probabilities into pf, the running sums updated; rarely (some lane's 8
+  // probabilities of a group sum above 2^8, or the first half) the half's
+  // maximum of each query is formed, m_ref raised, O and the sum rescaled
+  auto softmax = [&](f32x4 (&sc)[NG][2], bf16x8 (&pf)[NG], bool first) __attribute__((always_inline)) {
+    float rs[NG];
+    bool big = false;
+#pragma unroll
+    for (int gr = 0; gr < NG; ++gr) {
+      rs[gr] = probs(sc[gr], pf[gr]);
+      big |= !(rs[gr] <= ATT_RESCALE_SUM);
+    }
+    if (first || __builtin_amdgcn_ballot_w64(big) != 0) {
+#pragma unroll
+      for (int gr = 0; gr < NG; ++gr) {
+        float mx = sc[gr][0][0];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[gr][j][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float sh = first ? mx : fmaxf(mx, 0.f);
+        m_ref[gr] += sh;
+        if (!first) {   // (first: O and the sum are still zero)
+          const float alpha = __builtin_amdgcn_exp2f(-sh);
+          l_run[gr] *= alpha;
+#pragma unroll
+          for (int t = 0; t < DT; ++t) oacc[t][gr] *= alpha;
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[gr][j][i] -= sh;
+        rs[gr] = probs(sc[gr], pf[gr]);
+      }
+    }
+#pragma unroll
+    for (int gr = 0; gr < NG; ++gr) l_run[gr] += rs[gr];
+  };
+
+  // One tile: per 32-key half, the score product (8 K fragments x 3 query
+  // groups), its softmax, then O^T += V^T P^T (8 V^T fragments x 3 groups).
+  // Fragment reads run PD fragments ahead of their MFMAs.
+  constexpr int PD = 3;
+  auto tile_body = [&](auto&& rd, int kt, bool masked, bool first) __attribute__((always_inline)) {
+    bf16x8 fr[PD + 1];
+    f32x4 sc[NG][2];
+    bf16x8 pf[NG];
+    att_static_for<PD>([&](auto U_) __attribute__((always_inline)) {
+      constexpr int U = decltype(U_)::value;
+      fr[U] = rd(att_ic<U>{});
+    });
+    att_static_for<32>([&](auto U_) __attribute__((always_inline)) {
+      constexpr int U = decltype(U_)::value;
+      constexpr int H = U / 16, F = U % 16;
+      if constexpr (F == 0) {
+#pragma unroll
+        for (int gr = 0; gr < NG; ++gr)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) sc[gr][j] = f32x4{-m_ref[gr], -m_ref[gr], -m_ref[gr], -m_ref[gr]};
+      }
+      if constexpr (F == 8) {
+        if (masked) {   // only the last tile holds keys >= n
+          const int key0 = kt * ATT_BKV + 32 * H + 8 * lg;
+#pragma unroll
+          for (int gr = 0; gr < NG; ++gr)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (key0 + 4 * j + i >= p.n) sc[gr][j][i] = -INFINITY;
+        }
+        softmax(sc, pf, first && H == 0);
+      }
+      if constexpr (U + PD < 32) fr[(U + PD) % (PD + 1)] = rd(att_ic<U + PD>{});
+      const bf16x8& a = fr[U % (PD + 1)];
+      if constexpr (F < 8) {
+#pragma unroll
+        for (int gr = 0; gr < NG; ++gr) sc[gr][F / 4] = a48_mfma(a, qf[F % 4][gr], sc[gr][F / 4]);
+      } else {
+#pragma unroll
+        for (int gr = 0; gr < NG; ++gr) oacc[F - 8][gr] = a48_mfma(a, pf[gr], oacc[F - 8][gr]);
+      }
+    });
+  };
+
+  auto wait_tiles = [&](auto T_) __attribute__((always_inline)) { att_wait_vmcnt<decltype(T_)::value * NI>(); };
+  // steady tile with compile-time slot U (as attn_kernel)
+  auto tile_c = [&](auto U_, int kt) __attribute__((always_inline)) {
+    constexpr int U = decltype(U_)::value;
+    constexpr int SO = U * KBYTES;
+    wait_tiles(att_ic<2>{});
+    __builtin_amdgcn_s_barrier();
+    issue(kt + 3, (uint32_t)(((U + 3) % SLOTS) * KBYTES));
+    tile_body([&](auto F_) __attribute__((always_inline)) { return fread(att_ic<SO>{}, F_); }, kt, false, kt == 0);
+  };
+  auto tile_r = [&](int kt) __attribute__((always_inline)) {
+    const uint32_t so = (uint32_t)((kt % SLOTS) * KBYTES);
+    if (kt + 2 < KT) {
+      wait_tiles(att_ic<2>{});
+    } else if (kt + 1 < KT) {
+      wait_tiles(att_ic<1>{});
+    } else {
+      att_wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (kt + 3 < KT) issue(kt + 3, (uint32_t)(((kt + 3) % SLOTS) * KBYTES));
+    tile_body([&](auto F_) __attribute__((always_inline)) { return fread_rt(so, F_); }, kt, kt + 1 == KT, kt == 0);
+  };
+
+  issue(0, 0);
+  if (KT > 1) issue(1, KBYTES);
+  if (KT > 2) issue(2, 2 * KBYTES);
+  int kt = 0;
+  for (; kt + 7 <= KT; kt += 4) {
+    tile_c(att_ic<0>{}, kt);
+    tile_c(att_ic<1>{}, kt + 1);
+    tile_c(att_ic<2>{}, kt + 2);
+    tile_c(att_ic<3>{}, kt + 3);
+  }
+  for (; kt < KT; ++kt) tile_r(kt);
+
+#pragma unroll
+  for (int gr = 0; gr < NG; ++gr) {
+    float lsum = l_run[gr] + __shfl_xor(l_run[gr], 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    const int qrow = q0 + 16 * gr + lr;
+    if (qrow < p.n) {
+      uint16_t* op = p.o + (size_t)qrow * p.heads * HD + head * HD + 4 * lg;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const f32x4& a = oacc[t][gr];
+        *reinterpret_cast<uint2*>(op + 16 * t) =
+            make_uint2(pack2bf(a[0] * inv, a[1] * inv), pack2bf(a[2] * inv, a[3] * inv));
+      }
+    }
+  }
+}
+
 template <int HD>
 static hipError_t launch_hd(const AttnArgs& a, hipStream_t s) {
   if (!a.tile_idx) {
-    attn_kernel<HD, ATT_WAVES, false><<<dim3((a.n + ATT_BQ - 1) / ATT_BQ, a.heads), ATT_WAVES * 64, 0, s>>>(a);
+    if constexpr (HD == 128) {
+      attn48_kernel<<<dim3((a.n + A48_BQ - 1) / A48_BQ, a.heads), A48_WAVES * 64, 0, s>>>(a);
+    } else {
+      attn_kernel<HD, ATT_WAVES, false><<<dim3((a.n + ATT_BQ - 1) / ATT_BQ, a.heads), ATT_WAVES * 64, 0, s>>>(a);
+    }
   } else if (a.tile == 128) {
     attn_kernel<HD, 4, true><<<dim3((a.n + 127) / 128, a.heads), 256, 0, s>>>(a);
   } else if (a.tile == 64) {

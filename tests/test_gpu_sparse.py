@@ -3,7 +3,10 @@
 Generator masks (fixed budget per query tile, dense prefix queries, prefix keys
 kept) with both tile sizes, ragged row counts, shuffled lists, an empty list
 and out-of-range indices; a selection of every tile in order must reproduce the
-dense kernel bit for bit; a 2-block sparse forward against the oracle; and the
+dense kernel bit for bit where the two share their per-wave arithmetic (head_dim
+96), and agree with it to rounding at head_dim 128, where the dense kernel runs
+48 queries per wave on 16 x 16 x 32 MFMAs; a 2-block sparse forward against the
+oracle; and the
 N = 49,840 geometry (56 heads, tile 128, an eighth of the key tiles) on sampled
 (head, query tile) pairs.
 """
@@ -89,7 +92,7 @@ def test_empty_and_out_of_range_lists():
 
 @pytest.mark.parametrize("dims,n,tile", [(synth.TINY_DIMS, 300, 64), (synth.H3_DIMS, 1192, 128)],
                          ids=["tiny-T64", "h3-T128"])
-def test_every_tile_in_order_equals_dense_kernel_bitwise(dims, n, tile):
+def test_every_tile_in_order_equals_dense_kernel(dims, n, tile):
     say("sparse all tiles == dense", n, tile)
     q, k, v, qd, kd, vtd = _inputs(dims, n, seed=23)
     off, idx = synth.make_tile_mask(n, dims.heads, tile, 1.0, seed=23)
@@ -97,7 +100,10 @@ def test_every_tile_in_order_equals_dense_kernel_bitwise(dims, n, tile):
     dense = torch.empty_like(got)
     lib.attention(dims, qd, kd, vtd, n, dense)
     torch.cuda.synchronize()
-    assert torch.equal(got, dense)
+    if dims.head_dim != 128:
+        assert torch.equal(got, dense)
+    else:   # same keys, same values, another summation order and probability rounding
+        assert rel_l2(host_bf16(got), host_bf16(dense).astype(np.float64)) < TOL_ATTN
 
 
 def test_sparse_forward_two_blocks_matches_oracle():
