@@ -456,12 +456,17 @@ __device__ __forceinline__ f32x4 a48_mfma(const bf16x8& a, const bf16x8& b, cons
 }
 // key (within a 32-key half) read by A row r of score slice j
 __device__ __forceinline__ int a48_krow(int j, int r) { return 8 * (r >> 2) + 4 * j + (r & 3); }
-// K rows: chunk c at position c ^ a48_kswz(row).  The eight rows one 8-lane
-// group of a fragment read touches differ in (row & 3) and bit 3, which this
-// maps to eight distinct positions modulo 8 (distinct banks).
-__device__ __forceinline__ int a48_kswz(int r) { return (r & 3) | ((r >> 1) & 4); }
-// V^T rows (64 keys = 8 chunks): chunk c at position c ^ (row & 7)
-__device__ __forceinline__ int a48_vswz(int r) { return r & 7; }
+// A 16-byte LDS read takes 16 lanes (256 bytes, all 64 banks) per cycle, so
+// each 16-lane group of a fragment read must touch 16 distinct 16-byte bank
+// groups (and, then, each 8-lane half 8 distinct ones modulo 8).
+// K rows (256 bytes = 16 chunks): chunk c at position c ^ a48_kswz(row).  The
+// 16 rows of a fragment's 16 lanes differ in bits 0, 1, 3 and 4, which this
+// maps to 16 distinct positions.
+__device__ __forceinline__ int a48_kswz(int r) { return (r & 3) | ((r >> 1) & 12); }
+// V^T rows (64 keys = 8 chunks, two rows per 256 bytes): chunk c at position
+// c ^ a48_vswz(row); 16 consecutive rows land on 16 distinct bank groups, and 8
+// consecutive rows on 8 distinct positions.
+__device__ __forceinline__ int a48_vswz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 
 __global__ __launch_bounds__(A48_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn48_kernel(
     AttnArgs p) {
