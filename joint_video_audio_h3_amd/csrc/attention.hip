@@ -536,14 +536,14 @@ __global__ __launch_bounds__(A48_WAVES * 64) __attribute__((amdgpu_waves_per_eu(
     for (int s = 0; s < NI; ++s) att_dma16s(dvo[s], s < NIK ? kb : vb, dm[s] + slot_off);
   };
 
-  // fragment read bases: K for slice j and d chunk dc, V^T for half h; the
-  // slot, the half's key offset (K) and the d tile (V^T) are immediates
-  uint32_t kbr[2][DC], vbr[2];
+  // fragment read bases: K for d chunk dc, V^T for half h; the slot, the half's
+  // key offset, the slice (its rows are slice 0's plus 4, with the same
+  // swizzle: a48_krow(0, r) has bit 2 clear) and the d tile are immediates
+  uint32_t kbr[DC], vbr[2];
+  {
+    const int r = a48_krow(0, lr);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = a48_krow(j, lr);
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) kbr[j][dc] = ring0 + r * KROW + (((4 * dc + lg) ^ a48_kswz(r)) * 16);
+    for (int dc = 0; dc < DC; ++dc) kbr[dc] = ring0 + r * KROW + (((4 * dc + lg) ^ a48_kswz(r)) * 16);
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) vbr[h] = ring0 + 65536 + lr * VROW + (((4 * h + lg) ^ a48_vswz(lr)) * 16);
@@ -553,13 +553,13 @@ __global__ __launch_bounds__(A48_WAVES * 64) __attribute__((amdgpu_waves_per_eu(
   auto fread = [&](auto SO_, auto U_) __attribute__((always_inline)) {
     constexpr int SO = decltype(SO_)::value, U = decltype(U_)::value;
     constexpr int H = U / 16, F = U % 16;
-    if constexpr (F < 8) return att_read16(kbr[F / 4][F % 4] + (SO + H * 32 * KROW));
+    if constexpr (F < 8) return att_read16(kbr[F % 4] + (SO + H * 32 * KROW + (F / 4) * 4 * KROW));
     else return att_read16(vbr[H] + (SO + (F - 8) * 16 * VROW));
   };
   auto fread_rt = [&](uint32_t so, auto U_) __attribute__((always_inline)) {
     constexpr int U = decltype(U_)::value;
     constexpr int H = U / 16, F = U % 16;
-    if constexpr (F < 8) return att_read16(kbr[F / 4][F % 4] + so + H * 32 * KROW);
+    if constexpr (F < 8) return att_read16(kbr[F % 4] + so + (H * 32 * KROW + (F / 4) * 4 * KROW));
     else return att_read16(vbr[H] + so + (F - 8) * 16 * VROW);
   };
 
@@ -568,9 +568,16 @@ __global__ __launch_bounds__(A48_WAVES * 64) __attribute__((amdgpu_waves_per_eu(
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int gr = 0; gr < NG; ++gr) oacc[t][gr] = f32x4{};
-  float m_ref[NG], l_run[NG];
+  // -m of each query (its reference point, replicated in a 4-register tuple):
+  // the C operand of the first MFMA of every score slice, so scores come out
+  // relative to m with no per-half initialisation
+  f32x4 mneg[NG];
+  float l_run[NG];
 #pragma unroll
-  for (int gr = 0; gr < NG; ++gr) m_ref[gr] = l_run[gr] = 0.f;
+  for (int gr = 0; gr < NG; ++gr) {
+    mneg[gr] = f32x4{};
+    l_run[gr] = 0.f;
+  }
   const att_bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const int KT = (p.n + ATT_BKV - 1) / ATT_BKV;
 
@@ -589,10 +596,10 @@ __global__ __launch_bounds__(A48_WAVES * 64) __attribute__((amdgpu_waves_per_eu(
       }
     return rs;
   };
-  // the half's softmax (scores sc[gr][j], already relative to m_ref): the
+  // the half's softmax (scores sc[gr][j], already relative to m): the
   // probabilities into pf, the running sums updated; rarely (some lane's 8
   // probabilities of a group sum above 2^8, or the first half) the half's
-  // maximum of each query is formed, m_ref raised, O and the sum rescaled
+  // maximum of each query is formed, m raised, O and the sum rescaled
   auto softmax = [&](f32x4 (&sc)[NG][2], bf16x8 (&pf)[NG], bool first) __attribute__((always_inline)) {
     float rs[NG];
     bool big = false;
@@ -612,7 +619,7 @@ __global__ __launch_bounds__(A48_WAVES * 64) __attribute__((amdgpu_waves_per_eu(
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float sh = first ? mx : fmaxf(mx, 0.f);
-        m_ref[gr] += sh;
+        mneg[gr] -= sh;
         if (!first) {   // (first: O and the sum are still zero)
           const float alpha = __builtin_amdgcn_exp2f(-sh);
           l_run[gr] *= alpha;
@@ -645,12 +652,6 @@ __global__ __launch_bounds__(A48_WAVES * 64) __attribute__((amdgpu_waves_per_eu(
     att_static_for<32>([&](auto U_) __attribute__((always_inline)) {
       constexpr int U = decltype(U_)::value;
       constexpr int H = U / 16, F = U % 16;
-      if constexpr (F == 0) {
-#pragma unroll
-        for (int gr = 0; gr < NG; ++gr)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) sc[gr][j] = f32x4{-m_ref[gr], -m_ref[gr], -m_ref[gr], -m_ref[gr]};
-      }
       if constexpr (F == 8) {
         if (masked) {   // only the last tile holds keys >= n
           const int key0 = kt * ATT_BKV + 32 * H + 8 * lg;
@@ -668,7 +669,8 @@ __global__ __launch_bounds__(A48_WAVES * 64) __attribute__((amdgpu_waves_per_eu(
       const bf16x8& a = fr[U % (PD + 1)];
       if constexpr (F < 8) {
 #pragma unroll
-        for (int gr = 0; gr < NG; ++gr) sc[gr][F / 4] = a48_mfma(a, qf[F % 4][gr], sc[gr][F / 4]);
+        for (int gr = 0; gr < NG; ++gr)
+          sc[gr][F / 4] = a48_mfma(a, qf[F % 4][gr], F % 4 == 0 ? mneg[gr] : sc[gr][F / 4]);
       } else {
 #pragma unroll
         for (int gr = 0; gr < NG; ++gr) oacc[F - 8][gr] = a48_mfma(a, pf[gr], oacc[F - 8][gr]);
