@@ -40,6 +40,16 @@
  *     the stream, so not under stream capture; check-mode calls that overlap
  *     on one device share the counter) and returns H3_ERR_INVALID_ARG, with
  *     nothing else enqueued, if any lies outside that range.
+ *   - H3_UNFUSED=1 in the environment (a debugging switch, read at every
+ *     call): the block forwards with bf16 weights run each GEMM with a plain
+ *     fp32 store of acc + bias and its epilogue (QK-RMSNorm + RoPE + q scale +
+ *     head-major scatter, SwiGLU, gated residual) as a separate elementwise
+ *     kernel, to compare the fused epilogues against (the pages keep unfused
+ *     two-kernel versions of their fused kernels switchable in the same way:
+ *     H3-metal digest, "Exact DiT fusions").  h3_workspace_size then adds one
+ *     fp32 buffer of n_pad x max(3 * heads * head_dim, 2 * ffn, hidden), so
+ *     the switch must be the same when a workspace is sized and when it is
+ *     used.  Other weight formats and the step entry points ignore it.
  *
  * Supported shapes: hidden % 256 == 0 and hidden <= 8192; head_dim in
  * {96, 128}; ffn % 128 == 0 and (ffn + 256) * hidden * 2 < 2^32; rope_split

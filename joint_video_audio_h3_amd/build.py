@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(os.path.dirname(PKG), "_build")
 LIB_PATH = os.path.join(PKG, "libh3dit.so")
-SOURCES = ["adaln_rope.hip", "gemm.hip", "attention.hip", "io.hip", "scratch.hip", "h3dit.cpp"]
+SOURCES = ["adaln_rope.hip", "gemm.hip", "attention.hip", "io.hip", "unfused.hip", "scratch.hip", "h3dit.cpp"]
 ARCH = "gfx950"
 
 

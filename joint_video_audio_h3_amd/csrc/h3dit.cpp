@@ -153,8 +153,19 @@ struct Arena {
   int8_t* qa;   // W8A8: int8 codes of the activation about to be consumed (h, o, h2 or a)
   float* qs;    // W8A8: its scales [K/G][n_pad]
   uint16_t* wdq;  // INT8 weights, when the workspace holds it: one linear's bf16 weights at a time
+  float* tmp;     // H3_UNFUSED=1: one GEMM's fp32 output (acc + bias) before its separate epilogue
   size_t bytes;
 };
+
+// H3_UNFUSED=1 in the environment (read at every call, so it must not change
+// between sizing a workspace and using it): the bf16-weight block forward runs
+// each GEMM with a plain fp32 store and its epilogue (QK-norm + RoPE + scatter,
+// SwiGLU, gated residual) as a separate elementwise kernel, to A/B the fused
+// epilogues on the device.  Other weight formats ignore it.
+bool unfused_mode(const h3_dims& d) {
+  const char* e = std::getenv("H3_UNFUSED");
+  return d.wfmt == H3_W_BF16 && e && std::strcmp(e, "1") == 0;
+}
 
 size_t up256(size_t b) { return (b + 255) / 256 * 256; }
 
@@ -197,6 +208,7 @@ Arena carve(const h3_dims& d, int64_t n, char* base, bool wdq = false) {
     const size_t wmax = std::max(std::max(3 * Di * D, D * Di), std::max(2 * F * D, D * F));
     a.wdq = reinterpret_cast<uint16_t*>(take(wmax * 2));
   }
+  if (unfused_mode(d)) a.tmp = reinterpret_cast<float*>(take(np * std::max(std::max(3 * Di, 2 * F), D) * 4));
   a.bytes = off;
   return a;
 }
@@ -403,10 +415,60 @@ h3_status run_block_w8a8(const h3_dims& d, float* x, const int32_t* tag, const u
   return H3_OK;
 }
 
+// H3_UNFUSED=1: a GEMM's output acc + bias stored as fp32 [n][n_out] into tmp
+hipError_t do_store_f32(const h3_dims& d, const uint16_t* A, const void* W, const uint16_t* b, int K, int n_out,
+                        int64_t n, float* tmp, hipStream_t s) {
+  h3::GemmArgs g = gemm_base(d, A, W, nullptr, b, (int)n, K, n_out);
+  g.x = tmp;
+  g.ldx = n_out;
+  return h3::launch_gemm(h3::EPI_STORE, H3_W_BF16, g, s);
+}
+
+// The bf16 block with every GEMM epilogue run as its own kernel (H3_UNFUSED=1).
+h3_status run_block_unfused(const h3_dims& d, float* x, const int32_t* tag, const uint16_t* table,
+                            const h3_block_weights& w, int64_t n, const Arena& ar, hipStream_t s,
+                            const Sparse* sp) {
+  const int D = d.hidden, Di = d.heads * d.head_dim, F = d.ffn;
+  h3_status st;
+  if ((st = hip_ok(do_adaln(d, x, tag, table, 0, n, ar.h, s), "adaln (attention)")) != H3_OK) return st;
+  h3::UnfusedQkvArgs qa{};
+  qa.u = ar.tmp;
+  qa.gq = w.q_norm;
+  qa.gk = w.k_norm;
+  qa.cs = ar.cs;
+  qa.q = ar.q;
+  qa.k = ar.k;
+  qa.vt = ar.vt;
+  qa.n = (int)n;
+  qa.n_pad = (int)pad_rows(n);
+  qa.heads = d.heads;
+  qa.head_dim = d.head_dim;
+  qa.eps = d.qk_eps;
+  qa.q_scale = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
+  if ((st = hip_ok(do_store_f32(d, ar.h, w.w_qkv, w.b_qkv, D, 3 * Di, n, ar.tmp, s), "qkv (unfused)")) != H3_OK ||
+      (st = hip_ok(h3::launch_unfused_qkv(qa, s), "qk-norm+rope (unfused)")) != H3_OK)
+    return st;
+  if ((st = hip_ok(do_attn(d, ar.q, ar.k, ar.vt, n, ar.o, s, sp), "attention")) != H3_OK) return st;
+  if ((st = hip_ok(do_store_f32(d, ar.o, w.w_out, w.b_out, Di, D, n, ar.tmp, s), "out-proj (unfused)")) != H3_OK ||
+      (st = hip_ok(h3::launch_unfused_resid(ar.tmp, n, D, table + (size_t)2 * D, tag, 6 * D, x, s),
+                   "gate1 residual (unfused)")) != H3_OK)
+    return st;
+  if ((st = hip_ok(do_adaln(d, x, tag, table, 1, n, ar.h, s), "adaln (mlp)")) != H3_OK) return st;
+  if ((st = hip_ok(do_store_f32(d, ar.h, w.w_fc1, w.b_fc1, D, 2 * F, n, ar.tmp, s), "fc1 (unfused)")) != H3_OK ||
+      (st = hip_ok(h3::launch_unfused_swiglu(ar.tmp, n, F, ar.a, s), "swiglu (unfused)")) != H3_OK)
+    return st;
+  if ((st = hip_ok(do_store_f32(d, ar.a, w.w_fc2, w.b_fc2, F, D, n, ar.tmp, s), "fc2 (unfused)")) != H3_OK ||
+      (st = hip_ok(h3::launch_unfused_resid(ar.tmp, n, D, table + (size_t)5 * D, tag, 6 * D, x, s),
+                   "gate2 residual (unfused)")) != H3_OK)
+    return st;
+  return H3_OK;
+}
+
 h3_status run_block(const h3_dims& d, float* x, const int32_t* tag, const uint16_t* table,
                     const h3_block_weights& w, int64_t n, const Arena& ar, hipStream_t s,
                     const Sparse* sp = nullptr) {
   if (d.wfmt == H3_W_W8A8) return run_block_w8a8(d, x, tag, table, w, n, ar, s, sp);
+  if (ar.tmp && d.wfmt == H3_W_BF16) return run_block_unfused(d, x, tag, table, w, n, ar, s, sp);
   const int Di = d.heads * d.head_dim;
   h3_status st;
   if ((st = hip_ok(do_adaln(d, x, tag, table, 0, n, ar.h, s), "adaln (attention)")) != H3_OK) return st;

@@ -96,6 +96,22 @@ hipError_t launch_euler(float* z, const float* v, float dt, int64_t n, hipStream
 hipError_t launch_euler2(float* z, const float* v1, const float* v0, float a, float b, int64_t n,
                          hipStream_t s);
 
+// Unfused epilogues (H3_UNFUSED=1): plain kernels over a GEMM's fp32 output.
+struct UnfusedQkvArgs {
+  const float* u;        // [n][3 * heads * head_dim]: per head [q | k | v] sections (acc + bias)
+  const uint16_t *gq, *gk;   // bf16 [head_dim] norm gains, or null (1)
+  const float* cs;       // [n_pad][head_dim / 2][2] rotary (cos, sin)
+  uint16_t *q, *k, *vt;  // [H][n_pad][d], [H][n_pad][d], [H][d][n_pad]; pad rows written as 0
+  int n, n_pad, heads, head_dim;
+  float eps, q_scale;
+};
+hipError_t launch_unfused_qkv(const UnfusedQkvArgs& a, hipStream_t s);
+// out[n][F] = silu(z[:, :F]) * z[:, F:] (bf16) from z fp32 [n][2F]
+hipError_t launch_unfused_swiglu(const float* z, int64_t n, int F, uint16_t* out, hipStream_t s);
+// x[n][D] += gate[tag[r] * tag_stride + c] * y[r][c]
+hipError_t launch_unfused_resid(const float* y, int64_t n, int D, const uint16_t* gate, const int32_t* tag,
+                                int tag_stride, float* x, hipStream_t s);
+
 // device address of the tag check's counter on the current device
 hipError_t bad_tags_counter(unsigned int** ptr);
 // device address of the library's static scratch array (H3_NOALLOC_SCRATCH_BYTES)

@@ -55,6 +55,20 @@ def test_padded_rows_and_workspace(L):
     assert 3.3e9 < ws < 3.6e9
 
 
+def test_unfused_workspace_holds_one_gemm_output(L, monkeypatch):
+    """H3_UNFUSED=1 adds one fp32 buffer for the widest GEMM output of a block
+    (bf16 weights only; other formats ignore the switch)."""
+    n = 1192
+    np_ = lib.padded_rows(n)
+    d = synth.H3_DIMS
+    base = lib.workspace_size(d, n)
+    base8 = lib.workspace_size(synth.H3_W8A8_DIMS, n)
+    monkeypatch.setenv("H3_UNFUSED", "1")
+    widest = max(3 * d.heads * d.head_dim, 2 * d.ffn, d.hidden)
+    assert lib.workspace_size(d, n) == base + (np_ * widest * 4 + 255) // 256 * 256
+    assert lib.workspace_size(synth.H3_W8A8_DIMS, n) == base8
+
+
 def test_int8_workspace_holds_one_dequantised_linear(L):
     """INT8 weights: the full workspace adds FC1's bf16 weights (the largest
     linear) to the bf16 model's arena; a workspace without that buffer is still
