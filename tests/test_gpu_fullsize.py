@@ -246,3 +246,30 @@ def test_full_depth_permutation_equivariance(wname, fifty_blocks):
     say("permuted vs plain: rel-L2 x_out", e, "update", du)
     assert np.isfinite(gb).all()
     assert e < TOL_DEPTH and du < 2 * TOL_DEPTH
+
+
+def test_int8_w8a16_gated_residual_split_launch_n7461():
+    """INT8 group-32 weights (the dequantising kernel of the step entry point)
+    at 7,461 rows, where FC2's gated residual runs as two launches (rows
+    [0, 6144) in 256-wide tiles, the rest in 128-wide ones): sampled rows either
+    side of the split against the oracle's dequantised weights."""
+    n = 7461
+    dims = synth.WORKLOADS["h3_1blk_n1192_int8"].dims
+    say("fullsize int8 residual, split launch", n)
+    host = synth.make_block_weights(dims, 0, seed=22)
+    devw = lib.to_device_block(host)
+    a = synth.make_device_activation(n, dims.ffn, seed=22, std=0.3)
+    x = synth.make_device_rows(synth.Workload("f", dims, 1, n, 0, 0, (0, 0, 0)), seed=22)[0]
+    x0 = x.clone()
+    tags = synth.make_tags(n, 3, seed=22)
+    table = synth.make_table(dims, 1, seed=22)[0]
+    lib.mlp_fc2_residual(dims, a.view(torch.int16), devw, dev(table), dev(tags), x)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([_rows(n, 16, seed=22), [6143, 6144, 6145]]))
+    ridx = torch.from_numpy(rows).cuda()
+    got = (x[ridx] - x0[ridx]).cpu().numpy().astype(np.float64)
+    g = oracle.modulation_from_table(table, tags[rows])["gate2"]
+    ref = g * (oracle.bf16_to_f64(_bits(a[ridx])) @ oracle.weight(host, "fc2").T
+               + oracle.bias(host, "fc2", dims.hidden))
+    assert rel_l2(got, ref) < TOL_RESID_DELTA
+

@@ -228,3 +228,28 @@ def test_fullsize_w8a8_block_sampled_rows(wname):
     say("fullsize w8a8 rel-L2", rel_l2(got, ref), rel_l2(got - xr, ref - xr))
     assert rel_l2(got, ref) < TOL_BLOCK
     assert rel_l2(got - xr, ref - xr) < 2 * TOL_BLOCK
+
+
+def test_per_row_fc2_split_launch_n7461():
+    """At 7,461 rows FC2's gated-residual GEMM runs as two launches (rows
+    [0, 6144) in 256-wide tiles, the rest in 128-wide ones); with the per-row
+    W8A8 form the second launch's int8 codes and row scales start at row 6,144.
+    Sampled rows either side of the split against the oracle."""
+    n, dims = 7461, W8_H3_ROWFC2
+    say("residual w8a8 per-row fc2, split launch", n)
+    host, devw = _weights(dims, seed=21)
+    K = dims.ffn
+    a = synth.make_activation_bf16(n, K, "a", 21, std=0.4)
+    qa, sa = _oracle_qa(a, K)
+    x = synth.make_x(n, dims, 21)
+    tags = synth.make_tags(n, dims.n_tags, 21)
+    table = synth.make_table(dims, 1, 21)[0]
+    xd = dev(x)
+    lib.mlp_fc2_residual(dims, _qa_buffer(qa, sa, K), devw, dev(table), dev(tags), xd)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(21).choice(n, 20, replace=False),
+                                     [0, 6143, 6144, 6145, n - 1]]))
+    g = oracle.modulation_from_table(table, tags[rows])["gate2"]
+    y = oracle.linear_w8a8(qa[rows], sa[rows, 0], host["w_fc2"], host["s_fc2"], oracle.bias(host, "fc2", dims.hidden))
+    got = xd.cpu().numpy().astype(np.float64)[rows] - x[rows]
+    assert rel_l2(got, g * y) < TOL_RESID_DELTA
