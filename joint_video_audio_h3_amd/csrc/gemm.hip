@@ -1256,24 +1256,38 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // exact in fp32, then rounded once).  The block forward uses it when its
 // workspace holds a layer's bf16 weights: at a few row tiles and beyond, one
 // pass over the weights costs less than dequantising them once per row tile.
-// One thread per 16 consecutive codes of a row (K % 32 == 0, so a chunk lies in
-// one scale group); 16-byte loads, two 16-byte stores.
+// A chunk is 16 consecutive codes of a row; K % 32 == 0, so chunk c lies in
+// scale group c / 2 of the row-major [rows][K/32] scales, and no row index is
+// needed.  Each thread takes four chunks 256 apart (a block covers 1,024
+// consecutive chunks, 16 KB of codes): four 16-byte code loads and four scale
+// loads are in flight before the first conversion, then eight 16-byte stores.
+constexpr int DQ_PER_THREAD = 4;
+
 __global__ __launch_bounds__(256) void dequant_w8_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict__ sc,
-                                                         uint16_t* __restrict__ out, int64_t chunks, int K) {
+                                                         uint16_t* __restrict__ out, int64_t chunks) {
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  const int cpr = K / 16;   // chunks per row
-  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * 256) {
-    const int64_t row = c / cpr;
-    const int kc = (int)(c - row * cpr);
-    const float sv = bf2f(sc[row * (K / 32) + kc / 2]);
-    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(q + c * 16);
+  const int64_t c0 = (int64_t)blockIdx.x * (256 * DQ_PER_THREAD) + threadIdx.x;
+  u32x4_t w[DQ_PER_THREAD];
+  float sv[DQ_PER_THREAD];
+#pragma unroll
+  for (int u = 0; u < DQ_PER_THREAD; ++u) {
+    const int64_t c = c0 + 256 * u;
+    if (c < chunks) {
+      w[u] = *reinterpret_cast<const u32x4_t*>(q + c * 16);
+      sv[u] = bf2f(sc[c >> 1]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < DQ_PER_THREAD; ++u) {
+    const int64_t c = c0 + 256 * u;
+    if (c >= chunks) break;
     uint32_t o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint32_t word = w[e / 2];
+      const uint32_t word = w[u][e / 2];
       const int sh = (e % 2) * 16;
-      const float lo = (float)(int8_t)((word >> sh) & 0xffu) * sv;
-      const float hi = (float)(int8_t)((word >> (sh + 8)) & 0xffu) * sv;
+      const float lo = (float)(int8_t)((word >> sh) & 0xffu) * sv[u];
+      const float hi = (float)(int8_t)((word >> (sh + 8)) & 0xffu) * sv[u];
       o[e] = pack2bf(lo, hi);
     }
     u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + c * 16);
@@ -1285,8 +1299,9 @@ __global__ __launch_bounds__(256) void dequant_w8_kernel(const int8_t* __restric
 hipError_t launch_dequant_w8(const DequantArgs& a, hipStream_t s) {
   if (a.K % 32 != 0 || a.rows <= 0) return hipErrorInvalidValue;
   const int64_t chunks = (int64_t)a.rows * (a.K / 16);
-  const int64_t blocks = (chunks + 255) / 256;
-  dequant_w8_kernel<<<dim3((unsigned)(blocks < 8192 ? blocks : 8192)), 256, 0, s>>>(a.q, a.s, a.out, chunks, a.K);
+  const int64_t blocks = (chunks + 256 * DQ_PER_THREAD - 1) / (256 * DQ_PER_THREAD);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  dequant_w8_kernel<<<dim3((unsigned)blocks), 256, 0, s>>>(a.q, a.s, a.out, chunks);
   return hipGetLastError();
 }
 

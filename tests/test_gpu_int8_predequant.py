@@ -9,7 +9,9 @@ other MFMA operand roles and fp32 rounding inside the products): each must
 match the oracle's INT8 forward within the depth bound, and the two must agree
 with each other to the one-block bound.  Row counts: 1,192 (5 row tiles, the
 last partial) and 8,449 (34 row tiles, the last holding one row), the latter
-on sampled rows.
+on sampled rows.  The dequantised weights themselves are pinned bit for bit:
+the first path must reproduce the bf16 block run on the oracle's dequantised
+weights exactly.
 """
 import dataclasses
 
@@ -72,3 +74,53 @@ def test_int8_forward_on_both_gemm_paths(n, nb):
         else:
             say(f"int8 {label} sampled rel-L2 x_out", rel_l2(g[rows], ref), "update", rel_l2(g[rows] - xr, ref - xr))
             assert rel_l2(g[rows], ref) < TOL_BLOCK and rel_l2(g[rows] - xr, ref - xr) < 2 * TOL_BLOCK
+
+
+def _bf16_block_from_oracle_dequant(host8):
+    """The INT8 block's weights as bf16 bits, dequantised by the oracle
+    (RNE_bf16(q * s), exact bf16 values, so their top 16 bits are the value)."""
+    out = {}
+    for k, v in host8.items():
+        if k.startswith("w_"):
+            wdq = oracle.dequant_int8_g32(v, host8["s_" + k[2:]])
+            f = wdq.astype(np.float32)
+            assert np.array_equal(f.astype(np.float64), wdq)
+            bits = f.view(np.uint32)
+            assert not (bits & 0xFFFF).any()
+            out[k] = (bits >> 16).astype(np.uint16)
+        elif k.startswith("s_"):
+            out[k] = None
+        else:
+            out[k] = v
+    return out
+
+
+@pytest.fixture(scope="module")
+def int8_and_dequantised_blocks():
+    host8 = synth.make_block_weights(INT8, 0, seed=71)
+    return lib.to_device_block(host8), lib.to_device_block(_bf16_block_from_oracle_dequant(host8))
+
+
+@pytest.mark.parametrize("n", [300, 1192])
+def test_predequant_block_is_the_bf16_block_on_oracle_dequantised_weights(n, int8_and_dequantised_blocks):
+    """With the full workspace the INT8 block writes each linear's bf16 weights
+    into the workspace and runs the bf16 GEMM on them, so it must equal, bit for
+    bit, the bf16 block whose weights are the oracle's RNE_bf16(q * s) (a
+    wrong element of any of the four dequantised matrices changes the fp32
+    products of its output column in every row)."""
+    say("int8 predequant block vs bf16 block on oracle-dequantised weights:", n, "rows")
+    seed = 71
+    bf16 = dataclasses.replace(INT8, wfmt=synth.WFMT_BF16)
+    block8, block16 = int8_and_dequantised_blocks
+    x = synth.make_x(n, INT8, seed=seed)
+    tags = dev(synth.make_tags(n, INT8.n_tags, seed=seed))
+    pos = dev(synth.make_positions(n, seed=seed))
+    table = dev(synth.make_table(INT8, 1, seed=seed)[0])
+    xa, xb = dev(x), dev(x)
+    ws8 = lib.alloc_workspace(INT8, n)
+    lib.dit_block_forward(INT8, xa, tags, pos, table, block8, ws8)
+    ws16 = lib.alloc_workspace(bf16, n)
+    lib.dit_block_forward(bf16, xb, tags, pos, table, block16, ws16)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(xa).all())
+    assert torch.equal(xa, xb)
