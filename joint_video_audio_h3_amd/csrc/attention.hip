@@ -663,7 +663,12 @@ __global__ __launch_bounds__(A48_WAVES * 64) __attribute__((amdgpu_waves_per_eu(
               for (int i = 0; i < 4; ++i)
                 if (key0 + 4 * j + i >= p.n) sc[gr][j][i] = -INFINITY;
         }
+        // the softmax at low wave priority, the MFMA runs at high: while one wave
+        // of a SIMD works through its softmax, the other's MFMAs win the issue
+        // port (measured 1.8 % faster at 49,840 rows)
+        __builtin_amdgcn_s_setprio(0);
         softmax(sc, pf, first && H == 0);
+        __builtin_amdgcn_s_setprio(1);
       }
       if constexpr (U + PD < 32) fr[(U + PD) % (PD + 1)] = rd(att_ic<U + PD>{});
       const bf16x8& a = fr[U % (PD + 1)];
