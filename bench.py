@@ -33,7 +33,7 @@ HBM = perf_model.PEAK_HBM_GBS
 # bytes per launch after the copy-kernel calibration (profiles/), with the first
 # 16 hex digits of the SHA-256 of the kernel's source file when the counters
 # were taken: reported only while that source is unchanged, else None.
-TRAFFIC_BYTES = {("h3_50blk_n49840", "attention"): (8.578e9, "491a083b6aa28b13")}
+TRAFFIC_BYTES = {("h3_50blk_n49840", "attention"): (8.578e9, "0ff5dc2ed7652585")}
 KERNEL_SOURCE = {"attention": "attention.hip", "qkv_rope": "gemm.hip", "fc1_swiglu": "gemm.hip",
                  "fc2_resid": "gemm.hip", "out_proj_resid": "gemm.hip"}
 

@@ -327,16 +327,21 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       mask(s1, kt * ATT_BKV + 32);
     }
     bf16x8 pf[2];
+    // each softmax at low wave priority, the MFMA runs at high (as attn48_kernel)
+    __builtin_amdgcn_s_setprio(0);
     softmax(s0, [&](float sh) __attribute__((always_inline)) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) s1[v] -= sh;
     }, first, pf);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < 2 * DT; ++i) {
       oacc[i / 2] = mfma32(va[i], pf[i % 2], oacc[i / 2]);
       vb[i] = vr(i / 2, 2 + i % 2);
     }
+    __builtin_amdgcn_s_setprio(0);
     softmax(s1, [](float) {}, false, pf);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < 2 * DT; ++i) oacc[i / 2] = mfma32(vb[i], pf[i % 2], oacc[i / 2]);
   };
